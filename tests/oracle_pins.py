@@ -1,0 +1,412 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Every ``check_*`` takes the oracle module as its argument and raises on a
+mismatch.  ``test_oracle_pins.py`` runs them against the real oracle;
+``test_oracle_mutations.py`` runs them against deliberately broken copies of it
+to show that a plausible mistake anywhere in the oracle fails at least one pin.
+
+The logical-to-physical writer ``pool_from_logical`` below places contiguous K/V
+into pages by reshaping whole blocks, a different mechanism from the oracle's
+index arithmetic, so the round trip through ``gather`` is a real check.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def pool_from_logical(Ks, Vs, block_size, *, seed=0, spare=3, shared_prefix_blocks=0):
+    """Write per-sequence contiguous K/V ``[L_b, Hkv, d]`` into a randomly placed pool.
+
+    Whole blocks are written by reshaping ``[n_pages * bs, Hkv, d]`` into
+    ``[n_pages, bs, Hkv, d]``; unused pages and past-the-end slots are NaN.  With
+    ``shared_prefix_blocks`` the first blocks of every sequence are the same
+    physical pages (taken from sequence 0's values).
+    """
+    bs = block_size
+    Hkv, d = Ks[0].shape[1:]
+    pages = [-(-len(K) // bs) for K in Ks]
+    sp = shared_prefix_blocks
+    total = sp + sum(p - sp for p in pages)
+    nb = total + spare
+    perm = np.random.default_rng(seed).permutation(nb)
+    pool = np.full((nb, 2, bs, Hkv, d), np.nan, dtype=np.float32)
+    bt = np.full((len(Ks), max(pages)), perm[-1], dtype=np.int32)
+
+    def write(ids, K, V, n):
+        padK = np.full((n * bs, Hkv, d), np.nan, dtype=np.float32)
+        padV = padK.copy()
+        padK[:len(K)] = K
+        padV[:len(V)] = V
+        pool[ids, 0] = padK.reshape(n, bs, Hkv, d)
+        pool[ids, 1] = padV.reshape(n, bs, Hkv, d)
+
+    prefix_ids = perm[:sp]
+    if sp:
+        write(prefix_ids, Ks[0][:sp * bs], Vs[0][:sp * bs], sp)
+    cur = sp
+    for b, (K, V) in enumerate(zip(Ks, Vs)):
+        n = pages[b] - sp
+        ids = perm[cur:cur + n]
+        cur += n
+        write(ids, K[sp * bs:], V[sp * bs:], n)
+        bt[b, :sp] = prefix_ids
+        bt[b, sp:pages[b]] = ids
+    return pool, bt
+
+
+def _qsl(qlens):
+    return np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+
+
+def _random_logical(lens, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    Ks = [rng.standard_normal((L, Hkv, d)).astype(np.float32) for L in lens]
+    Vs = [rng.standard_normal((L, Hkv, d)).astype(np.float32) for L in lens]
+    return Ks, Vs
+
+
+# A small mixed batch: two decodes, a chunk with context, a full prefill, a chunk.
+MIX_Q = [1, 1, 16, 37, 5]
+MIX_L = [17, 33, 64, 37, 40]
+
+
+# ---------------------------------------------------------------------------
+
+def check_kv_cache_shape(O):
+    g = _golden("kv_cache_shape.json")
+    for case in g["cases"]:
+        assert tuple(O.kv_cache_shape(*case["args"])) == tuple(case["shape"])
+    for bs in g["rejected_block_sizes"]:
+        try:
+            O.kv_cache_shape(4, bs, 2, 64)
+        except ValueError:
+            continue
+        raise AssertionError(f"block size {bs} accepted")
+
+
+def check_gather_roundtrip(O):
+    for bs, lens in ((16, [1, 15, 16, 17, 50]), (32, [33, 64, 5]), (48, [100, 47])):
+        Ks, Vs = _random_logical(lens, 3, 8, seed=bs)
+        pool, bt = pool_from_logical(Ks, Vs, bs, seed=bs + 1)
+        for b, L in enumerate(lens):
+            K, V = O.gather(pool, bt[b], L)
+            assert K.shape == (L, 3, 8)
+            assert np.array_equal(K, Ks[b]) and np.array_equal(V, Vs[b])
+
+
+def check_single_key(O):
+    # One key per sequence; the other slots of the page are NaN.  The output is
+    # that key's V row exactly and the LSE is the single scaled score.
+    Ks, Vs = _random_logical([1, 1], 2, 32, seed=3)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=4)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 32)).astype(np.float32)
+    scale = 0.37
+    out, lse = O.attention(q, pool, bt, _qsl([1, 1]), np.array([1, 1]), scale, dtype="fp32")
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, h], Vs[b][0, h // 2].astype(np.float64))
+            s = scale * math.fsum(float(a) * float(c) for a, c in zip(q[b, h], Ks[b][0, h // 2]))
+            assert abs(lse[b, h] - s) < 1e-12
+
+
+def check_equal_scores(O):
+    # q = 0: every visible score is 0, so the output is the plain mean of the
+    # visible V rows and the LSE is ln(number of visible keys).
+    H, Hkv, d = 6, 2, 8
+    g = H // Hkv
+    Ks, Vs = _random_logical(MIX_L, Hkv, d, seed=6)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=7)
+    q = np.zeros((sum(MIX_Q), H, d), dtype=np.float32)
+    qsl = _qsl(MIX_Q)
+    for causal in (True, False):
+        out, lse = O.attention(q, pool, bt, qsl, np.array(MIX_L), 0.5, dtype="fp32", causal=causal)
+        for b, (qb, L) in enumerate(zip(MIX_Q, MIX_L)):
+            c = L - qb
+            for i in range(qb):
+                n = (c + i + 1) if causal else L
+                r = qsl[b] + i
+                for h in range(H):
+                    exp_o = Vs[b][:n, h // g].astype(np.float64).mean(axis=0)
+                    assert np.max(np.abs(out[r, h] - exp_o)) < 1e-12
+                    assert abs(lse[r, h] - math.log(n)) < 1e-12
+
+
+def check_ramp_needle(O):
+    # K[t, :, 0] = 256 t, q[., 0] = 1: the score grows by 256*scale = 64 per key,
+    # so all weight sits on the last visible key (next one down: e^-64).
+    H, Hkv, d, scale = 4, 2, 16, 0.25
+    g = H // Hkv
+    Ks, Vs = [], []
+    for L in MIX_L:
+        K = np.zeros((L, Hkv, d), dtype=np.float32)
+        K[:, :, 0] = 256.0 * np.arange(L)[:, None]
+        V = (np.arange(L)[:, None, None] + 1000.0 * np.arange(Hkv)[None, :, None]
+             + 0.001 * np.arange(d)[None, None, :]).astype(np.float32)
+        Ks.append(K)
+        Vs.append(V)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=8)
+    q = np.zeros((sum(MIX_Q), H, d), dtype=np.float32)
+    q[:, :, 0] = 1.0
+    qsl = _qsl(MIX_Q)
+    out, lse = O.attention(q, pool, bt, qsl, np.array(MIX_L), scale, dtype="fp32")
+    for b, (qb, L) in enumerate(zip(MIX_Q, MIX_L)):
+        c = L - qb
+        for i in range(qb):
+            r = qsl[b] + i
+            for h in range(H):
+                assert np.max(np.abs(out[r, h] - Vs[b][c + i, h // g])) < 1e-9
+                assert abs(lse[r, h] - 64.0 * (c + i)) < 1e-9
+
+
+def check_bruteforce_tiny(O):
+    # Pure-Python loops with math.fsum / math.exp, indexing the pool directly.
+    H, Hkv, d, bs, scale = 4, 2, 8, 16, 0.3
+    g = H // Hkv
+    lens, qlens = [17, 33, 40, 20], [1, 1, 8, 20]
+    Ks, Vs = _random_logical(lens, Hkv, d, seed=9)
+    pool, bt = pool_from_logical(Ks, Vs, bs, seed=10)
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((sum(qlens), H, d)).astype(np.float32)
+    qsl = _qsl(qlens)
+    out, lse = O.attention(q, pool, bt, qsl, np.array(lens), scale, dtype="fp32")
+    for b in range(len(lens)):
+        c = lens[b] - qlens[b]
+        for i in range(qlens[b]):
+            r = int(qsl[b]) + i
+            for h in range(H):
+                kv = h // g
+                sc = []
+                for t in range(c + i + 1):
+                    blk, slot = int(bt[b][t // bs]), t % bs
+                    sc.append(scale * math.fsum(float(q[r, h, j]) * float(pool[blk, 0, slot, kv, j])
+                                                for j in range(d)))
+                m = max(sc)
+                w = [math.exp(s - m) for s in sc]
+                Z = math.fsum(w)
+                for j in range(d):
+                    val = math.fsum(w[t] * float(pool[int(bt[b][t // bs]), 1, t % bs, kv, j])
+                                    for t in range(len(w))) / Z
+                    assert abs(out[r, h, j] - val) < 1e-12
+                assert abs(lse[r, h] - (m + math.log(Z))) < 1e-12
+
+
+def check_sdpa_special_case(O):
+    # torch's CPU attention in float64 with an explicit boolean-derived additive
+    # mask (key t visible iff t <= c + i) and K/V heads repeated g times.
+    import torch
+    H, Hkv, d, scale = 8, 2, 16, 0.2
+    g = H // Hkv
+    lens, qlens = [37, 64, 30, 50], [37, 64, 10, 1]
+    Ks, Vs = _random_logical(lens, Hkv, d, seed=12)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=13)
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((sum(qlens), H, d)).astype(np.float32)
+    qsl = _qsl(qlens)
+    out, lse = O.attention(q, pool, bt, qsl, np.array(lens), scale, dtype="fp32")
+    for b, (L, qb) in enumerate(zip(lens, qlens)):
+        c = L - qb
+        Q = torch.from_numpy(q[qsl[b]:qsl[b + 1]].astype(np.float64)).transpose(0, 1)[None]
+        K = torch.from_numpy(np.repeat(Ks[b], g, axis=1).astype(np.float64)).transpose(0, 1)[None]
+        V = torch.from_numpy(np.repeat(Vs[b], g, axis=1).astype(np.float64)).transpose(0, 1)[None]
+        vis = np.arange(L)[None, :] <= (c + np.arange(qb))[:, None]
+        am = torch.from_numpy(np.where(vis, 0.0, -np.inf))
+        o_ref, lse_ref = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu(
+            Q.contiguous(), K.contiguous(), V.contiguous(), 0.0, False, attn_mask=am, scale=scale)[:2]
+        o_ref = o_ref[0].transpose(0, 1).numpy()
+        lse_ref = lse_ref[0].transpose(0, 1).numpy()
+        assert np.max(np.abs(out[qsl[b]:qsl[b + 1]] - o_ref)) < 1e-10
+        assert np.max(np.abs(lse[qsl[b]:qsl[b + 1]] - lse_ref)) < 1e-10
+
+
+def check_cascade_equals_full(O):
+    # Two shared blocks (32 tokens) at the front of every table.
+    H, Hkv, d, bs = 4, 2, 16, 16
+    lens, qlens = [50, 33, 60, 90], [1, 1, 8, 3]
+    rng = np.random.default_rng(15)
+    prefix_K = rng.standard_normal((32, Hkv, d)).astype(np.float32)
+    prefix_V = rng.standard_normal((32, Hkv, d)).astype(np.float32)
+    Ks, Vs = _random_logical(lens, Hkv, d, seed=16)
+    for K, V in zip(Ks, Vs):
+        K[:32], V[:32] = prefix_K, prefix_V
+    pool, bt = pool_from_logical(Ks, Vs, bs, seed=17, shared_prefix_blocks=2)
+    q = rng.standard_normal((sum(qlens), H, d)).astype(np.float32)
+    qsl = _qsl(qlens)
+    full = O.attention(q, pool, bt, qsl, np.array(lens), 0.25, dtype="fp32")
+    casc = O.cascade_attention(q, pool, bt, qsl, np.array(lens), 0.25, 32, dtype="fp32")
+    assert np.max(np.abs(full[0] - casc[0])) < 1e-12
+    assert np.max(np.abs(full[1] - casc[1])) < 1e-12
+    # the prefix blocks reported by the metadata are the shared physical blocks
+    md = O.metadata(qsl, np.array(lens), 32, bt, bs)
+    assert list(md["prefix_blocks"]) == list(bt[0, :2])
+
+
+def check_chunk_consistency(O):
+    # One 90-token prompt processed whole, or as three chunks whose context is
+    # everything before them: each row must come out the same.
+    H, Hkv, d = 4, 1, 16
+    Ks, Vs = _random_logical([90], Hkv, d, seed=18)
+    pool, bt1 = pool_from_logical(Ks, Vs, 16, seed=19)
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((90, H, d)).astype(np.float32)
+    whole = O.attention(q, pool, bt1, _qsl([90]), np.array([90]), 0.3, dtype="fp32")
+    bt3 = np.repeat(bt1, 3, axis=0)
+    chunks = O.attention(q, pool, bt3, _qsl([30, 34, 26]), np.array([30, 64, 90]), 0.3, dtype="fp32")
+    assert np.max(np.abs(whole[0] - chunks[0])) < 1e-12
+    assert np.max(np.abs(whole[1] - chunks[1])) < 1e-12
+
+
+def check_gqa_expansion(O):
+    # GQA with g = 4 equals MHA over a pool whose KV heads are repeated 4 times.
+    H, Hkv, d = 8, 2, 16
+    Ks, Vs = _random_logical(MIX_L, Hkv, d, seed=21)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=22)
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((sum(MIX_Q), H, d)).astype(np.float32)
+    qsl = _qsl(MIX_Q)
+    gqa = O.attention(q, pool, bt, qsl, np.array(MIX_L), 0.3, dtype="fp32")
+    mha = O.attention(q, np.repeat(pool, H // Hkv, axis=3), bt, qsl, np.array(MIX_L), 0.3, dtype="fp32")
+    assert np.max(np.abs(gqa[0] - mha[0])) < 1e-12
+    assert np.max(np.abs(gqa[1] - mha[1])) < 1e-12
+
+
+def check_batch_permutation(O):
+    # Reordering the sequences of a batch only reorders the output rows.
+    H, Hkv, d = 4, 2, 16
+    Ks, Vs = _random_logical(MIX_L, Hkv, d, seed=24)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=25)
+    rng = np.random.default_rng(26)
+    q = rng.standard_normal((sum(MIX_Q), H, d)).astype(np.float32)
+    qsl = _qsl(MIX_Q)
+    ref = O.attention(q, pool, bt, qsl, np.array(MIX_L), 0.3, dtype="fp32")
+    perm = [3, 0, 4, 2, 1]
+    qlens2 = [MIX_Q[p] for p in perm]
+    qsl2 = _qsl(qlens2)
+    rows = np.concatenate([np.arange(qsl[p], qsl[p + 1]) for p in perm])
+    out = O.attention(q[rows], pool, bt[perm], qsl2, np.array([MIX_L[p] for p in perm]), 0.3, dtype="fp32")
+    assert np.array_equal(out[0], ref[0][rows]) and np.array_equal(out[1], ref[1][rows])
+    md = O.metadata(qsl2, np.array([MIX_L[p] for p in perm]))
+    is_dec = [q == 1 for q in qlens2]
+    assert list(md["order"]) == [i for i in range(5) if is_dec[i]] + [i for i in range(5) if not is_dec[i]]
+
+
+def check_block_permutation(O):
+    # Moving pages to other physical slots and rewriting the table changes nothing.
+    H, Hkv, d = 4, 2, 16
+    Ks, Vs = _random_logical(MIX_L, Hkv, d, seed=27)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=28)
+    rng = np.random.default_rng(29)
+    q = rng.standard_normal((sum(MIX_Q), H, d)).astype(np.float32)
+    qsl = _qsl(MIX_Q)
+    ref = O.attention(q, pool, bt, qsl, np.array(MIX_L), 0.3, dtype="fp32")
+    perm = rng.permutation(pool.shape[0])
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    out = O.attention(q, pool2, perm[bt].astype(np.int32), qsl, np.array(MIX_L), 0.3, dtype="fp32")
+    assert np.array_equal(out[0], ref[0]) and np.array_equal(out[1], ref[1])
+
+
+def check_metadata_golden(O):
+    for case in _golden("decode_first.json")["cases"]:
+        qsl = _qsl(case["query_lens"])
+        md = O.metadata(qsl, np.array(case["seq_lens"]))
+        assert [int(x) for x in md["is_decode"]] == case["is_decode"]
+        assert [int(x) for x in md["order"]] == case["order"]
+        for k in ("num_decodes", "num_decode_tokens", "num_prefills", "num_prefill_tokens"):
+            assert md[k] == case[k], k
+        assert [int(x) for x in md["context_lens"]] == case["context_lens"]
+        assert [int(x) for x in md["is_chunked"]] == case["is_chunked"]
+
+
+def check_metadata_cascade_errors(O):
+    qsl = _qsl([1, 1])
+    bt = np.array([[3, 4, 5], [3, 4, 6]], dtype=np.int32)
+    md = O.metadata(qsl, np.array([40, 45]), 32, bt, 16)
+    assert list(md["prefix_blocks"]) == [3, 4]
+    bad = [
+        (np.array([40, 45]), 24, bt),                                   # not whole blocks
+        (np.array([40, 45]), 48, bt),                                   # blocks differ
+        (np.array([40, 30]), 32, bt),                                   # longer than a context
+    ]
+    for lens, P, table in bad:
+        try:
+            O.metadata(qsl, lens, P, table, 16)
+        except ValueError:
+            continue
+        raise AssertionError(f"cascade prefix {P} accepted")
+
+
+def check_cascade_reads_golden(O):
+    g = _golden("cascade_reads.json")
+    r = O.cascade_prefix_reads(g["R"], g["P"])
+    assert r["prefix_naive"] == g["prefix_naive"]
+    assert r["prefix_cascade"] == g["prefix_cascade"]
+    r2 = O.cascade_prefix_reads(3, 10, [1, 2, 3])
+    assert r2["naive"] == 3 * 10 + 6 and r2["cascade"] == 10 + 6
+
+
+def check_merge_states(O):
+    rng = np.random.default_rng(30)
+    o = rng.standard_normal((3, 2, 4))
+    lam = rng.standard_normal((3, 2))
+    om, lm = O.merge_states(o, lam, o, lam)                    # two identical halves
+    assert np.max(np.abs(om - o)) < 1e-12 and np.max(np.abs(lm - (lam + math.log(2)))) < 1e-12
+    om, lm = O.merge_states(o, lam, rng.standard_normal((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.max(np.abs(om - o)) < 1e-12 and np.max(np.abs(lm - lam)) < 1e-12
+    # two single-key parts: weights e^s1 and e^s2
+    s1, s2 = 0.7, -1.3
+    v1, v2 = rng.standard_normal(4), rng.standard_normal(4)
+    om, lm = O.merge_states(v1[None], np.array([s1]), v2[None], np.array([s2]))
+    Z = math.exp(s1) + math.exp(s2)
+    assert np.max(np.abs(om[0] - (math.exp(s1) * v1 + math.exp(s2) * v2) / Z)) < 1e-12
+    assert abs(lm[0] - math.log(Z)) < 1e-12
+
+
+def check_decode_intensity_golden(O):
+    g = _golden("decode_intensity.json")
+    r = O.decode_intensity(128, 4096, g["bytes_per_elem"])
+    assert abs(r["macs_per_byte_one_product"] - g["macs_per_byte_one_product"]) < 1e-15
+    assert abs(r["flop_per_byte"] - 1.0) < 1e-15
+    assert abs(O.decode_intensity(128, 4096, 2, group=4)["flop_per_byte"] - 4.0) < 1e-15
+    assert abs(O.decode_intensity(128, 4096, 2, group=8)["flop_per_byte"] - 8.0) < 1e-15
+
+
+def check_bf16_widening(O):
+    # bf16 patterns widen exactly: 1.0 = 0x3F80, -2.0 = 0xC000, 0.15625 = 0x3E20,
+    # the smallest normal 2^-126 = 0x0080, NaN stays NaN.
+    bits = np.array([0x3F80, 0xC000, 0x3E20, 0x0080, 0x7FC0], dtype=np.uint16)
+    v = O.to_f64(bits, "bf16")
+    assert list(v[:4]) == [1.0, -2.0, 0.15625, 2.0 ** -126] and np.isnan(v[4])
+
+
+ALL_CHECKS = [
+    check_kv_cache_shape,
+    check_gather_roundtrip,
+    check_single_key,
+    check_equal_scores,
+    check_ramp_needle,
+    check_bruteforce_tiny,
+    check_sdpa_special_case,
+    check_cascade_equals_full,
+    check_chunk_consistency,
+    check_gqa_expansion,
+    check_batch_permutation,
+    check_block_permutation,
+    check_metadata_golden,
+    check_metadata_cascade_errors,
+    check_cascade_reads_golden,
+    check_merge_states,
+    check_decode_intensity_golden,
+    check_bf16_widening,
+]

@@ -1,0 +1,73 @@
+"""Plant plausible mistakes in copies of the oracle and check that a pin fails.
+
+Each mutant is the oracle's source with one edit, executed as a fresh module on
+the CPU.  The test passes when at least one pin in ``oracle_pins`` rejects the
+mutant, showing that the pins constrain that part of the oracle.
+"""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "causal_off_by_one": ("visible = t[None, :] <= (cb + i)[:, None]\n        else:\n            visible = np.ones((len(i), Lb)",
+                          "visible = t[None, :] < (cb + i)[:, None]\n        else:\n            visible = np.ones((len(i), Lb)"),
+    "context_ignores_query_len": ("cb = Lb - qb\n", "cb = Lb - 1\n"),
+    "kv_slot_swapped": ("K = kv_cache[blocks, 0, slots]\n    V = kv_cache[blocks, 1, slots]",
+                        "K = kv_cache[blocks, 1, slots]\n    V = kv_cache[blocks, 0, slots]"),
+    "block_and_slot_swapped": ("[t // bs]\n    slots = t % bs", "[t % bs]\n    slots = t // bs"),
+    "gqa_interleaved": ("            heads = slice(kvh * g, (kvh + 1) * g)\n            o, s = _partial(Q[:, heads, :]",
+                        "            heads = slice(kvh, H, Hkv)\n            o, s = _partial(Q[:, heads, :]"),
+    "lse_base_2": ("lse[has] = m[has] + np.log(l[has])", "lse[has] = m[has] + np.log2(l[has])"),
+    "scale_dropped": ("S = scale * (Qg @ K.T)", "S = (Qg @ K.T)"),
+    "v_replaced_by_k": ("num = E @ V ", "num = E @ K "),
+    "not_normalised": ("o[has] = num[has] / l[has][:, None]", "o[has] = num[has]"),
+    "lse_without_max": ("lse[has] = m[has] + np.log(l[has])", "lse[has] = np.log(l[has])"),
+    "decode_threshold": ("is_decode = qlen == 1", "is_decode = qlen <= 2"),
+    "prefill_first": ("order = np.array(decodes + prefills", "order = np.array(prefills + decodes"),
+    "merge_unnormalised": ("o = (w1 / tot_safe)[..., None] * o1 + (w2 / tot_safe)[..., None] * o2",
+                           "o = w1[..., None] * o1 + w2[..., None] * o2"),
+    "merge_lse_max_only": ("lse = np.where(tot > 0, mx_safe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)",
+                           "lse = np.where(tot > 0, mx_safe, -np.inf)"),
+    "cascade_suffix_positions": ("t = np.arange(P, Lb)", "t = np.arange(0, Lb - P)"),
+    "cascade_reads_naive": ('"prefix_naive": R * P,', '"prefix_naive": R + P,'),
+    "shape_order": ("return (int(num_blocks), 2, int(block_size), int(num_kv_heads), int(head_size))",
+                    "return (int(num_blocks), int(block_size), 2, int(num_kv_heads), int(head_size))"),
+    "no_block_size_check": ("if block_size % 16 != 0:\n        raise ValueError(\"block size must",
+                            "if block_size % 8 != 0:\n        raise ValueError(\"block size must"),
+    "bf16_widen_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "intensity_drops_pv": ("flops = g * 4 * L * d", "flops = g * 2 * L * d"),
+}
+
+
+def _load(src: str):
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_copy_passes():
+    with open(SRC) as f:
+        mod = _load(f.read())
+    for check in oracle_pins.ALL_CHECKS:
+        check(mod)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mod = _load(src.replace(old, new, 1))
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:  # any failure (assertion or crash) counts as caught
+            failed.append(check.__name__)
+    assert failed, f"mutant {name} passed every pin"
