@@ -1,0 +1,374 @@
+// C ABI of libpagedattn: argument checks, plan ownership, device copies of the
+// schedule, error reporting and the optional per-launch timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+struct pa_plan {
+  pa::HostPlan hp;
+  int device = -1;
+  void* dev_buf = nullptr;
+  pa::DeviceSchedule ds{};
+  size_t ws_bytes = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status set_err(pa_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+pa_status hip_err(hipError_t e, const char* what) {
+  return set_err(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Makes `dev` current for the scope of a call and restores the caller's device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (dev >= 0 && dev != prev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t begin, end;
+};
+
+struct ProfState {
+  bool active = false;
+  int max = 0;
+  int pending = -1;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> recs;
+};
+
+thread_local ProfState g_prof;
+
+void prof_release() {
+  for (hipEvent_t e : g_prof.pool) (void)hipEventDestroy(e);
+  g_prof = ProfState{};
+}
+
+}  // namespace
+
+namespace pa {
+
+void profile_before(const char* name, void* stream) {
+  if (!g_prof.active || (int)g_prof.recs.size() >= g_prof.max) return;
+  const size_t i = g_prof.recs.size();
+  ProfRec r{name, g_prof.pool[2 * i], g_prof.pool[2 * i + 1]};
+  if (hipEventRecord(r.begin, static_cast<hipStream_t>(stream)) != hipSuccess) return;
+  g_prof.recs.push_back(r);
+  g_prof.pending = (int)i;
+}
+
+void profile_after(void* stream) {
+  if (g_prof.pending < 0) return;
+  (void)hipEventRecord(g_prof.recs[g_prof.pending].end, static_cast<hipStream_t>(stream));
+  g_prof.pending = -1;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_kv_cache_shape(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                            int64_t shape_out[5]) {
+  g_err.clear();
+  if (!shape_out) return set_err(PA_ERR_INVALID_ARG, "shape_out is NULL");
+  if (block_size < 16 || block_size % 16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "block size must be a positive multiple of 16");
+  if (num_blocks < 1 || num_kv_heads < 1 || head_size < 1)
+    return set_err(PA_ERR_INVALID_ARG, "num_blocks, num_kv_heads and head_size must be >= 1");
+  shape_out[0] = num_blocks;
+  shape_out[1] = 2;
+  shape_out[2] = block_size;
+  shape_out[3] = num_kv_heads;
+  shape_out[4] = head_size;
+  return PA_OK;
+}
+
+pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc, const int32_t* seq_lens,
+                         const int32_t* block_table, int device, pa_plan** plan_out) {
+  g_err.clear();
+  if (!plan_out) return set_err(PA_ERR_INVALID_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  if (!params) return set_err(PA_ERR_INVALID_ARG, "params is NULL");
+
+  int num_cus = 256;
+  if (device >= 0) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_err(e, "hipGetDeviceCount");
+    if (device >= n) return set_err(PA_ERR_INVALID_ARG, "device index out of range");
+    e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_err(e, "hipDeviceGetAttribute");
+  }
+
+  pa_plan* plan = new (std::nothrow) pa_plan();
+  if (!plan) return set_err(PA_ERR_OOM, "host allocation failed");
+  std::string err;
+  pa_status st = pa::build_host_plan(*params, query_start_loc, seq_lens, block_table, num_cus, plan->hp, err);
+  if (st != PA_OK) {
+    delete plan;
+    return set_err(st, err);
+  }
+  pa::HostPlan& hp = plan->hp;
+  plan->device = device;
+  plan->ws_bytes = hp.num_partials > 0
+                       ? align256((size_t)hp.num_partials * params->num_heads * params->head_size * sizeof(float)) +
+                             align256((size_t)hp.num_partials * params->num_heads * sizeof(float))
+                       : 0;
+
+  if (device >= 0) {
+    const size_t b_dec = hp.decode_items.size() * sizeof(pa::WorkItem);
+    const size_t b_pre = hp.prefill_items.size() * sizeof(pa::WorkItem);
+    const size_t b_pfx = hp.prefix_items.size() * sizeof(pa::WorkItem);
+    const size_t b_mrg = hp.merges.size() * sizeof(pa::MergeRow);
+    const size_t b_row = hp.row_pbase.size() * sizeof(int32_t);
+    const size_t o_dec = 0, o_pre = o_dec + align256(b_dec), o_pfx = o_pre + align256(b_pre),
+                 o_mrg = o_pfx + align256(b_pfx), o_row = o_mrg + align256(b_mrg), total = o_row + align256(b_row);
+    if (total > 0) {
+      DeviceGuard guard(device);
+      if (!guard.ok) {
+        delete plan;
+        return set_err(PA_ERR_HIP, "hipSetDevice failed");
+      }
+      std::vector<unsigned char> host(total, 0);
+      std::memcpy(host.data() + o_dec, hp.decode_items.data(), b_dec);
+      std::memcpy(host.data() + o_pre, hp.prefill_items.data(), b_pre);
+      std::memcpy(host.data() + o_pfx, hp.prefix_items.data(), b_pfx);
+      std::memcpy(host.data() + o_mrg, hp.merges.data(), b_mrg);
+      std::memcpy(host.data() + o_row, hp.row_pbase.data(), b_row);
+      hipError_t e = hipMalloc(&plan->dev_buf, total);
+      if (e != hipSuccess) {
+        delete plan;
+        return set_err(PA_ERR_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
+      }
+      e = hipMemcpy(plan->dev_buf, host.data(), total, hipMemcpyHostToDevice);
+      if (e != hipSuccess) {
+        (void)hipFree(plan->dev_buf);
+        delete plan;
+        return hip_err(e, "hipMemcpy");
+      }
+      unsigned char* base = static_cast<unsigned char*>(plan->dev_buf);
+      pa::DeviceSchedule& ds = plan->ds;
+      ds.decode = reinterpret_cast<const pa::WorkItem*>(base + o_dec);
+      ds.n_decode = (int)hp.decode_items.size();
+      ds.prefill = reinterpret_cast<const pa::WorkItem*>(base + o_pre);
+      ds.n_prefill = (int)hp.prefill_items.size();
+      ds.prefix = reinterpret_cast<const pa::WorkItem*>(base + o_pfx);
+      ds.n_prefix = (int)hp.prefix_items.size();
+      ds.merge = reinterpret_cast<const pa::MergeRow*>(base + o_mrg);
+      ds.n_merge = (int)hp.merges.size();
+      ds.row_pbase = reinterpret_cast<const int32_t*>(base + o_row);
+      ds.num_partials = hp.num_partials;
+    }
+  }
+  *plan_out = plan;
+  return PA_OK;
+}
+
+pa_status pa_plan_get_info(const pa_plan* plan, pa_plan_info* info) {
+  g_err.clear();
+  if (!plan || !info) return set_err(PA_ERR_INVALID_ARG, "plan or info is NULL");
+  *info = plan->hp.info;
+  return PA_OK;
+}
+
+pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, int64_t capacity, int64_t* count) {
+  g_err.clear();
+  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
+  const std::vector<int32_t>* v = nullptr;
+  switch (which) {
+    case PA_ARRAY_ORDER: v = &plan->hp.order; break;
+    case PA_ARRAY_IS_DECODE: v = &plan->hp.is_decode; break;
+    case PA_ARRAY_PREFIX_BLOCKS: v = &plan->hp.prefix_blocks; break;
+    case PA_ARRAY_ROW_PARTIALS: v = &plan->hp.row_partials; break;
+    default: return set_err(PA_ERR_INVALID_ARG, "unknown plan array");
+  }
+  if (count) *count = (int64_t)v->size();
+  if ((int64_t)v->size() > capacity) return set_err(PA_ERR_INVALID_ARG, "capacity too small");
+  if (!v->empty()) {
+    if (!dst) return set_err(PA_ERR_INVALID_ARG, "dst is NULL");
+    std::memcpy(dst, v->data(), v->size() * sizeof(int32_t));
+  }
+  return PA_OK;
+}
+
+size_t pa_plan_workspace_bytes(const pa_plan* plan) { return plan ? plan->ws_bytes : 0; }
+
+pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
+  const pa::HostPlan& hp = plan->hp;
+  if (hp.T == 0) return PA_OK;
+  if (!q || !kv_cache || !block_table || !out) return set_err(PA_ERR_INVALID_ARG, "q/kv_cache/block_table/out is NULL");
+  if (workspace_bytes < plan->ws_bytes) return set_err(PA_ERR_INVALID_ARG, "workspace too small");
+  if (plan->ws_bytes > 0 && !workspace) return set_err(PA_ERR_INVALID_ARG, "workspace is NULL");
+
+  const pa_params& p = hp.p;
+  pa::LaunchGeom g{};
+  g.H = p.num_heads;
+  g.Hkv = p.num_kv_heads;
+  g.g = p.num_heads / p.num_kv_heads;
+  g.D = p.head_size;
+  g.bs = p.block_size;
+  g.max_blocks = p.max_blocks_per_seq;
+  g.dtype = p.dtype;
+  g.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
+  g.ps = hp.ps;
+
+  pa::Tensors t{};
+  t.q = q;
+  t.kv = kv_cache;
+  t.block_table = block_table;
+  t.out = out;
+  t.lse = lse;
+  if (plan->ws_bytes > 0) {
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    t.ws_o = reinterpret_cast<float*>(w);
+    t.ws_lse = reinterpret_cast<float*>(w + align256((size_t)hp.num_partials * p.num_heads * p.head_size * sizeof(float)));
+  }
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return set_err(PA_ERR_HIP, "hipSetDevice failed");
+  const int e = pa::launch_forward(g, plan->ds, t, stream);
+  if (e != 0) return hip_err((hipError_t)e, "kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o_out,
+                          float* lse_out, int32_t num_tokens, int32_t num_heads, int32_t head_size, int32_t dtype,
+                          void* stream) {
+  g_err.clear();
+  if (num_tokens < 0 || num_heads < 1) return set_err(PA_ERR_INVALID_ARG, "num_tokens < 0 or num_heads < 1");
+  if (dtype != PA_BF16 && dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
+  if (head_size != 64 && head_size != 128) return set_err(PA_ERR_UNSUPPORTED, "head_size not built (64, 128)");
+  if (num_tokens == 0) return PA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  const int e = pa::launch_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out, num_tokens, num_heads, head_size,
+                                        dtype, stream);
+  if (e != 0) return hip_err((hipError_t)e, "kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int32_t seq_len, const pa_params* params,
+                       void* k_out, void* v_out, void* stream) {
+  g_err.clear();
+  if (!params) return set_err(PA_ERR_INVALID_ARG, "params is NULL");
+  if (seq_len < 0) return set_err(PA_ERR_INVALID_ARG, "seq_len < 0");
+  if (params->block_size < 16 || params->block_size % 16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "block size must be a positive multiple of 16");
+  if (params->num_kv_heads < 1 || params->head_size < 1 || params->head_size % 8 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "num_kv_heads >= 1 and head_size a positive multiple of 8 required");
+  if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
+  if (seq_len == 0) return PA_OK;
+  if (!kv_cache || !block_table_row || !k_out || !v_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  const int e = pa::launch_gather(kv_cache, block_table_row, seq_len, params->block_size, params->num_kv_heads,
+                                  params->head_size, params->dtype, k_out, v_out, stream);
+  if (e != 0) return hip_err((hipError_t)e, "kernel launch");
+  return PA_OK;
+}
+
+void pa_plan_destroy(pa_plan* plan) {
+  if (!plan) return;
+  if (plan->dev_buf) {
+    DeviceGuard guard(plan->device);
+    (void)hipFree(plan->dev_buf);
+  }
+  delete plan;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported";
+    case PA_ERR_HIP: return "HIP error";
+    case PA_ERR_OOM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+pa_status pa_profile_start(int32_t max_launches) {
+  g_err.clear();
+  if (max_launches < 1) return set_err(PA_ERR_INVALID_ARG, "max_launches < 1");
+  prof_release();
+  g_prof.pool.resize(2 * (size_t)max_launches);
+  for (auto& e : g_prof.pool) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      g_prof.pool.erase(std::remove(g_prof.pool.begin(), g_prof.pool.end(), nullptr), g_prof.pool.end());
+      prof_release();
+      return hip_err(r, "hipEventCreate");
+    }
+  }
+  g_prof.max = max_launches;
+  g_prof.active = true;
+  return PA_OK;
+}
+
+pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count) {
+  g_err.clear();
+  if (!g_prof.active) return set_err(PA_ERR_INVALID_ARG, "no profiling session on this thread");
+  std::map<std::string, std::pair<int, double>> agg;
+  std::vector<std::string> names;
+  pa_status st = PA_OK;
+  for (const ProfRec& r : g_prof.recs) {
+    hipError_t e = hipEventSynchronize(r.end);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.begin, r.end);
+    if (e != hipSuccess) {
+      st = hip_err(e, "hipEventElapsedTime");
+      break;
+    }
+    auto it = agg.find(r.name);
+    if (it == agg.end()) {
+      names.push_back(r.name);
+      agg[r.name] = {1, (double)ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  prof_release();
+  if (st != PA_OK) return st;
+  if (count) *count = (int32_t)names.size();
+  if ((int32_t)names.size() > capacity || (!out && !names.empty()))
+    return set_err(PA_ERR_INVALID_ARG, "capacity too small");
+  for (size_t i = 0; i < names.size(); ++i) {
+    std::memset(&out[i], 0, sizeof(pa_kernel_time));
+    std::snprintf(out[i].name, sizeof(out[i].name), "%s", names[i].c_str());
+    out[i].launches = agg[names[i]].first;
+    out[i].total_ms = agg[names[i]].second;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Internal types of libpagedattn: the schedule a plan holds and the launch
+// interface between the C ABI (api.cpp) and the kernels (kernels.hip).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/pagedattn.h"
+
+namespace pa {
+
+// One unit of attention work for one KV head (the KV head is the grid's y index).
+// Columns are (query position, query head) pairs: position n in [0, nrows) is
+// token row row0 + n.  Keys [kv_begin, kv_end) of block-table row `seq` are read;
+// with `causal` set, position n sees only keys t <= lim0 + n.
+struct WorkItem {
+  int32_t seq;
+  int32_t row0;
+  int32_t nrows;
+  int32_t lim0;
+  int32_t kv_begin;
+  int32_t kv_end;
+  int32_t slot;    // partial record = row_pbase[row] + slot when row_pbase[row] >= 0
+  int32_t causal;
+};
+static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+
+// A token row whose result is the LSE-merge of `count` partial records
+// starting at `pbase`.
+struct MergeRow {
+  int32_t row;
+  int32_t pbase;
+  int32_t count;
+  int32_t pad;
+};
+static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
+
+// Prefill tiling: a workgroup owns 128 columns = 8 tiles of 16.  Tile j holds
+// head (j / tiles_per_head) of the workgroup's head group and positions
+// 16 * (j % tiles_per_head) .. +15.
+struct PrefillShape {
+  int heads_per_wg;    // 1, 2, 4 or 8, divides g
+  int tiles_per_head;  // 8 / heads_per_wg
+  int rows_per_item;   // 16 * tiles_per_head
+  int head_groups;     // g / heads_per_wg
+};
+PrefillShape prefill_shape(int group);
+
+// Everything the kernels need besides the caller's tensors.
+struct LaunchGeom {
+  int H, Hkv, g, D, bs, max_blocks, dtype;
+  float scale_log2;  // scale * log2(e)
+  PrefillShape ps;
+};
+
+struct DeviceSchedule {
+  const WorkItem* decode;
+  int n_decode;
+  const WorkItem* prefill;
+  int n_prefill;
+  const WorkItem* prefix;
+  int n_prefix;
+  const MergeRow* merge;
+  int n_merge;
+  const int32_t* row_pbase;
+  int num_partials;
+};
+
+struct Tensors {
+  const void* q;
+  const void* kv;
+  const int32_t* block_table;
+  void* out;
+  float* lse;
+  float* ws_o;    // [num_partials, H, D]
+  float* ws_lse;  // [num_partials, H]
+};
+
+// Launchers (kernels.hip).  Each returns a HIP error code (0 = success).
+int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream);
+int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o,
+                        float* l, int n_tok, int n_heads, int head_size, int dtype, void* stream);
+int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,
+                  int dtype, void* k_out, void* v_out, void* stream);
+
+// Launch bookkeeping for pa_profile_* (api.cpp).
+void profile_before(const char* name, void* stream);
+void profile_after(void* stream);
+
+// Host planner (planner.cpp): validates and builds the schedule.
+struct HostPlan {
+  pa_params p{};
+  int32_t T = 0;
+  std::vector<int32_t> order, is_decode, prefix_blocks, row_partials, row_pbase;
+  std::vector<WorkItem> decode_items, prefill_items, prefix_items;
+  std::vector<MergeRow> merges;
+  pa_plan_info info{};
+  PrefillShape ps{};
+  int num_partials = 0;
+};
+
+// Returns PA_OK or an error with `err` filled in.
+pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t* seq_lens,
+                          const int32_t* block_table, int num_cus, HostPlan& out, std::string& err);
+
+}  // namespace pa

@@ -1,0 +1,730 @@
+// HIP kernels of libpagedattn for gfx950 (CDNA4, wave64).
+//
+// Both attention kernels compute, for a tile of up to 16 "columns" (query
+// heads of one decode token, or query positions of one head), the transposed
+// scores S^T = K Q^T with bf16 MFMA 16x16x32 (fp32 MFMA 16x16x4 for fp32 data),
+// an online softmax per column, and O^T += V^T P^T with the same MFMA.  Working
+// on the transposes keeps every operand in registers:
+//   * S^T's accumulator layout (lane (qd, r) holds keys 4qd..4qd+3 of column r)
+//     is already the B-operand layout P^T needs for the second product, once two
+//     16-key tiles are concatenated along the contraction;
+//   * V^T as the A operand needs, per lane, 8 keys of one head-dimension row.
+//     Head dimension d = (D/16)*m + dt is assigned to row m of output tile dt,
+//     so each lane loads D/16 contiguous elements of 8 key rows (16-byte loads
+//     for D = 128 bf16, whole 256-byte rows per 16 lanes) and transposes the
+//     8 x (D/16) block in registers.
+// Decode (one query token, all heads of a KV group as the columns) streams K/V
+// straight from HBM into registers; prefill stages 64-key K/V blocks in LDS and
+// shares them among the four waves of a workgroup (the query heads of one KV
+// head).  Partial results of split KV ranges and of the cascade prefix are
+// merged by their natural-log LSE.
+//
+// Sources: «El especialista del plato estrella», §Por qué prefill y decode son
+// problemas opuestos (decode streams the whole KV and is bandwidth-bound,
+// prefill is matrix-unit-bound), §Cómo lee el backend el KV paginado (gather
+// through the block table), §Qué aporta FlashInfer (cascade);
+// «AttentionBackend: capa de abstracción», §Límites y fallos (LSE base).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+// Lazy rescaling: the running max used for exponentiation is only raised when
+// a block's max exceeds it by more than this (log2 units), so P <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// ---------------------------------------------------------------------------
+// Element-type operations.  A Frag is the 8 contraction elements one lane
+// supplies to a 16x16 MFMA step of K = 32 (bf16: one 16x16x32; fp32: eight
+// 16x16x4, step e taking element e of every lane).
+// ---------------------------------------------------------------------------
+template <typename T, int VE>
+struct Ops;
+
+template <int VE>
+struct Ops<uint16_t, VE> {
+  struct Frag {
+    u32x4 v;
+  };
+  struct VRaw {  // VE contiguous elements of one key row
+    uint32_t w[VE / 2];
+  };
+  static __device__ __forceinline__ Frag zero() { return Frag{u32x4{0u, 0u, 0u, 0u}}; }
+  static __device__ __forceinline__ Frag load(const uint16_t* p) {
+    return Frag{*reinterpret_cast<const u32x4*>(p)};
+  }
+  static __device__ __forceinline__ void mma(f32x4& c, const Frag& a, const Frag& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                __builtin_bit_cast(bf16x8_t, b.v), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ VRaw load_v(const uint16_t* p) {
+    VRaw r;
+    if constexpr (VE == 8) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+      r.w[0] = x[0];
+      r.w[1] = x[1];
+      r.w[2] = x[2];
+      r.w[3] = x[3];
+    } else {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      r.w[0] = x[0];
+      r.w[1] = x[1];
+    }
+    return r;
+  }
+  // Element dt of each of the 8 key rows, packed in key order.
+  template <int DT>
+  static __device__ __forceinline__ Frag vtrans(const VRaw* vr) {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = vr[2 * j].w[DT >> 1], b = vr[2 * j + 1].w[DT >> 1];
+      f.v[j] = (DT & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    return f;
+  }
+  static __device__ __forceinline__ Frag pack_p(const float* p) {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+    return f;
+  }
+  // Store VE consecutive output values.
+  static __device__ __forceinline__ void store_out(uint16_t* dst, const float* v) {
+    if constexpr (VE == 8) {
+      u32x4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+      *reinterpret_cast<u32x4*>(dst) = x;
+    } else {
+      u32x2 x;
+      x[0] = pack_bf16x2(v[0], v[1]);
+      x[1] = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(dst) = x;
+    }
+  }
+};
+
+template <int VE>
+struct Ops<float, VE> {
+  struct Frag {
+    float v[8];
+  };
+  struct VRaw {
+    float w[VE];
+  };
+  static __device__ __forceinline__ Frag zero() {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = 0.f;
+    return f;
+  }
+  static __device__ __forceinline__ Frag load(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return Frag{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
+  }
+  static __device__ __forceinline__ void mma(f32x4& c, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ VRaw load_v(const float* p) {
+    VRaw r;
+#pragma unroll
+    for (int k = 0; k < VE; k += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + k);
+      r.w[k] = x[0];
+      r.w[k + 1] = x[1];
+      r.w[k + 2] = x[2];
+      r.w[k + 3] = x[3];
+    }
+    return r;
+  }
+  template <int DT>
+  static __device__ __forceinline__ Frag vtrans(const VRaw* vr) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = vr[e].w[DT];
+    return f;
+  }
+  static __device__ __forceinline__ Frag pack_p(const float* p) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = p[e];
+    return f;
+  }
+  static __device__ __forceinline__ void store_out(float* dst, const float* v) {
+#pragma unroll
+    for (int k = 0; k < VE; k += 4)
+      *reinterpret_cast<f32x4*>(dst + k) = f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]};
+  }
+};
+
+// Compile-time loop helper (the transposed-V index must be a constant).
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
+struct KArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* bt;
+  void* out;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  const WorkItem* items;
+  const int32_t* row_pbase;
+  int n_items;
+  int H, Hkv, g, bs, max_blocks;
+  int head_groups;     // grid.y = Hkv * head_groups
+  int heads_per_grp;   // decode: 16 columns; prefill: heads per workgroup
+  int tiles_per_head;  // prefill only
+  float scale_log2;
+};
+
+// Online-softmax update of one 16-column tile with the 8 scores (log2 units,
+// masked = -inf) a lane holds for its column.  Returns P in `p`.
+template <int VE>
+__device__ __forceinline__ void softmax_step(float (&x)[8], float& m_run, float& l_run, f32x4 (&o)[VE],
+                                             float (&p)[8]) {
+  float mb = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const bool need = mb > m_run + kRescaleThreshold;
+  if (__any(need)) {
+    const float m_new = need ? mb : m_run;
+    const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;  // m_run = -inf -> 0
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) o[dt] *= alpha;
+  }
+  const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = fast_exp2(x[e] - mref);
+    s += p[e];
+  }
+  l_run += s;
+}
+
+// Normalise and write one column's result: to out/lse directly, or as a
+// partial record (fp32 o and lse) when the row merges several parts.
+template <typename T, int VE>
+__device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int slot, int qd,
+                                             const f32x4 (&o)[VE], float m_run, float l_run) {
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  constexpr int D = 16 * VE;
+  const int pb = a.row_pbase[row];
+  float v[VE];
+  if (pb < 0) {
+    T* dst = static_cast<T*>(a.out) + ((int64_t)row * a.H + h) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt) v[dt] = o[dt][i] * inv;
+      Ops<T, VE>::store_out(dst + VE * (4 * qd + i), v);
+    }
+    if (qd == 0 && a.lse) a.lse[(int64_t)row * a.H + h] = lse;
+  } else {
+    const int64_t rec = (int64_t)(pb + slot) * a.H + h;
+    float* dst = a.ws_o + rec * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int dt = 0; dt < VE; ++dt) v[dt] = o[dt][i] * inv;
+      Ops<float, VE>::store_out(dst + VE * (4 * qd + i), v);
+    }
+    if (qd == 0) a.ws_lse[rec] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one wave per work item (a KV range of one sequence for one KV head);
+// the columns are the query heads of that KV head (up to 16 per head group).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) decode_kernel(KArgs a) {
+  constexpr int VE = D / 16;
+  constexpr int KS = D / 32;
+  using O = Ops<T, VE>;
+  using Frag = typename O::Frag;
+  using VRaw = typename O::VRaw;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int idx = blockIdx.x * 4 + wave;
+  if (idx >= a.n_items) return;
+  const int kvh = blockIdx.y / a.head_groups;
+  const int hgrp = blockIdx.y % a.head_groups;
+  const WorkItem it = a.items[idx];
+  const int r = lane & 15, qd = lane >> 4;
+
+  const T* q = static_cast<const T*>(a.q);
+  const T* kv = static_cast<const T*>(a.kv);
+
+  // Q^T operand: column r = query head kvh * g + hgrp * 16 + r
+  const int hcol = hgrp * 16 + r;
+  const bool colv = hcol < a.g;
+  const int head = kvh * a.g + (colv ? hcol : 0);
+  Frag qf[KS];
+  {
+    const T* qp = q + ((int64_t)it.row0 * a.H + head) * D + 8 * qd;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = colv ? O::load(qp + 32 * kk) : O::zero();
+  }
+
+  const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
+  const int64_t slot_stride = (int64_t)a.Hkv * D;
+  const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
+  const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
+  const T* kvh_base = kv + (int64_t)kvh * D;
+  const int kv_end = it.kv_end;
+
+  f32x4 o[VE];
+#pragma unroll
+  for (int dt = 0; dt < VE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
+    // One physical block per 16-key tile.  Keys past kv_end are clamped to the
+    // last valid key (so only pool rows of this sequence are read) and masked.
+    const T* pb[2];
+    int pst[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int ks = min(t0 + 16 * tt, kv_end - 1);
+      const int blk = ks / a.bs;
+      pst[tt] = blk * a.bs;
+      pb[tt] = kvh_base + (int64_t)btrow[blk] * blk_stride;
+    }
+    Frag kf[2][KS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int key = min(t0 + 16 * tt + r, kv_end - 1);
+      const T* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
+    }
+    VRaw vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tt = e >> 2;
+      const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
+      vr[e] = O::load_v(pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r);
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) O::mma(s[tt], kf[tt][kk], qf[kk]);
+    }
+    float x[8];
+    const bool full = t0 + 32 <= kv_end;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = t0 + 16 * (e >> 2) + 4 * qd + (e & 3);
+      const float sv = s[e >> 2][e & 3] * a.scale_log2;
+      x[e] = (full || key < kv_end) ? sv : -INFINITY;
+    }
+    float p[8];
+    softmax_step<VE>(x, m_run, l_run, o, p);
+    const Frag pf = O::pack_p(p);
+    static_for<VE>([&](auto dtc) {
+      constexpr int dt = decltype(dtc)::value;
+      const Frag vf = O::template vtrans<dt>(vr);
+      O::mma(o[dt], vf, pf);
+    });
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill (and the cascade prefix pass): a workgroup of 4 waves owns 128
+// columns, 8 tiles of 16 (tile j: head j / tiles_per_head of the head group,
+// positions 16 * (j % tiles_per_head) ..); wave w takes tiles 2w and 2w + 1.
+// 64-key (32 for fp32) K/V blocks are gathered into LDS once per workgroup.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
+  constexpr int VE = D / 16;
+  constexpr int KS = D / 32;
+  constexpr int KT = sizeof(T) == 2 ? 64 : 32;          // keys per LDS block
+  constexpr int ROWB = D * (int)sizeof(T) + 16;         // padded LDS row, bytes
+  constexpr int CPR = D * (int)sizeof(T) / 16;          // 16-byte chunks per key row
+  constexpr int RPI = 256 / CPR;                        // key rows per load step
+  constexpr int NLD = KT / RPI;                         // load steps per block
+  using O = Ops<T, VE>;
+  using Frag = typename O::Frag;
+  using VRaw = typename O::VRaw;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * KT * ROWB];
+  unsigned char* const ldsK = lds;
+  unsigned char* const ldsV = lds + KT * ROWB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const WorkItem it = a.items[blockIdx.x];
+  const int kvh = blockIdx.y / a.head_groups;
+  const int hgrp = blockIdx.y % a.head_groups;
+  const int r = lane & 15, qd = lane >> 4;
+
+  const T* q = static_cast<const T*>(a.q);
+  const T* kv = static_cast<const T*>(a.kv);
+  const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
+
+  // the wave's two column tiles
+  int head[2], pos0[2], lim[2], tile_min_lim[2];
+  Frag qf[2][KS];
+  int wave_max_lim = -1;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int j = 2 * wave + c;
+    head[c] = kvh * a.g + hgrp * a.heads_per_grp + j / a.tiles_per_head;
+    pos0[c] = 16 * (j % a.tiles_per_head);
+    const int pos = pos0[c] + r;
+    const bool valid = pos < it.nrows;
+    const T* qp = q + ((int64_t)(it.row0 + (valid ? pos : 0)) * a.H + head[c]) * D + 8 * qd;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[c][kk] = valid ? O::load(qp + 32 * kk) : O::zero();
+    lim[c] = it.causal ? it.lim0 + pos : kv_hi - 1;
+    tile_min_lim[c] = it.causal ? it.lim0 + pos0[c] : kv_hi - 1;
+    const int last_pos = min(pos0[c] + 15, it.nrows - 1);
+    const int tmax = it.causal ? it.lim0 + last_pos : kv_hi - 1;
+    if (pos0[c] < it.nrows) wave_max_lim = max(wave_max_lim, tmax);
+  }
+
+  const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
+  const int64_t slot_stride = (int64_t)a.Hkv * D;
+  const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
+  const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
+  const T* kvh_base = kv + (int64_t)kvh * D;
+  const int chunk = tid % CPR;
+
+  u32x4 stK[NLD], stV[NLD];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int key = min(kb + tid / CPR + j * RPI, kv_hi - 1);
+      const int blk = key / a.bs;
+      const T* base = kvh_base + (int64_t)btrow[blk] * blk_stride + (int64_t)(key - blk * a.bs) * slot_stride;
+      stK[j] = reinterpret_cast<const u32x4*>(base)[chunk];
+      stV[j] = reinterpret_cast<const u32x4*>(base + v_half)[chunk];
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int kr = tid / CPR + j * RPI;
+      *reinterpret_cast<u32x4*>(ldsK + kr * ROWB + 16 * chunk) = stK[j];
+      *reinterpret_cast<u32x4*>(ldsV + kr * ROWB + 16 * chunk) = stV[j];
+    }
+  };
+
+  f32x4 o[2][VE];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (kv_lo < kv_hi) {
+    gload(kv_lo);
+    lstore();
+  }
+  __syncthreads();
+  for (int kb = kv_lo; kb < kv_hi; kb += KT) {
+    const bool more = kb + KT < kv_hi;
+    if (more) gload(kb + KT);
+#pragma unroll
+    for (int sb = 0; sb < KT / 32; ++sb) {
+      const int k0 = kb + 32 * sb;
+      if (k0 >= kv_hi || k0 > wave_max_lim) break;
+      f32x4 s[2][2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        s[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[1][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* kr = ldsK + (32 * sb + 16 * tt + r) * ROWB + (8 * qd) * (int)sizeof(T);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const Frag kf = O::load(reinterpret_cast<const T*>(kr + 32 * kk * (int)sizeof(T)));
+          O::mma(s[0][tt], kf, qf[0][kk]);
+          O::mma(s[1][tt], kf, qf[1][kk]);
+        }
+      }
+      VRaw vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kr = 32 * sb + 16 * (e >> 2) + 4 * qd + (e & 3);
+        vr[e] = O::load_v(reinterpret_cast<const T*>(ldsV + kr * ROWB + VE * r * (int)sizeof(T)));
+      }
+      Frag pf[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[8];
+        const bool full = (k0 + 31 <= tile_min_lim[c]) && (k0 + 32 <= kv_hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = k0 + 16 * (e >> 2) + 4 * qd + (e & 3);
+          const float sv = s[c][e >> 2][e & 3] * a.scale_log2;
+          x[e] = (full || (key <= lim[c] && key < kv_hi)) ? sv : -INFINITY;
+        }
+        float p[8];
+        softmax_step<VE>(x, m_run[c], l_run[c], o[c], p);
+        pf[c] = O::pack_p(p);
+      }
+      static_for<VE>([&](auto dtc) {
+        constexpr int dt = decltype(dtc)::value;
+        const Frag vf = O::template vtrans<dt>(vr);
+        O::mma(o[0][dt], vf, pf[0]);
+        O::mma(o[1][dt], vf, pf[1]);
+      });
+    }
+    __syncthreads();
+    if (more) {
+      lstore();
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float l = l_run[c];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int pos = pos0[c] + r;
+    if (pos < it.nrows) write_column<T, VE>(a, it.row0 + pos, head[c], it.slot, qd, o[c], m_run[c], l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of several partial records per row by their LSE.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, f32x4 v) {
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, f32x4 v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* src);
+template <>
+__device__ __forceinline__ f32x4 load4<uint16_t>(const uint16_t* src) {
+  const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+  return f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xFFFF0000u), __uint_as_float(x[1] << 16),
+               __uint_as_float(x[1] & 0xFFFF0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float* src) {
+  return *reinterpret_cast<const f32x4*>(src);
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, const float* ws_o, const float* ws_lse,
+                                                    T* out, float* lse, int H) {
+  const MergeRow mr = rows[blockIdx.x];
+  constexpr int C4 = D / 4;
+  for (int idx = threadIdx.x; idx < H * C4; idx += blockDim.x) {
+    const int h = idx / C4, c = idx % C4;
+    float mx = -INFINITY;
+    for (int s = 0; s < mr.count; ++s) mx = fmaxf(mx, ws_lse[(int64_t)(mr.pbase + s) * H + h]);
+    const float ms = (mx == -INFINITY) ? 0.f : mx;
+    float tot = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < mr.count; ++s) {
+      const int64_t rec = (int64_t)(mr.pbase + s) * H + h;
+      const float w = __expf(ws_lse[rec] - ms);
+      tot += w;
+      acc += w * *reinterpret_cast<const f32x4*>(ws_o + rec * D + 4 * c);
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    store4<T>(out + ((int64_t)mr.row * H + h) * D + 4 * c, acc * inv);
+    if (c == 0 && lse) lse[(int64_t)mr.row * H + h] = tot > 0.f ? ms + logf(tot) : -INFINITY;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) merge_states_kernel(const T* oa, const float* la, const T* ob, const float* lb,
+                                                           T* o, float* l, int64_t n_vec4, int D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_vec4) return;
+  const int c4 = D / 4;
+  const int64_t th = i / c4;  // token * H + head
+  const float xa = la[th], xb = lb[th];
+  const float mx = fmaxf(xa, xb);
+  const float ms = (mx == -INFINITY) ? 0.f : mx;
+  const float wa = __expf(xa - ms), wb = __expf(xb - ms);
+  const float tot = wa + wb;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const f32x4 va = load4<T>(oa + i * 4), vb = load4<T>(ob + i * 4);
+  store4<T>(o + i * 4, (wa * inv) * va + (wb * inv) * vb);
+  if (l && (i % c4) == 0) l[th] = tot > 0.f ? ms + logf(tot) : -INFINITY;
+}
+
+__global__ void __launch_bounds__(256) gather_kernel(const unsigned char* kv, const int32_t* bt_row, int seq_len,
+                                                     int bs, int64_t row_bytes, unsigned char* k_out,
+                                                     unsigned char* v_out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t cpt = row_bytes / 16;  // 16-byte chunks per token (all KV heads)
+  if (i >= (int64_t)seq_len * cpt) return;
+  const int t = (int)(i / cpt);
+  const int64_t c = i % cpt;
+  const int64_t blk = bt_row[t / bs];
+  const unsigned char* src = kv + (blk * 2 * bs + t % bs) * row_bytes + 16 * c;
+  reinterpret_cast<u32x4*>(k_out + (int64_t)t * row_bytes)[c] = *reinterpret_cast<const u32x4*>(src);
+  reinterpret_cast<u32x4*>(v_out + (int64_t)t * row_bytes)[c] =
+      *reinterpret_cast<const u32x4*>(src + (int64_t)bs * row_bytes);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers
+// ---------------------------------------------------------------------------
+template <typename K, typename... Args>
+int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args... args) {
+  if (grid.x == 0 || grid.y == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  profile_before(name, stream);
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  const hipError_t e = hipGetLastError();
+  profile_after(stream);
+  return (int)e;
+}
+
+template <typename T, int D>
+int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream, const char* tag) {
+  KArgs a{};
+  a.q = t.q;
+  a.kv = t.kv;
+  a.bt = t.block_table;
+  a.out = t.out;
+  a.lse = t.lse;
+  a.ws_o = t.ws_o;
+  a.ws_lse = t.ws_lse;
+  a.row_pbase = s.row_pbase;
+  a.H = g.H;
+  a.Hkv = g.Hkv;
+  a.g = g.g;
+  a.bs = g.bs;
+  a.max_blocks = g.max_blocks;
+  a.scale_log2 = g.scale_log2;
+  char name[48];
+  int err = 0;
+
+  // cascade prefix pass (all rows against the shared prefix), then decodes,
+  // then prefills, then the LSE merge of rows with several parts
+  if (s.n_prefix > 0) {
+    KArgs p = a;
+    p.items = s.prefix;
+    p.n_items = s.n_prefix;
+    p.head_groups = g.ps.head_groups;
+    p.heads_per_grp = g.ps.heads_per_wg;
+    p.tiles_per_head = g.ps.tiles_per_head;
+    snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
+    err = launch(name, prefill_kernel<T, D>, dim3(s.n_prefix, g.Hkv * g.ps.head_groups), dim3(256), stream, p);
+    if (err) return err;
+  }
+  if (s.n_decode > 0) {
+    KArgs d = a;
+    d.items = s.decode;
+    d.n_items = s.n_decode;
+    d.head_groups = (g.g + 15) / 16;
+    d.heads_per_grp = 16;
+    d.tiles_per_head = 1;
+    snprintf(name, sizeof(name), "decode_%s_d%d", tag, D);
+    err = launch(name, decode_kernel<T, D>, dim3((s.n_decode + 3) / 4, g.Hkv * d.head_groups), dim3(256), stream, d);
+    if (err) return err;
+  }
+  if (s.n_prefill > 0) {
+    KArgs p = a;
+    p.items = s.prefill;
+    p.n_items = s.n_prefill;
+    p.head_groups = g.ps.head_groups;
+    p.heads_per_grp = g.ps.heads_per_wg;
+    p.tiles_per_head = g.ps.tiles_per_head;
+    snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
+    err = launch(name, prefill_kernel<T, D>, dim3(s.n_prefill, g.Hkv * g.ps.head_groups), dim3(256), stream, p);
+    if (err) return err;
+  }
+  if (s.n_merge > 0) {
+    snprintf(name, sizeof(name), "merge_%s_d%d", tag, D);
+    err = launch(name, merge_kernel<T, D>, dim3(s.n_merge), dim3(256), stream, s.merge,
+                 (const float*)t.ws_o, (const float*)t.ws_lse, static_cast<T*>(t.out), t.lse, g.H);
+  }
+  return err;
+}
+
+}  // namespace
+
+int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream) {
+  if (g.dtype == PA_BF16) {
+    return g.D == 128 ? forward_impl<uint16_t, 128>(g, s, t, stream, "bf16")
+                      : forward_impl<uint16_t, 64>(g, s, t, stream, "bf16");
+  }
+  return g.D == 128 ? forward_impl<float, 128>(g, s, t, stream, "fp32") : forward_impl<float, 64>(g, s, t, stream, "fp32");
+}
+
+int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,
+                        int n_heads, int head_size, int dtype, void* stream) {
+  const int64_t n4 = (int64_t)n_tok * n_heads * head_size / 4;
+  if (n4 == 0) return 0;
+  const dim3 grid((unsigned)((n4 + 255) / 256));
+  if (dtype == PA_BF16)
+    return launch("merge_states_bf16", merge_states_kernel<uint16_t>, grid, dim3(256), stream,
+                  (const uint16_t*)oa, la, (const uint16_t*)ob, lb, (uint16_t*)o, l, n4, head_size);
+  return launch("merge_states_fp32", merge_states_kernel<float>, grid, dim3(256), stream, (const float*)oa, la,
+                (const float*)ob, lb, (float*)o, l, n4, head_size);
+}
+
+int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D, int dtype, void* k_out,
+                  void* v_out, void* stream) {
+  const int64_t row_bytes = (int64_t)Hkv * D * (dtype == PA_BF16 ? 2 : 4);
+  const int64_t n = (int64_t)seq_len * (row_bytes / 16);
+  if (n == 0) return 0;
+  return launch("gather", gather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), stream,
+                (const unsigned char*)kv, bt_row, seq_len, bs, row_bytes, (unsigned char*)k_out,
+                (unsigned char*)v_out);
+}
+
+}  // namespace pa

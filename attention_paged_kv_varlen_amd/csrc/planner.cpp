@@ -1,0 +1,274 @@
+// Host metadata builder: validates a batch and turns it into work lists.
+//
+// «FlashAttention y FlashInfer», §Responsabilidades: the builder splits the
+// batch into decodes and prefills, fills the per-sequence metadata and computes
+// the kernel schedule ahead of time; the FlashInfer builder also reorders the
+// batch so decodes come first (closing paragraph of §Flujo de datos).  Here the
+// order is recorded (a stable partition) and the schedule walks it: decode work
+// items first, then prefill work items.  Output rows keep the caller's order.
+//
+// «El especialista del plato estrella», §Qué aporta FlashInfer: with a shared
+// prefix the prefix attention is scheduled once for all query rows and merged
+// with each sequence's suffix attention through the LSE.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace pa {
+
+PrefillShape prefill_shape(int group) {
+  PrefillShape s{};
+  int hpw = 1;
+  for (int c : {8, 4, 2}) {
+    if (group % c == 0) {
+      hpw = c;
+      break;
+    }
+  }
+  s.heads_per_wg = hpw;
+  s.tiles_per_head = 8 / hpw;
+  s.rows_per_item = 16 * s.tiles_per_head;
+  s.head_groups = group / hpw;
+  return s;
+}
+
+namespace {
+
+constexpr int kPrefixChunk = 1024;  // shared-prefix keys per cascade work item
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+pa_status fail(std::string& err, pa_status st, const char* fmt, long long a = 0, long long b = 0,
+               long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+  err = buf;
+  return st;
+}
+
+}  // namespace
+
+pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t* seq_lens,
+                          const int32_t* block_table, int num_cus, HostPlan& hp, std::string& err) {
+  // ---- validation («FlashAttention y FlashInfer», §Límites y fallos;
+  //      «AttentionBackend: capa de abstracción», §Límites y fallos)
+  const int B = p.num_seqs;
+  if (B < 0) return fail(err, PA_ERR_INVALID_ARG, "num_seqs %lld < 0", B);
+  if (!qsl || !seq_lens) return fail(err, PA_ERR_INVALID_ARG, "query_start_loc / seq_lens is NULL");
+  if (p.num_heads < 1 || p.num_kv_heads < 1)
+    return fail(err, PA_ERR_INVALID_ARG, "num_heads %lld / num_kv_heads %lld must be >= 1", p.num_heads,
+                p.num_kv_heads);
+  if (p.num_heads % p.num_kv_heads != 0)
+    return fail(err, PA_ERR_INVALID_ARG, "num_heads %lld is not a multiple of num_kv_heads %lld",
+                p.num_heads, p.num_kv_heads);
+  if (p.block_size < 16 || p.block_size % 16 != 0)
+    return fail(err, PA_ERR_INVALID_ARG, "block_size %lld must be a positive multiple of 16", p.block_size);
+  if (p.head_size != 64 && p.head_size != 128)
+    return fail(err, PA_ERR_UNSUPPORTED, "head_size %lld not built (64, 128)", p.head_size);
+  if (p.dtype != PA_BF16 && p.dtype != PA_FP32)
+    return fail(err, PA_ERR_UNSUPPORTED, "dtype %lld not built (PA_BF16, PA_FP32)", p.dtype);
+  if (p.num_blocks < 1) return fail(err, PA_ERR_INVALID_ARG, "num_blocks %lld < 1", p.num_blocks);
+  if (p.max_blocks_per_seq < 1)
+    return fail(err, PA_ERR_INVALID_ARG, "max_blocks_per_seq %lld < 1", p.max_blocks_per_seq);
+  if (p.causal != 0 && p.causal != 1) return fail(err, PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(p.scale)) return fail(err, PA_ERR_INVALID_ARG, "scale is not finite");
+  if (p.kv_split_tokens < 0 || p.kv_split_tokens % 32 != 0)
+    return fail(err, PA_ERR_INVALID_ARG, "kv_split_tokens %lld must be 0 or a positive multiple of 32",
+                p.kv_split_tokens);
+  if (p.common_prefix_len < 0) return fail(err, PA_ERR_INVALID_ARG, "common_prefix_len < 0");
+  if (qsl[0] != 0) return fail(err, PA_ERR_INVALID_ARG, "query_start_loc[0] = %lld, must be 0", qsl[0]);
+
+  const int bs = p.block_size;
+  const int mb = p.max_blocks_per_seq;
+  for (int b = 0; b < B; ++b) {
+    const int64_t qb = (int64_t)qsl[b + 1] - qsl[b];
+    if (qb < 1)
+      return fail(err, PA_ERR_INVALID_ARG, "sequence %lld has %lld query tokens (need >= 1)", b, qb);
+    if (seq_lens[b] < qb)
+      return fail(err, PA_ERR_INVALID_ARG, "sequence %lld: seq_len %lld < query tokens %lld", b,
+                  seq_lens[b], qb);
+    if (ceil_div(seq_lens[b], bs) > mb)
+      return fail(err, PA_ERR_INVALID_ARG, "sequence %lld needs %lld blocks > max_blocks_per_seq %lld", b,
+                  ceil_div(seq_lens[b], bs), mb);
+    if (block_table) {
+      const int nb = (int)ceil_div(seq_lens[b], bs);
+      for (int j = 0; j < nb; ++j) {
+        const int32_t id = block_table[(int64_t)b * mb + j];
+        if (id < 0 || id >= p.num_blocks)
+          return fail(err, PA_ERR_INVALID_ARG, "block_table[%lld][%lld] = %lld outside the pool", b, j, id);
+      }
+    }
+  }
+  if (B > 0 && (int64_t)qsl[B] > INT32_MAX / 2)
+    return fail(err, PA_ERR_INVALID_ARG, "too many tokens");
+
+  const int P = p.common_prefix_len;
+  if (P > 0) {
+    if (!block_table) return fail(err, PA_ERR_INVALID_ARG, "cascade (common_prefix_len > 0) needs block_table");
+    if (P % bs != 0)
+      return fail(err, PA_ERR_INVALID_ARG, "common_prefix_len %lld is not a multiple of block_size %lld", P, bs);
+    for (int b = 0; b < B; ++b) {
+      const int ctx = seq_lens[b] - (qsl[b + 1] - qsl[b]);
+      if (ctx < P)
+        return fail(err, PA_ERR_INVALID_ARG, "common_prefix_len %lld exceeds the context %lld of sequence %lld",
+                    P, ctx, b);
+      for (int j = 0; j < P / bs; ++j)
+        if (block_table[(int64_t)b * mb + j] != block_table[j])
+          return fail(err, PA_ERR_INVALID_ARG, "prefix block %lld of sequence %lld differs from sequence 0", j, b);
+    }
+  }
+
+  // ---- metadata: decode / prefill split, decode-first stable order
+  hp = HostPlan{};
+  hp.p = p;
+  const int H = p.num_heads, Hkv = p.num_kv_heads, g = H / Hkv;
+  hp.T = B > 0 ? qsl[B] : 0;
+  hp.order.reserve(B);
+  hp.is_decode.resize(B);
+  int nd = 0, ndt = 0, np = 0, npt = 0;
+  for (int b = 0; b < B; ++b) {
+    const int qb = qsl[b + 1] - qsl[b];
+    hp.is_decode[b] = qb == 1;
+    if (qb == 1) {
+      hp.order.push_back(b);
+      ++nd;
+      ndt += 1;
+    }
+  }
+  for (int b = 0; b < B; ++b) {
+    const int qb = qsl[b + 1] - qsl[b];
+    if (qb != 1) {
+      hp.order.push_back(b);
+      ++np;
+      npt += qb;
+    }
+  }
+  if (P > 0) hp.prefix_blocks.assign(block_table, block_table + P / bs);
+
+  // ---- schedule
+  hp.ps = prefill_shape(g);
+  const int QB = hp.ps.rows_per_item;
+  const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
+  const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
+
+  // decode KV chunk: explicit, or sized so that the decode work spreads over
+  // several waves per CU (items x Hkv ~ 32 per CU) without tiny items.
+  int64_t dec_tokens = 0;
+  for (int i = 0; i < nd; ++i) dec_tokens += seq_lens[hp.order[i]] - P;
+  int split = p.kv_split_tokens;
+  if (split == 0) {
+    const int64_t target_items = std::max<int64_t>(1, (int64_t)32 * std::max(num_cus, 1) / Hkv);
+    split = (int)std::min<int64_t>(8192, std::max<int64_t>(256, round_up(ceil_div(dec_tokens, target_items), 32)));
+  }
+
+  std::vector<int32_t> contrib(hp.T, 0);
+  int64_t dec_read = 0, pre_read = 0, pfx_read = 0;
+  for (int oi = 0; oi < B; ++oi) {
+    const int b = hp.order[oi];
+    const int qb = qsl[b + 1] - qsl[b];
+    const int L = seq_lens[b];
+    const int ctx = L - qb;
+    if (qb == 1) {
+      const int span = L - P;
+      const int n = (int)ceil_div(span, split);
+      const int part = (int)round_up(ceil_div(span, n), 32);
+      // n parts of equal size (multiple of 32, at most `split`): since
+      // (n - 1) * part <= (n - 1) * split < span, every part is non-empty.
+      for (int j = 0; j < n; ++j) {
+        WorkItem it{};
+        it.seq = b;
+        it.row0 = qsl[b];
+        it.nrows = 1;
+        it.lim0 = L - 1;
+        it.kv_begin = P + j * part;
+        it.kv_end = std::min(L, P + (j + 1) * part);
+        it.slot = n_pc + j;
+        it.causal = 0;
+        hp.decode_items.push_back(it);
+        dec_read += it.kv_end - it.kv_begin;
+      }
+      contrib[qsl[b]] = n_pc + n;
+    } else {
+      for (int i0 = 0; i0 < qb; i0 += QB) {
+        WorkItem it{};
+        it.seq = b;
+        it.row0 = qsl[b] + i0;
+        it.nrows = std::min(QB, qb - i0);
+        it.lim0 = ctx + i0;
+        it.kv_begin = P;
+        it.kv_end = p.causal ? std::min(L, ctx + i0 + it.nrows) : L;
+        it.slot = n_pc;
+        it.causal = p.causal;
+        hp.prefill_items.push_back(it);
+        pre_read += (int64_t)(it.kv_end - it.kv_begin) * hp.ps.head_groups;
+      }
+      for (int r = qsl[b]; r < qsl[b + 1]; ++r) contrib[r] = n_pc + 1;
+    }
+  }
+  if (P > 0) {
+    for (int r0 = 0; r0 < hp.T; r0 += QB) {
+      for (int j = 0; j < n_pc; ++j) {
+        WorkItem it{};
+        it.seq = 0;
+        it.row0 = r0;
+        it.nrows = std::min(QB, hp.T - r0);
+        it.lim0 = 0;
+        it.kv_begin = j * pc_len;
+        it.kv_end = std::min(P, (j + 1) * pc_len);
+        it.slot = j;
+        it.causal = 0;
+        if (it.kv_begin >= it.kv_end) continue;
+        hp.prefix_items.push_back(it);
+        pfx_read += (int64_t)(it.kv_end - it.kv_begin) * hp.ps.head_groups;
+      }
+    }
+  }
+  // longest work first, so the tail of each launch is short items
+  auto longer = [](const WorkItem& a, const WorkItem& b) {
+    const int64_t ca = (int64_t)(a.kv_end - a.kv_begin), cb = (int64_t)(b.kv_end - b.kv_begin);
+    return ca > cb;
+  };
+  std::stable_sort(hp.decode_items.begin(), hp.decode_items.end(), longer);
+  std::stable_sort(hp.prefill_items.begin(), hp.prefill_items.end(), longer);
+
+  // partial records: one range per row that merges several contributions
+  hp.row_pbase.assign(hp.T, -1);
+  hp.row_partials.assign(hp.T, 0);
+  int next = 0;
+  for (int r = 0; r < hp.T; ++r) {
+    if (contrib[r] > 1) {
+      hp.row_pbase[r] = next;
+      hp.row_partials[r] = contrib[r];
+      hp.merges.push_back(MergeRow{r, next, contrib[r], 0});
+      next += contrib[r];
+    }
+  }
+  hp.num_partials = next;
+
+  pa_plan_info& in = hp.info;
+  in.num_seqs = B;
+  in.num_tokens = hp.T;
+  in.num_decodes = nd;
+  in.num_decode_tokens = ndt;
+  in.num_prefills = np;
+  in.num_prefill_tokens = npt;
+  in.common_prefix_len = P;
+  in.num_prefix_blocks = P / bs;
+  in.num_decode_items = (int32_t)hp.decode_items.size();
+  in.num_prefill_items = (int32_t)hp.prefill_items.size();
+  in.num_prefix_items = (int32_t)hp.prefix_items.size();
+  in.num_merge_rows = (int32_t)hp.merges.size();
+  in.num_partials = hp.num_partials;
+  in.kv_split_tokens = split;
+  in.decode_tokens_read = dec_read * Hkv;
+  in.prefill_tokens_read = pre_read * Hkv;
+  in.prefix_tokens_read = pfx_read * Hkv;
+  in.kv_tokens_read = in.decode_tokens_read + in.prefill_tokens_read + in.prefix_tokens_read;
+  return PA_OK;
+}
+
+}  // namespace pa

@@ -1,0 +1,245 @@
+/*
+ * libpagedattn — attention over a paged KV cache for a mixed varlen batch,
+ * written for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * What is computed.  For every query token row r of sequence b, head h:
+ *   out[r, h, :] = sum_t softmax_t(scale * q[r, h, :] . K_b[t, h / g, :]) * V_b[t, h / g, :]
+ *   lse[r, h]    = ln sum_t exp(scale * q[r, h, :] . K_b[t, h / g, :])
+ * over the visible keys t of that row, where K_b/V_b are gathered through the
+ * block table (see pa_gather_kv).  Query i of a sequence with q_b query tokens
+ * and seq_len L_b sits at position c_b + i, c_b = L_b - q_b, and with causal
+ * masking sees keys 0 .. c_b + i (a decode, q_b = 1, sees all L_b keys).
+ * Query head h reads KV head h / g, g = num_heads / num_kv_heads.
+ *
+ * Sources (cited by page title and section):
+ *  - «FlashAttention y FlashInfer: los dos grandes backends de atención en
+ *    GPU», §Responsabilidades: the forward takes Q as [num_tokens, num_heads,
+ *    head_size], the paged KV cache and the metadata (query_start_loc,
+ *    seq_lens, block table); the FlashInfer builder splits decodes from
+ *    prefills and orders decodes first.  §Flujo de datos (get_kv_cache_shape
+ *    listing): pool shape and the multiple-of-16 block size.
+ *  - «El especialista del plato estrella: el backend de atención de vLLM»,
+ *    §Por qué prefill y decode son problemas opuestos (decode is HBM-bound,
+ *    prefill is compute-bound), §El truco del scheduler (both in one forward),
+ *    §Cómo lee el backend el KV paginado (gather through the block table),
+ *    §Qué aporta FlashInfer (cascade attention for a shared prefix).
+ *  - «AttentionBackend: capa de abstracción de backends de atención»,
+ *    §Flujo de datos (build(common_prefix_len, common_attn_metadata) and
+ *    forward(..., kv_cache, attn_metadata, output) signatures), §Motivación de
+ *    diseño and §Límites y fallos (LSE output, natural-log base, head-size and
+ *    dtype limits).
+ *
+ * Conventions for every call:
+ *  - Every function returns a pa_status and never aborts.  On error nothing is
+ *    launched, outputs are untouched, and pa_last_error() (per calling thread)
+ *    holds a message.
+ *  - "host" pointers are ordinary CPU memory read during the call only.
+ *    "device" pointers are GPU memory on the plan's device, owned by the caller.
+ *  - Calls that launch work are asynchronous on the given HIP stream (NULL = the
+ *    default stream); they neither allocate nor synchronise.
+ *  - Element types: PA_BF16 (bfloat16, stored as 16-bit patterns) or PA_FP32.
+ *    q, kv_cache and out share one element type; lse is always float32.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* malformed sizes, metadata or pointers */
+  PA_ERR_UNSUPPORTED = 2, /* well-formed but not built: head_size, dtype */
+  PA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_OOM = 4          /* host or device allocation failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 } pa_dtype;
+
+/* Sizes of one batch.  All fields are read by pa_plan_create only. */
+typedef struct pa_params {
+  int32_t num_seqs;           /* B >= 0 */
+  int32_t num_heads;          /* H >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1 */
+  int32_t head_size;          /* d: 64 or 128 are built; others -> PA_ERR_UNSUPPORTED */
+  int32_t block_size;         /* bs: a multiple of 16 (else PA_ERR_INVALID_ARG) */
+  int32_t num_blocks;         /* pages in the pool; every used block id must be below it */
+  int32_t max_blocks_per_seq; /* row stride of block_table */
+  int32_t dtype;              /* pa_dtype */
+  int32_t causal;             /* 1: key t visible to query i iff t <= c_b + i; 0: all L_b keys */
+  int32_t common_prefix_len;  /* P: 0 = no cascade; else shared prefix tokens (see below) */
+  int32_t kv_split_tokens;    /* 0 = automatic; else decode KV chunk per work item, multiple of 32 */
+  float scale;                /* softmax scale applied to q . k (finite) */
+} pa_params;
+
+/* Opaque, immutable schedule for one batch; reusable across layers and calls. */
+typedef struct pa_plan pa_plan;
+
+typedef struct pa_plan_info {
+  int32_t num_seqs;
+  int32_t num_tokens;           /* T = query_start_loc[B] */
+  int32_t num_decodes;          /* sequences with exactly one query token */
+  int32_t num_decode_tokens;
+  int32_t num_prefills;         /* sequences with two or more query tokens */
+  int32_t num_prefill_tokens;
+  int32_t common_prefix_len;    /* P actually used (0 = cascade off) */
+  int32_t num_prefix_blocks;    /* P / block_size */
+  int32_t num_decode_items;     /* decode work items per KV head */
+  int32_t num_prefill_items;    /* prefill work items per KV head and head group */
+  int32_t num_prefix_items;     /* cascade prefix work items per KV head and head group */
+  int32_t num_merge_rows;       /* token rows combined from several partial results */
+  int32_t num_partials;         /* partial (out, lse) records in the workspace */
+  int32_t kv_split_tokens;      /* decode KV chunk used */
+  int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
+  int64_t prefix_tokens_read;   /* of which rows of the shared prefix */
+  int64_t decode_tokens_read;   /* of which by decode work items */
+  int64_t prefill_tokens_read;  /* of which by prefill work items */
+} pa_plan_info;
+
+/* Arrays a plan exposes through pa_plan_get_array. */
+typedef enum pa_plan_array {
+  PA_ARRAY_ORDER = 0,         /* int32[B]: decode-first stable order of sequence ids */
+  PA_ARRAY_IS_DECODE = 1,     /* int32[B]: 1 if the sequence is a decode */
+  PA_ARRAY_PREFIX_BLOCKS = 2, /* int32[P/bs]: the shared prefix's physical block ids */
+  PA_ARRAY_ROW_PARTIALS = 3   /* int32[T]: partial records combined for each row (0 = direct write) */
+} pa_plan_array;
+
+/* Per-kernel timing gathered by pa_profile_start/stop. */
+typedef struct pa_kernel_time {
+  char name[48];     /* kernel family, e.g. "decode_bf16_d128" */
+  int32_t launches;  /* launches recorded */
+  double total_ms;   /* summed device time between HIP events around each launch */
+} pa_kernel_time;
+
+/*
+ * Shape of the paged pool: (num_blocks, 2, block_size, num_kv_heads, head_size),
+ * dim 1 = 0 for K and 1 for V.  «FlashAttention y FlashInfer», §Flujo de datos
+ * (get_kv_cache_shape listing).  shape_out: host int64[5].
+ * Errors: block_size not a positive multiple of 16, or any size < 1 -> INVALID_ARG.
+ */
+pa_status pa_kv_cache_shape(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                            int32_t head_size, int64_t shape_out[5]);
+
+/*
+ * Build the schedule for one batch (the metadata builder).  «AttentionBackend:
+ * capa de abstracción», §Flujo de datos: build(common_prefix_len,
+ * common_attn_metadata); «FlashAttention y FlashInfer», §Responsabilidades:
+ * split decodes from prefills, order decodes first, schedule ahead of time.
+ *
+ *  params          host; sizes above.
+ *  query_start_loc host int32[B+1]: 0 = qsl[0] < qsl[1] < ... (every q_b >= 1).
+ *  seq_lens        host int32[B]: L_b >= q_b; ceil(L_b / bs) <= max_blocks_per_seq.
+ *  block_table     host int32[B * max_blocks_per_seq] or NULL.  When given, every
+ *                  used id (the first ceil(L_b / bs) of each row) is checked to be
+ *                  in [0, num_blocks).  Required when common_prefix_len > 0.
+ *  device          HIP device that will run the plan; < 0 builds a host-only plan
+ *                  (metadata queries only, pa_forward rejects it).
+ *  plan_out        receives the plan; release it with pa_plan_destroy.
+ *
+ * Cascade («El especialista del plato estrella», §Qué aporta FlashInfer): with
+ * P = common_prefix_len > 0 the first P / bs block ids must be identical in every
+ * row, P must be a multiple of bs, and P <= c_b for every sequence (the prefix
+ * is context of all of them).  Violations -> INVALID_ARG.
+ * The plan copies its work lists to device memory it owns (a few KB).
+ * Errors: INVALID_ARG (any rule above, H % Hkv != 0, NULL pointers),
+ * UNSUPPORTED (head_size, dtype), HIP / OOM (device copy).
+ */
+pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, const int32_t* block_table, int device,
+                         pa_plan** plan_out);
+
+/* Counts and schedule figures of a plan.  info: host. */
+pa_status pa_plan_get_info(const pa_plan* plan, pa_plan_info* info);
+
+/*
+ * Copy one of the plan's int32 arrays (pa_plan_array) into host memory dst of
+ * `capacity` elements; *count (host, may be NULL) receives its length.
+ * Errors: unknown array or capacity too small -> INVALID_ARG.
+ */
+pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, int64_t capacity,
+                            int64_t* count);
+
+/* Bytes of device workspace pa_forward needs for this plan (0 is possible). */
+size_t pa_plan_workspace_bytes(const pa_plan* plan);
+
+/*
+ * Run attention for the planned batch.  «AttentionBackend: capa de abstracción»,
+ * §Archivos clave: forward(layer, query, key, value, kv_cache, attn_metadata,
+ * output); the new tokens' K/V are already in the pool (the cache write is a
+ * separate step, «FlashAttention y FlashInfer», §Responsabilidades).
+ *
+ *  q           device [T, H, d], element type of the plan.
+ *  kv_cache    device [num_blocks, 2, bs, Hkv, d], same element type.
+ *  block_table device int32[B * max_blocks_per_seq]; the used ids must equal the
+ *              host table given to (or implied by) the plan.
+ *  out         device [T, H, d], same element type; fully written.
+ *  lse         device float32[T, H] natural-log LSE, or NULL to skip it.
+ *  workspace   device scratch of at least pa_plan_workspace_bytes(plan) bytes
+ *              (NULL allowed when that is 0); contents need no initialisation.
+ *  stream      hipStream_t (NULL = default stream).
+ * Row order of out/lse is the caller's token order; the decode-first order only
+ * affects the schedule.  Concurrent calls on one plan need separate workspaces.
+ * Errors: INVALID_ARG (host-only plan, NULL pointers, small workspace),
+ * HIP (launch failure).
+ */
+pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
+                     const int32_t* block_table, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Combine two partial attentions over disjoint key sets by their LSE.
+ * «AttentionBackend: capa de abstracción», §Motivación de diseño and §Límites y
+ * fallos (partial softmax results combine through a natural-log LSE):
+ *   lse = ln(e^lse_a + e^lse_b),  o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.
+ * A part with lse = -inf contributes nothing; both -inf gives o = 0, lse = -inf.
+ *  o_a, o_b, o_out device [num_tokens, num_heads, head_size] of `dtype`;
+ *  lse_a, lse_b, lse_out device float32[num_tokens, num_heads] (lse_out may be NULL).
+ * Errors: INVALID_ARG (sizes < 0, NULL pointers), UNSUPPORTED (dtype, head_size).
+ */
+pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                          void* o_out, float* lse_out, int32_t num_tokens, int32_t num_heads,
+                          int32_t head_size, int32_t dtype, void* stream);
+
+/*
+ * Copy one sequence's K and V out of the pool, contiguous, bit for bit.
+ * «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
+ * token t is slot t % bs of block block_table_row[t / bs].
+ *  kv_cache        device pool of params->dtype.
+ *  block_table_row device int32[ceil(seq_len / bs)].
+ *  k_out, v_out    device [seq_len, Hkv, d] each.
+ * Uses params->block_size, num_kv_heads, head_size, dtype.  The ids are not
+ * checked on the device: they must be in [0, num_blocks).
+ * Errors: INVALID_ARG (sizes, NULL pointers), UNSUPPORTED (dtype).
+ */
+pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int32_t seq_len,
+                       const pa_params* params, void* k_out, void* v_out, void* stream);
+
+/* Release a plan (NULL is ignored).  Not while a forward using it is in flight. */
+void pa_plan_destroy(pa_plan* plan);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * Timing of the library's own launches on the calling thread.  After
+ * pa_profile_start(max_launches), every launch made by this thread records a
+ * HIP event before and after it, on the launch's stream, up to max_launches.
+ * pa_profile_stop waits for the recorded events, sums device time per kernel
+ * family into out (host, `capacity` entries; *count receives how many) and
+ * ends the session.  Errors: INVALID_ARG (no session / bad sizes), HIP.
+ */
+pa_status pa_profile_start(int32_t max_launches);
+pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

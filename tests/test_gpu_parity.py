@@ -1,0 +1,278 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Small batches are compared on every element; the full-size workloads on
+sampled rows the oracle computes one by one, plus properties that hold at any
+size (finite outputs, cascade = non-cascade).  Gathers are bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, oracle_full, run_gpu, sample_rows
+from workloads import config_batch, f32_to_bf16_bits, make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _mixed(qlens, lens, **kw):
+    return lambda: make_batch(qlens, lens, **kw)
+
+
+SMALL = {
+    # configuration 1 exactly: fp32, 2 decodes, a chunk with 48 context tokens, a full prefill
+    "cfg1_tiny_mixed_fp32": lambda: config_batch(1),
+    "mixed_bf16_d128_g4_bs16": _mixed([1, 1, 1, 1, 1, 37, 130, 200], [1, 16, 17, 700, 2100, 337, 130, 264],
+                                      num_heads=8, num_kv_heads=2, head_size=128, block_size=16, seed=11),
+    "mixed_bf16_d128_g8_bs64": _mixed([1, 1, 1, 64, 100, 1], [65, 640, 1500, 600, 100, 64],
+                                      num_heads=16, num_kv_heads=2, head_size=128, block_size=64, seed=12),
+    "mixed_bf16_d64_g2_bs32": _mixed([1, 1, 33, 70, 1], [5, 333, 100, 70, 1000],
+                                     num_heads=4, num_kv_heads=2, head_size=64, block_size=32, seed=13),
+    "mixed_fp32_d128_g1_bs16": _mixed([1, 1, 150, 20], [40, 513, 150, 300],
+                                      num_heads=2, num_kv_heads=2, head_size=128, block_size=16, dtype="fp32",
+                                      seed=14),
+    "mixed_fp32_d64_g4_bs16": _mixed([1, 17, 1], [90, 17, 33],
+                                     num_heads=8, num_kv_heads=2, head_size=64, block_size=16, dtype="fp32",
+                                     seed=15),
+    "mixed_bf16_d128_g16_bs16": _mixed([1, 1, 40, 1], [300, 1, 90, 47],
+                                       num_heads=16, num_kv_heads=1, head_size=128, block_size=16, seed=16),
+    "mixed_bf16_d128_g32_bs48": _mixed([1, 1, 50], [700, 49, 150],
+                                       num_heads=32, num_kv_heads=1, head_size=128, block_size=48, seed=17),
+    "mixed_bf16_d128_g3_bs16": _mixed([1, 30, 1], [77, 95, 1200],
+                                      num_heads=6, num_kv_heads=2, head_size=128, block_size=16, seed=18),
+    "noncausal_bf16_d128_g4": _mixed([1, 40, 7], [64, 100, 7], num_heads=8, num_kv_heads=2, head_size=128,
+                                     block_size=16, seed=19, causal=False),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_batch_matches_oracle(name):
+    batch = SMALL[name]()
+    announce(f"{name} B={batch.num_seqs} T={batch.num_tokens} H={batch.num_heads}/{batch.num_kv_heads} "
+             f"d={batch.head_size} bs={batch.block_size} {batch.dtype} causal={batch.causal}")
+    out, lse, _ = run_gpu(batch)
+    ref_o, ref_l = oracle_full(batch)
+    assert_close(out, lse, ref_o, ref_l, name)
+
+
+def test_cascade_small_matches_oracle_and_non_cascade():
+    P = 128
+    qlens = [1, 1, 1, 1, 1, 1, 20, 9]
+    extra = [5, 40, 100, 1, 300, 17, 70, 9]
+    lens = [P + e for e in extra]
+    batch = make_batch(qlens, lens, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, seed=21,
+                       shared_prefix_blocks=P // 16)
+    announce(f"cascade_small P={P} B={batch.num_seqs}")
+    ref_o, ref_l = oracle_full(batch)
+    co, cl, _ = run_gpu(batch)
+    assert_close(co, cl, ref_o, ref_l, "cascade vs oracle")
+    po, pl, _ = run_gpu(batch, common_prefix_len=0)
+    assert_close(po, pl, ref_o, ref_l, "non-cascade vs oracle")
+    assert_close(co, cl, po, pl, "cascade vs non-cascade")
+
+
+@pytest.mark.parametrize("split", [32, 96, 512, 0])
+def test_split_kv_invariance(split):
+    rng = np.random.default_rng(22)
+    lens = rng.integers(1, 3000, size=12).tolist() + [4096, 33]
+    batch = make_batch([1] * len(lens), lens, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, seed=22)
+    announce(f"split_kv split={split}")
+    ref_o, ref_l = oracle_full(batch)
+    out, lse, db = run_gpu(batch, kv_split_tokens=split)
+    assert_close(out, lse, ref_o, ref_l, f"split {split}")
+    base_o, base_l, _ = run_gpu(batch, kv_split_tokens=4096)
+    assert_close(out, lse, base_o, base_l, f"split {split} vs one split")
+
+
+def test_block_permutation_is_bit_exact():
+    batch = SMALL["mixed_bf16_d128_g4_bs16"]()
+    announce("block_permutation")
+    o1, l1, _ = run_gpu(batch)
+    rng = np.random.default_rng(23)
+    perm = rng.permutation(batch.num_blocks)
+    pool2 = np.empty_like(batch.kv_cache)
+    pool2[perm] = batch.kv_cache
+    bt2 = perm[batch.block_table].astype(np.int32)
+    o2, l2, _ = run_gpu(batch, kv_cache=pool2, block_table=bt2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_runs_are_deterministic():
+    batch = SMALL["mixed_bf16_d128_g8_bs64"]()
+    announce("determinism")
+    o1, l1, db = run_gpu(batch, kv_split_tokens=64)
+    import torch
+    db.forward()
+    torch.cuda.synchronize()
+    o2 = db.out.float().cpu().numpy().astype(np.float64)
+    l2 = db.lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_gather_is_bit_exact():
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    for name in ("mixed_bf16_d128_g8_bs64", "mixed_fp32_d128_g1_bs16", "mixed_bf16_d64_g2_bs32"):
+        batch = SMALL[name]()
+        announce(f"gather {name}")
+        db = pa.to_device(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc, batch.seq_lens,
+                          num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                          block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale)
+        tdt = torch.bfloat16 if batch.dtype == "bf16" else torch.float32
+        for b in range(batch.num_seqs):
+            L = int(batch.seq_lens[b])
+            k = torch.empty((L, batch.num_kv_heads, batch.head_size), dtype=tdt, device="cuda")
+            v = torch.empty_like(k)
+            pa.pa_gather_kv(db.kv_cache, db.block_table[b], L, db.params, k, v)
+            torch.cuda.synchronize()
+            K, V = oracle.gather(batch.kv_cache, batch.block_table[b], L)
+            view = torch.uint16 if batch.dtype == "bf16" else torch.int32
+            kb = k.view(view).cpu().numpy()
+            vb = v.view(view).cpu().numpy()
+            assert np.array_equal(kb, K.view(kb.dtype)) and np.array_equal(vb, V.view(vb.dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_merge_states_matches_oracle(dtype):
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    announce(f"merge_states {dtype}")
+    rng = np.random.default_rng(24)
+    T, H, D = 37, 6, 128
+    oa = rng.standard_normal((T, H, D)).astype(np.float32)
+    ob = rng.standard_normal((T, H, D)).astype(np.float32)
+    la = (rng.standard_normal((T, H)) * 5).astype(np.float32)
+    lb = (rng.standard_normal((T, H)) * 5).astype(np.float32)
+    la[0, 0] = -np.inf
+    lb[1, 1] = -np.inf
+    la[2, 2] = lb[2, 2] = -np.inf
+    if dtype == "bf16":
+        oa_h, ob_h = f32_to_bf16_bits(oa), f32_to_bf16_bits(ob)
+        ta = torch.from_numpy(oa_h).view(torch.bfloat16).cuda()
+        tb = torch.from_numpy(ob_h).view(torch.bfloat16).cuda()
+    else:
+        oa_h, ob_h = oa, ob
+        ta, tb = torch.from_numpy(oa).cuda(), torch.from_numpy(ob).cuda()
+    tla, tlb = torch.from_numpy(la).cuda(), torch.from_numpy(lb).cuda()
+    to = torch.empty_like(ta)
+    tl = torch.empty_like(tla)
+    pa.pa_merge_states(ta, tla, tb, tlb, to, tl)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.merge_states(oracle.to_f64(oa_h, dtype), la, oracle.to_f64(ob_h, dtype), lb)
+    got_o = to.float().cpu().numpy().astype(np.float64)
+    got_l = tl.cpu().numpy().astype(np.float64)
+    both = np.isinf(ref_l)
+    assert np.array_equal(np.isinf(got_l), both)
+    assert np.max(np.abs(got_o - ref_o)) <= OUT_TOL
+    assert np.max(np.abs(got_l[~both] - ref_l[~both])) <= LSE_TOL
+    assert np.all(got_o[both] == 0)
+
+
+def test_gpu_closed_forms():
+    """q = 0 gives the mean of the visible V rows and LSE = ln(count); a single
+    key gives its V row exactly; the ramp needle picks V[c + i]."""
+    qlens, lens = [1, 1, 1, 16, 40], [1, 17, 250, 64, 40]
+    batch = make_batch(qlens, lens, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, seed=25)
+    announce("closed_forms equal scores")
+    q0 = np.zeros_like(batch.q)
+    out, lse, _ = run_gpu(batch, q=q0)
+    qsl = batch.query_start_loc
+    for b, (qb, L) in enumerate(zip(qlens, lens)):
+        for i in range(qb):
+            n = L - qb + i + 1
+            assert np.max(np.abs(lse[qsl[b] + i] - np.log(n))) <= LSE_TOL
+    ref_o, ref_l = oracle_full(batch, q=q0)
+    assert_close(out, lse, ref_o, ref_l, "equal scores")
+    # single key: the sequence of length 1 returns V[0] bit for bit
+    K, V = oracle.gather(batch.kv_cache, batch.block_table[0], 1)
+    got = run_gpu(batch)[0][0]
+    assert np.array_equal(got, np.repeat(oracle.to_f64(V[0], "bf16"), 4, axis=0))
+    # ramp needle: K[t, :, 0] = 256 t, q[., 0] = 1
+    announce("closed_forms ramp needle")
+    pool = batch.kv_cache.copy()
+    bs = batch.block_size
+    for b, L in enumerate(lens):
+        for t in range(L):
+            blk = batch.block_table[b, t // bs]
+            pool[blk, 0, t % bs] = 0
+            pool[blk, 0, t % bs, :, 0] = f32_to_bf16_bits(np.array([256.0 * t], np.float32))[0]
+    qn = np.zeros_like(batch.q)
+    qn[:, :, 0] = f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    out, lse, _ = run_gpu(batch, q=qn, kv_cache=pool)
+    for b, (qb, L) in enumerate(zip(qlens, lens)):
+        _, Vb = oracle.gather(pool, batch.block_table[b], L)
+        for i in range(qb):
+            want = np.repeat(oracle.to_f64(Vb[L - qb + i], "bf16"), 4, axis=0)
+            assert np.max(np.abs(out[qsl[b] + i] - want)) <= OUT_TOL
+
+
+def test_forward_rejects_small_workspace_and_keeps_outputs():
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    batch = SMALL["mixed_bf16_d128_g4_bs16"]()
+    announce("workspace too small")
+    db = pa.to_device(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc, batch.seq_lens,
+                      num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                      block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, kv_split_tokens=64)
+    need = pa.pa_plan_workspace_bytes(db.plan)
+    assert need > 0
+    db.out.fill_(3.0)
+    with pytest.raises(pa.PagedAttnError) as ei:
+        pa.pa_forward(db.plan, db.q, db.kv_cache, db.block_table, db.out, db.lse, db.workspace,
+                      workspace_bytes=need - 1)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool(torch.all(db.out.float() == 3.0))
+
+
+def test_profile_records_kernel_times():
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    batch = SMALL["mixed_bf16_d128_g4_bs16"]()
+    announce("profile")
+    db = pa.to_device(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc, batch.seq_lens,
+                      num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                      block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, kv_split_tokens=64)
+    pa.pa_profile_start(16)
+    db.forward()
+    db.forward()
+    rec = pa.pa_profile_stop()
+    torch.cuda.synchronize()
+    names = {r["name"]: r for r in rec}
+    assert "decode_bf16_d128" in names and "prefill_bf16_d128" in names and "merge_bf16_d128" in names
+    assert all(r["launches"] == 2 and r["total_ms"] > 0 for r in rec)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_config_sampled_rows(cfg):
+    announce(f"full config {cfg}: generating")
+    batch = config_batch(cfg)
+    announce(f"full config {cfg}: B={batch.num_seqs} T={batch.num_tokens} pool={batch.kv_cache.nbytes / 1e9:.2f} GB")
+    out, lse, _ = run_gpu(batch)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rows = sample_rows(batch, seed=cfg)
+    ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
+                                         batch.seq_lens, batch.scale, rows, dtype=batch.dtype)
+    assert_close(out[rows], lse[rows], ref_o, ref_l, f"config {cfg} ({len(rows)} rows)")
+
+
+@pytest.mark.timeout(900)
+def test_full_config5_cascade():
+    announce("full config 5: generating")
+    batch = config_batch(5)
+    announce(f"full config 5: B={batch.num_seqs} P={batch.common_prefix_len}")
+    co, cl, db = run_gpu(batch)
+    po, pl, _ = run_gpu(batch, common_prefix_len=0)
+    assert_close(co, cl, po, pl, "config 5 cascade vs non-cascade (all rows)")
+    rows = sample_rows(batch, seed=5)
+    ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
+                                         batch.seq_lens, batch.scale, rows, dtype=batch.dtype)
+    assert_close(co[rows], cl[rows], ref_o, ref_l, f"config 5 cascade ({len(rows)} rows)")

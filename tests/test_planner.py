@@ -1,0 +1,164 @@
+"""The host metadata builder (pa_plan_create with device < 0) on the CPU:
+bit-exact agreement with the oracle's metadata, every validation error, and
+the cascade read counts against the pages' read model."""
+import numpy as np
+import pytest
+
+import attention_paged_kv_varlen_amd as pa
+import oracle
+from workloads import config_lengths
+
+
+def host_plan(qlens, lens, *, H=8, Hkv=2, d=128, bs=16, dtype="bf16", block_table=None, prefix=0, split=0,
+              num_blocks=None, mbs=None, causal=True):
+    qlens = np.asarray(qlens)
+    lens = np.asarray(lens)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    need = max(1, int(max((-(-int(L) // bs) for L in lens), default=1)))
+    mbs = mbs or need
+    if num_blocks is None:
+        num_blocks = max(1, len(lens) * mbs)
+    params = pa.make_params(num_seqs=len(lens), num_heads=H, num_kv_heads=Hkv, head_size=d, block_size=bs,
+                            num_blocks=num_blocks, max_blocks_per_seq=mbs, dtype=dtype, scale=0.1,
+                            common_prefix_len=prefix, kv_split_tokens=split, causal=causal)
+    plan = pa.pa_plan_create(params, qsl, lens, block_table, device=-1)
+    return plan, pa.pa_plan_get_info(plan)
+
+
+def check_against_oracle(qlens, lens, **kw):
+    plan, info = host_plan(qlens, lens, **kw)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    md = oracle.metadata(qsl, lens, kw.get("prefix", 0), kw.get("block_table"), kw.get("bs", 16))
+    assert np.array_equal(pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER), md["order"])
+    assert np.array_equal(pa.pa_plan_get_array(plan, pa.PA_ARRAY_IS_DECODE), md["is_decode"].astype(np.int32))
+    for k in ("num_decodes", "num_decode_tokens", "num_prefills", "num_prefill_tokens", "num_tokens"):
+        assert info[k] == md[k], k
+    assert np.array_equal(pa.pa_plan_get_array(plan, pa.PA_ARRAY_PREFIX_BLOCKS), md["prefix_blocks"])
+    return plan, info
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_metadata_is_bit_exact(cfg):
+    qlens, lens, sp = config_lengths(cfg)
+    H, Hkv, d, bs = {1: (4, 2, 64, 16), 2: (32, 8, 128, 16), 3: (32, 8, 128, 16), 4: (64, 8, 128, 64),
+                     5: (32, 8, 128, 16)}[cfg]
+    check_against_oracle(qlens, lens, H=H, Hkv=Hkv, d=d, bs=bs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shuffled_batches_order_decode_first(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    qlens = np.where(rng.random(B) < 0.5, 1, rng.integers(2, 300, size=B))
+    lens = qlens + rng.integers(0, 2000, size=B)
+    plan, info = check_against_oracle(qlens, lens)
+    order = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER)
+    nd = info["num_decodes"]
+    assert np.all(qlens[order[:nd]] == 1) and np.all(qlens[order[nd:]] > 1)
+
+
+def test_empty_batch():
+    plan, info = host_plan([], [])
+    assert info["num_tokens"] == 0 and info["num_decode_items"] == 0 and pa.pa_plan_workspace_bytes(plan) == 0
+
+
+def test_split_items_cover_each_decode_exactly():
+    lens = [1, 31, 32, 33, 1000, 4096]
+    for split in (32, 64, 96, 1024):
+        plan, info = host_plan([1] * len(lens), lens, split=split)
+        assert info["kv_split_tokens"] == split
+        assert info["decode_tokens_read"] == sum(lens) * 2  # every key once per KV head (Hkv = 2)
+        parts = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS)
+        want = [(-(-L // split)) for L in lens]
+        assert list(parts) == [n if n > 1 else 0 for n in want]
+
+
+def test_prefill_reads_follow_the_causal_staircase():
+    # one 100-token prompt, g = 4 -> 32 positions per work item: items read 32, 64, 96, 100 keys
+    plan, info = host_plan([100], [100], H=8, Hkv=2)
+    assert info["num_prefill_items"] == 4
+    assert info["prefill_tokens_read"] == (32 + 64 + 96 + 100) * 2
+
+
+def test_cascade_read_counts_match_the_read_model():
+    """«El especialista del plato estrella», §Qué aporta FlashInfer: the naive schedule
+    reads the prefix once per request, cascade once.  With R = 50 decodes and a
+    1024-token prefix: naive reads R*P + sum(s) key rows per KV head; the cascade
+    schedule reads the prefix once per 32-row column group (2 groups) plus the suffixes."""
+    R, P, bs, Hkv = 50, 1024, 16, 2
+    rng = np.random.default_rng(7)
+    s = rng.integers(1, 300, size=R)
+    lens = P + s
+    mbs = int(max(-(-L // bs) for L in lens))
+    nb = P // bs + int(sum(-(-int(x) // bs) for x in s)) + 1
+    bt = np.zeros((R, mbs), dtype=np.int32)
+    nxt = P // bs
+    for b in range(R):
+        bt[b, :P // bs] = np.arange(P // bs)
+        own = -(-int(lens[b]) // bs) - P // bs
+        bt[b, P // bs:P // bs + own] = np.arange(nxt, nxt + own)
+        nxt += own
+    model = oracle.cascade_prefix_reads(R, P, s)
+    plain, _ = host_plan([1] * R, lens, Hkv=Hkv, block_table=bt, num_blocks=nb, mbs=mbs, split=8192)
+    casc, _ = host_plan([1] * R, lens, Hkv=Hkv, block_table=bt, num_blocks=nb, mbs=mbs, prefix=P, split=8192)
+    ip, ic = pa.pa_plan_get_info(plain), pa.pa_plan_get_info(casc)  # noqa: F841
+    assert ip["kv_tokens_read"] == model["naive"] * Hkv
+    groups = -(-R // 32)
+    assert ic["prefix_tokens_read"] == groups * P * Hkv
+    assert ic["decode_tokens_read"] == int(s.sum()) * Hkv
+    assert ic["kv_tokens_read"] == (groups * P + int(s.sum())) * Hkv
+    assert ic["num_prefix_blocks"] == P // bs
+    assert np.array_equal(pa.pa_plan_get_array(casc, pa.PA_ARRAY_PREFIX_BLOCKS), np.arange(P // bs))
+    # every decode row merges the prefix parts and its suffix part
+    assert np.all(pa.pa_plan_get_array(casc, pa.PA_ARRAY_ROW_PARTIALS) == P // 1024 + 1)
+
+
+def _status(fn):
+    with pytest.raises(pa.PagedAttnError) as ei:
+        fn()
+    return ei.value.status
+
+
+def test_validation_errors():
+    INV, UNS = pa.PA_ERR_INVALID_ARG, pa.PA_ERR_UNSUPPORTED
+    # «FlashAttention y FlashInfer», §Límites y fallos: block size must be a multiple of 16
+    assert _status(lambda: host_plan([1], [10], bs=24)) == INV
+    assert _status(lambda: host_plan([1], [10], bs=8)) == INV
+    # «AttentionBackend: capa de abstracción», §Límites y fallos: head size / dtype limits
+    assert _status(lambda: host_plan([1], [10], d=96)) == UNS
+    assert _status(lambda: host_plan([1], [10], d=256)) == UNS
+    assert _status(lambda: host_plan([1], [10], dtype=7)) == UNS
+    assert _status(lambda: host_plan([1], [10], H=6, Hkv=4)) == INV
+    assert _status(lambda: host_plan([1, 0], [10, 4])) == INV           # a sequence without queries
+    assert _status(lambda: host_plan([5], [3])) == INV                   # seq_len < query tokens
+    assert _status(lambda: host_plan([1], [40], mbs=2)) == INV           # block table row too short
+    assert _status(lambda: host_plan([1], [10], split=48)) == INV        # split not a multiple of 32
+    bt = np.array([[0, 1, 7]], dtype=np.int32)
+    assert _status(lambda: host_plan([1], [40], block_table=bt, num_blocks=5)) == INV  # id outside the pool
+    # cascade preconditions
+    bt2 = np.array([[0, 1, 2], [0, 1, 3]], dtype=np.int32)
+    assert _status(lambda: host_plan([1, 1], [40, 45], prefix=32)) == INV                       # no table
+    assert _status(lambda: host_plan([1, 1], [40, 45], block_table=bt2, num_blocks=4, prefix=24)) == INV
+    assert _status(lambda: host_plan([1, 1], [40, 45], block_table=bt2, num_blocks=4, prefix=48)) == INV
+    assert _status(lambda: host_plan([1, 9], [40, 40], block_table=bt2, num_blocks=4, prefix=48)) == INV
+    ok, _ = host_plan([1, 1], [40, 45], block_table=bt2, num_blocks=4, prefix=32)
+    assert pa.pa_plan_get_info(ok)["common_prefix_len"] == 32
+
+
+def test_query_start_loc_must_start_at_zero():
+    params = pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=1, head_size=64, block_size=16, num_blocks=4,
+                            max_blocks_per_seq=4, dtype="bf16", scale=0.1)
+    assert _status(lambda: pa.pa_plan_create(params, [1, 2], [5], None, device=-1)) == pa.PA_ERR_INVALID_ARG
+
+
+def test_host_only_plan_cannot_run():
+    plan, _ = host_plan([1], [10])
+    assert _status(lambda: pa.pa_forward(plan, 1, 1, 1, 1, None, None, 0, stream=0)) == pa.PA_ERR_INVALID_ARG
+
+
+def test_workspace_size_accounts_for_partials():
+    plan, info = host_plan([1, 1], [100, 1000], split=64, H=8)
+    n = info["num_partials"]
+    assert n == 2 + 16
+    ws = pa.pa_plan_workspace_bytes(plan)
+    assert ws >= n * 8 * 128 * 4 + n * 8 * 4
