@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Throughput of libpagedattn on one MI355X, against the chip's roofline.
+
+A step is one pa_forward over one batch (every kernel the batch needs: cascade
+prefix pass, decode, prefill, LSE merge), inputs already resident in HBM.
+
+Default workload: decode-only, 256 sequences with context lengths drawn
+uniformly from [512, 8192], 32 query / 8 KV heads, head size 128, block size 16,
+bf16 (the decode half of the metric); the line also carries a secondary
+measurement of the causal varlen prefill workload (16 prompts of 512..4096
+tokens, same heads) for the prefill half of the metric.  Other workloads:
+``--workload prefill | mixed | cascade | tiny``.
+
+Prints ONE JSON line.  Algorithmic work counts each KV byte once per KV head
+(decode) and 4*H*d FLOPs per visible (query, key) pair (prefill); masked and
+skipped work is not counted.  ``roofline.achieved`` divides that by the
+dominant kernel's average launch duration, measured with HIP events recorded
+on the launch stream by the library (pa_profile_start/stop) over the timed
+region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}  # dense MFMA
+METRIC = "decode KV-read GB/s (% HBM peak) + prefill attn TFLOPS (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "attention_paged_kv_varlen_amd", "csrc", "kernels.hip")
+
+WORKLOADS = {
+    "decode": 2,
+    "prefill": 3,
+    "mixed": 4,
+    "cascade": 5,
+    "tiny": 1,
+}
+DESCRIPTIONS = {
+    1: "tiny mixed: 4 seqs, seq_lens 17/33/64/100, query_lens 1/1/16/100; 4 q / 2 kv heads, d=64, bs=16, fp32",
+    2: "decode-only: 256 seqs, q=1, ctx U[512,8192]; 32 q / 8 kv heads, d=128, bs=16, bf16, random page placement",
+    3: "prefill causal varlen: 16 prompts U[512,4096], no context; 32 q / 8 kv heads, d=128, bs=16, bf16",
+    4: "chunked-prefill mixed: 192 decodes ctx U[1024,16384] + 4 chunks of 512 with ctx U[2048,8192]; "
+       "64 q / 8 kv heads, d=128, bs=64, bf16, decode-first",
+    5: "cascade: 128 decodes sharing a 16384-token prefix + suffixes U[256,2048]; 32 q / 8 kv heads, d=128, "
+       "bs=16, bf16",
+}
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic counts
+# ---------------------------------------------------------------------------
+
+def algorithmic_counts(query_lens, seq_lens, *, num_heads, num_kv_heads, head_size, elem_bytes,
+                       common_prefix_len=0, causal=True) -> dict:
+    """Bytes and FLOPs the method needs, independent of how a kernel does it.
+
+    decode_bytes: K and V of every key a decode reads, once per KV head
+                  (2 * L * Hkv * d * s); with a shared prefix, the prefix once.
+    prefill_flops: 4 * H * d per visible (query row, key) pair; query i of a
+                   sequence with context c sees c + i + 1 keys (causal).
+    """
+    q = np.asarray(query_lens, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    P = int(common_prefix_len)
+    row_bytes = 2 * num_kv_heads * head_size * elem_bytes
+    dec = q == 1
+    dec_tokens = int(L[dec].sum())
+    if P:
+        dec_tokens_read = P + int((L[dec] - P).sum())
+    else:
+        dec_tokens_read = dec_tokens
+    ctx = L - q
+    if causal:
+        visible = int(np.sum(q[~dec] * ctx[~dec] + q[~dec] * (q[~dec] + 1) // 2))
+    else:
+        visible = int(np.sum(q[~dec] * L[~dec]))
+    flops_per_pair = 4 * num_heads * head_size
+    return {
+        "decode_seqs": int(dec.sum()),
+        "decode_kv_tokens": dec_tokens,
+        "decode_bytes": dec_tokens_read * row_bytes,
+        "decode_bytes_naive": dec_tokens * row_bytes,
+        "decode_flops": 4 * num_heads * head_size * dec_tokens,
+        "prefill_tokens": int(q[~dec].sum()),
+        "prefill_pairs": visible,
+        "prefill_flops": visible * flops_per_pair,
+        "prefill_kv_bytes": int(L[~dec].sum()) * row_bytes,
+        "prefix_flops": 4 * num_heads * head_size * P * int(q.sum()) if P else 0,
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def _batch_to_device(batch, common_prefix_len=None, kv_split_tokens=0):
+    import attention_paged_kv_varlen_amd as pa
+    cp = batch.common_prefix_len if common_prefix_len is None else common_prefix_len
+    return pa.to_device(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc, batch.seq_lens,
+                        num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                        block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, causal=batch.causal,
+                        common_prefix_len=cp, kv_split_tokens=kv_split_tokens, device="cuda:0")
+
+
+def time_steps(db, steps: int, warmup: int) -> dict:
+    """Warm up, then time `steps` forwards (wall clock between synchronisations)
+    while the library records HIP events around each of its launches."""
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        db.forward(stream)
+    torch.cuda.synchronize()
+    pa.pa_profile_start(steps * 8 + 8)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        db.forward(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = pa.pa_profile_stop()
+    return {
+        "ms_per_step": (t1 - t0) * 1e3 / steps,
+        "kernels": {k["name"]: {"launches": k["launches"], "avg_us": 1e3 * k["total_ms"] / max(k["launches"], 1)}
+                    for k in kern},
+    }
+
+
+def _traffic(kernel_name: str, launches_per_step: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when it is missing or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_name)
+    if not ent:
+        return None
+    with open(KERNEL_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if ent.get("kernel_source_sha256") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle, untuned, one thread)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
+    """Time the oracle on a bounded sample of the same batch: whole sequences in
+    a fixed random order until `budget_s` of CPU work; one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    rng = np.random.default_rng(0)
+    order = rng.permutation(batch.num_seqs)
+    qsl = batch.query_start_loc
+    L = batch.seq_lens.astype(np.int64)
+    ql = np.diff(qsl).astype(np.int64)
+    done_bytes = done_flops = 0
+    seqs = 0
+    row_bytes = 2 * batch.num_kv_heads * batch.head_size * (2 if batch.dtype == "bf16" else 4)
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for b in order:
+            rows = np.arange(qsl[b], qsl[b + 1])
+            t0 = time.perf_counter()
+            oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, qsl, batch.seq_lens, batch.scale,
+                                  rows, dtype=batch.dtype, causal=batch.causal)
+            t_total += time.perf_counter() - t0
+            seqs += 1
+            if ql[b] == 1:
+                done_bytes += int(L[b]) * row_bytes
+            else:
+                c = int(L[b] - ql[b])
+                done_flops += 4 * batch.num_heads * batch.head_size * int(ql[b] * c + ql[b] * (ql[b] + 1) // 2)
+            if t_total >= budget_s:
+                break
+    res = {"cores": 1, "kind": "oracle", "seconds": round(t_total, 3),
+           "sample": f"{seqs} of {batch.num_seqs} sequences of the same batch (numpy float64, 1 thread)"}
+    if counts["decode_seqs"] and done_bytes:
+        res.update(value=done_bytes / t_total / 1e9, unit="GB/s")
+    else:
+        res.update(value=done_flops / t_total / 1e12, unit="TFLOP/s")
+    return res
+
+
+# ---------------------------------------------------------------------------
+
+def measure(cfg: int, steps: int, warmup: int, seed=None) -> dict:
+    """Generate the workload, time it, and return the measurement record."""
+    import attention_paged_kv_varlen_amd as pa
+    from workloads import config_batch
+    batch = config_batch(cfg, seed=seed)
+    s = 2 if batch.dtype == "bf16" else 4
+    counts = algorithmic_counts(batch.query_lens, batch.seq_lens, num_heads=batch.num_heads,
+                                num_kv_heads=batch.num_kv_heads, head_size=batch.head_size, elem_bytes=s,
+                                common_prefix_len=batch.common_prefix_len, causal=batch.causal)
+    db = _batch_to_device(batch)
+    info = pa.pa_plan_get_info(db.plan)
+    t = time_steps(db, steps, warmup)
+    return {"cfg": cfg, "batch": batch, "counts": counts, "timing": t, "plan": info, "db": db}
+
+
+def _kernel(t, prefix):
+    for name, k in t["kernels"].items():
+        if name.startswith(prefix):
+            return name, k
+    return None, None
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of the path is described in DESIGN.md but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    cfg = WORKLOADS[args.workload]
+    m = measure(cfg, args.steps, args.warmup)
+    batch, counts, t = m["batch"], m["counts"], m["timing"]
+    ms = t["ms_per_step"]
+    dtype = batch.dtype
+    line = {
+        "metric": METRIC,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, random page placement)",
+        "config": {"workload": DESCRIPTIONS[cfg], "num_seqs": batch.num_seqs, "num_tokens": batch.num_tokens,
+                   "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
+                   "head_size": batch.head_size, "block_size": batch.block_size,
+                   "common_prefix_len": batch.common_prefix_len, "seed": cfg,
+                   "kv_split_tokens": m["plan"]["kv_split_tokens"]},
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in t["kernels"].items()},
+    }
+    bound = "hbm"
+    if counts["decode_seqs"] and not counts["prefill_tokens"]:
+        value = counts["decode_bytes"] / (ms * 1e-3) / 1e9
+        line.update(value=round(value, 2), unit="GB/s")
+        kname, k = _kernel(t, "decode_")
+        ach = counts["decode_bytes"] / (k["avg_us"] * 1e-6) / 1e9
+        if cfg == 5:  # cascade: the decode kernel reads only the suffixes
+            suffix = counts["decode_bytes"] - batch.common_prefix_len * 2 * batch.num_kv_heads * batch.head_size * 2
+            ach = suffix / (k["avg_us"] * 1e-6) / 1e9
+            line["cascade"] = {"effective_GBps_vs_naive_bytes": round(counts["decode_bytes_naive"] / (ms * 1e-3) / 1e9, 1),
+                               "naive_bytes": counts["decode_bytes_naive"], "cascade_bytes": counts["decode_bytes"]}
+        roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+        tr = _traffic(kname, 1)
+        roof["traffic"] = tr
+    elif counts["prefill_tokens"] and not counts["decode_seqs"]:
+        bound = "mfma"
+        value = counts["prefill_flops"] / (ms * 1e-3) / 1e12
+        line.update(value=round(value, 2), unit="TFLOP/s")
+        kname, k = _kernel(t, "prefill_")
+        ach = counts["prefill_flops"] / (k["avg_us"] * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": _traffic(kname, 1)}
+    else:
+        # mixed step: the roofline of the whole step is max(bytes/BW, flops/peak)
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        t_ideal = max(counts["decode_bytes"] / (HBM_PEAK_GBS * 1e9), counts["prefill_flops"] / (peak * 1e12))
+        value = t_ideal / (ms * 1e-3) * 100.0
+        line.update(value=round(value, 2), unit="% of step roofline max(bytes/HBM, flops/MFMA)")
+        kd, d = _kernel(t, "decode_")
+        kp, p = _kernel(t, "prefill_")
+        dec_ach = counts["decode_bytes"] / (d["avg_us"] * 1e-6) / 1e9 if d else 0.0
+        pre_ach = counts["prefill_flops"] / (p["avg_us"] * 1e-6) / 1e12 if p else 0.0
+        roof = {"bound": "hbm", "kernel": kd, "achieved": round(dec_ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_ach / HBM_PEAK_GBS, 4), "traffic": _traffic(kd, 1),
+                "prefill": {"kernel": kp, "achieved_TFLOPs": round(pre_ach, 2), "peak": peak,
+                            "frac": round(pre_ach / peak, 4)}}
+        line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
+        line["prefill_TFLOPs_step"] = round(counts["prefill_flops"] / (ms * 1e-3) / 1e12, 2)
+    line["roofline"] = roof
+    line["algorithmic"] = {k: counts[k] for k in ("decode_bytes", "prefill_flops", "decode_kv_tokens",
+                                                  "prefill_tokens")}
+
+    if cfg == 2 and not args.no_secondary:
+        del m
+        p = measure(3, max(10, args.steps // 4), max(2, args.warmup // 2))
+        kp, k = _kernel(p["timing"], "prefill_")
+        pf = p["counts"]["prefill_flops"]
+        line["secondary"] = {
+            "workload": DESCRIPTIONS[3],
+            "ms_per_step": round(p["timing"]["ms_per_step"], 5),
+            "value": round(pf / (p["timing"]["ms_per_step"] * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "kernel": kp, "achieved": round(pf / (k["avg_us"] * 1e-6) / 1e12, 2),
+                         "peak": MFMA_PEAK_TFLOPS["bf16"],
+                         "frac": round(pf / (k["avg_us"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                         "traffic": _traffic(kp, 1)},
+        }
+        del p
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(batch, counts, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
