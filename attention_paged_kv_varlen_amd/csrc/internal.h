@@ -37,16 +37,19 @@ struct MergeRow {
 };
 static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
 
-// Prefill tiling: a workgroup owns 128 columns = 8 tiles of 16.  Tile j holds
-// head (j / tiles_per_head) of the workgroup's head group and positions
-// 16 * (j % tiles_per_head) .. +15.
+// Prefill tiling: a workgroup owns `tiles` column tiles of 16 (two per wave).
+// Tile j holds head (j / tiles_per_head) of the workgroup's head group and
+// positions 16 * (j % tiles_per_head) .. +15.
 struct PrefillShape {
+  int tiles;           // column tiles per workgroup: 16 (bf16, d = 128) or 8
   int heads_per_wg;    // 1, 2, 4 or 8, divides g
-  int tiles_per_head;  // 8 / heads_per_wg
+  int tiles_per_head;  // tiles / heads_per_wg
   int rows_per_item;   // 16 * tiles_per_head
   int head_groups;     // g / heads_per_wg
 };
-PrefillShape prefill_shape(int group);
+PrefillShape prefill_shape(int group, int tiles);
+// The wide prefill kernel (16 tiles, 8 waves) serves bf16 with head size 128.
+inline bool use_wide_prefill(int dtype, int head_size) { return dtype == PA_BF16 && head_size == 128; }
 
 // Everything the kernels need besides the caller's tensors.
 struct LaunchGeom {

@@ -99,8 +99,10 @@ struct Ops<uint16_t, VE> {
     Frag f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      // v_perm_b32 picks bytes of {S0:S1} (S1 = bytes 0-3): the low (even DT) or
+      // high (odd DT) halves of key rows 2j and 2j+1
       const uint32_t a = vr[2 * j].w[DT >> 1], b = vr[2 * j + 1].w[DT >> 1];
-      f.v[j] = (DT & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      f.v[j] = __builtin_amdgcn_perm(b, a, (DT & 1) ? 0x07060302u : 0x05040100u);
     }
     return f;
   }
@@ -536,6 +538,220 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide prefill for bf16 with head size 128 (the fast path): a workgroup of 8
+// waves (two per SIMD, so one wave's softmax overlaps the other's MFMAs) owns
+// 16 column tiles; 64-key K/V blocks are double-buffered in LDS and filled with
+// global_load_lds_dwordx4, which writes lane l's 16 bytes at LDS base + 16 l
+// (no register staging, no LDS store instructions).  A 256-byte key row is 16
+// chunks of 16 bytes; chunk c of block row t sits at position c ^ (t & 15), so
+// the 16 lanes of one MFMA operand read hit 16 different bank groups.
+// Cross-lane reductions over the four 16-lane groups use permlane swaps (VALU)
+// instead of LDS shuffles.  The softmax scale is folded into the exponent's FMA
+// (the scale is positive, so max(scale * s) = scale * max(s)).
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 8;
+constexpr int kWideKT = 64;                  // keys per LDS block
+constexpr int kWideRow = 256;                // bytes per key row (128 bf16)
+constexpr int kWideBlk = kWideKT * kWideRow;  // bytes per K (or V) block
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ float xlane_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,1) and (2,3) exchanged
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves exchanged
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float xlane_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
+  constexpr int D = 128, VE = 8, KS = 4;
+  using O = Ops<uint16_t, VE>;
+  using Frag = O::Frag;
+  using VRaw = O::VRaw;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kWideBlk];  // [stage][K | V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const WorkItem it = a.items[blockIdx.x];
+  const int kvh = blockIdx.y / a.head_groups;
+  const int hgrp = blockIdx.y % a.head_groups;
+  const int r = lane & 15, qd = lane >> 4;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
+  const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
+  const float sl2 = a.scale_log2;
+
+  // this wave's two column tiles share one head
+  const int head = kvh * a.g + hgrp * a.heads_per_grp + (2 * wave) / a.tiles_per_head;
+  int pos0[2], lim[2], tmin[2];
+  Frag qf[2][KS];
+  int wave_max_lim = -1;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    pos0[c] = 16 * ((2 * wave + c) % a.tiles_per_head);
+    const int pos = pos0[c] + r;
+    const bool valid = pos < it.nrows;
+    const uint16_t* qp = q + ((int64_t)(it.row0 + (valid ? pos : 0)) * a.H + head) * D + 8 * qd;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qf[c][kk] = valid ? O::load(qp + 32 * kk) : O::zero();
+    lim[c] = it.causal ? it.lim0 + pos : kv_hi - 1;
+    tmin[c] = it.causal ? it.lim0 + pos0[c] : kv_hi - 1;
+    if (pos0[c] < it.nrows)
+      wave_max_lim = max(wave_max_lim, it.causal ? it.lim0 + min(pos0[c] + 15, it.nrows - 1) : kv_hi - 1);
+  }
+
+  // loader: wave w fills block rows 8w .. 8w+7 of K and of V (one 16-key tile,
+  // hence one physical block, per wave)
+  const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
+  const int64_t slot_stride = (int64_t)a.Hkv * D;
+  const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
+  const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
+  const uint16_t* kvh_base = kv + (int64_t)kvh * D;
+  auto issue = [&](int kb, int stage) {
+    const int ks = min(kb + 8 * wave, kv_hi - 1);
+    const int blk = ks / a.bs;
+    const int pst = blk * a.bs;
+    const uint16_t* page = kvh_base + (int64_t)btrow[blk] * blk_stride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 8 * wave + 4 * i + (lane >> 4);
+      const int key = min(kb + row, kv_hi - 1);
+      const int chunk = (lane & 15) ^ (row & 15);
+      const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * chunk;
+      lds_u8* dst = (lds_u8*)lds + stage * 2 * kWideBlk + (8 * wave + 4 * i) * kWideRow;
+      __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
+                                       (void __attribute__((address_space(3)))*)(dst + kWideBlk), 16, 0, 0);
+    }
+  };
+
+  f32x4 o[2][VE];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // per-lane LDS byte offsets of the swizzled operand reads (stage and block
+  // row bases are compile-time constants folded into the ds_read offsets)
+  int koff[KS], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) koff[kk] = r * kWideRow + 16 * ((4 * kk + qd) ^ r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (4 * qd + i) * kWideRow + 16 * (r ^ (4 * qd + i));
+
+  const int nblk = (kv_hi - kv_lo + kWideKT - 1) / kWideKT;
+  auto block = [&](auto stage_c, int jb) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    const int kb = kv_lo + jb * kWideKT;
+    // this wave's loads of block jb have landed; after the barrier everyone's
+    // have, and every wave is done reading the other stage (block jb - 1)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (jb + 1 < nblk) issue(kb + kWideKT, STAGE ^ 1);
+    if (kb > wave_max_lim) return;
+
+    const unsigned char* Kb = lds + STAGE * 2 * kWideBlk;
+    const unsigned char* Vb = Kb + kWideBlk;
+    f32x4 s[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Frag kf = Frag{*reinterpret_cast<const u32x4*>(Kb + kt * 16 * kWideRow + koff[kk])};
+        O::mma(s[0][kt], kf, qf[0][kk]);
+        O::mma(s[1][kt], kf, qf[1][kk]);
+      }
+    }
+    Frag pf[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) x[k] = s[c][k >> 2][k & 3];
+      // wave-uniform: is every key of the block visible to every column of the tile?
+      const int full = __builtin_amdgcn_readfirstlane((kb + kWideKT - 1 <= tmin[c]) && (kb + kWideKT <= kv_hi));
+      if (!full) {
+        // key kb + 16 kt + 4 qd + i is visible iff 16 kt + i <= rel
+        const int rel = min(lim[c], kv_hi - 1) - kb - 4 * qd;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x[k] = (16 * (k >> 2) + (k & 3) <= rel) ? x[k] : -INFINITY;
+      }
+      float m4[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) m4[kt] = fmaxf(fmaxf(x[4 * kt], x[4 * kt + 1]), fmaxf(x[4 * kt + 2], x[4 * kt + 3]));
+      float mb = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      mb = xlane_max(mb) * sl2;
+      const bool need = mb > m_run[c] + kRescaleThreshold;
+      if (__any(need)) {
+        const float m_new = need ? mb : m_run[c];
+        const float alpha = need ? fast_exp2(m_run[c] - m_new) : 1.f;
+        m_run[c] = m_new;
+        l_run[c] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < VE; ++dt) o[c][dt] *= alpha;
+      }
+      const float mref = (m_run[c] == -INFINITY) ? 0.f : m_run[c];
+      float p[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) p[k] = fast_exp2(__builtin_fmaf(x[k], sl2, -mref));
+      float s4[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s4[kt] = (p[4 * kt] + p[4 * kt + 1]) + (p[4 * kt + 2] + p[4 * kt + 3]);
+      l_run[c] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      pf[c][0] = O::pack_p(p);
+      pf[c][1] = O::pack_p(p + 8);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      VRaw vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vr[e] = O::load_v(reinterpret_cast<const uint16_t*>(Vb + (32 * h + 16 * (e >> 2)) * kWideRow + voff[e & 3]));
+      static_for<VE>([&](auto dtc) {
+        constexpr int dt = decltype(dtc)::value;
+        const Frag vf = O::template vtrans<dt>(vr);
+        O::mma(o[0][dt], vf, pf[0][h]);
+        O::mma(o[1][dt], vf, pf[1][h]);
+      });
+    }
+  };
+  if (nblk > 0) issue(kv_lo, 0);
+  for (int jb = 0; jb < nblk; jb += 2) {
+    block(std::integral_constant<int, 0>{}, jb);
+    if (jb + 1 < nblk) block(std::integral_constant<int, 1>{}, jb + 1);
+  }
+
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float l = xlane_sum(l_run[c]);
+    const int pos = pos0[c] + r;
+    if (pos < it.nrows) write_column<uint16_t, VE>(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of several partial records per row by their LSE.
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -633,6 +849,14 @@ int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args
 }
 
 template <typename T, int D>
+int launch_prefill(const char* name, dim3 grid, void* stream, const KArgs& p) {
+  if constexpr (std::is_same<T, uint16_t>::value && D == 128)
+    return launch(name, prefill_wide_kernel, grid, dim3(64 * kWideWaves), stream, p);
+  else
+    return launch(name, prefill_kernel<T, D>, grid, dim3(256), stream, p);
+}
+
+template <typename T, int D>
 int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream, const char* tag) {
   KArgs a{};
   a.q = t.q;
@@ -662,7 +886,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.heads_per_grp = g.ps.heads_per_wg;
     p.tiles_per_head = g.ps.tiles_per_head;
     snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
-    err = launch(name, prefill_kernel<T, D>, dim3(s.n_prefix, g.Hkv * g.ps.head_groups), dim3(256), stream, p);
+    err = launch_prefill<T, D>(name, dim3(s.n_prefix, g.Hkv * g.ps.head_groups), stream, p);
     if (err) return err;
   }
   if (s.n_decode > 0) {
@@ -684,7 +908,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.heads_per_grp = g.ps.heads_per_wg;
     p.tiles_per_head = g.ps.tiles_per_head;
     snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
-    err = launch(name, prefill_kernel<T, D>, dim3(s.n_prefill, g.Hkv * g.ps.head_groups), dim3(256), stream, p);
+    err = launch_prefill<T, D>(name, dim3(s.n_prefill, g.Hkv * g.ps.head_groups), stream, p);
     if (err) return err;
   }
   if (s.n_merge > 0) {

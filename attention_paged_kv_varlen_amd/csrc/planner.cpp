@@ -19,8 +19,9 @@
 
 namespace pa {
 
-PrefillShape prefill_shape(int group) {
+PrefillShape prefill_shape(int group, int tiles) {
   PrefillShape s{};
+  s.tiles = tiles;
   int hpw = 1;
   for (int c : {8, 4, 2}) {
     if (group % c == 0) {
@@ -29,7 +30,7 @@ PrefillShape prefill_shape(int group) {
     }
   }
   s.heads_per_wg = hpw;
-  s.tiles_per_head = 8 / hpw;
+  s.tiles_per_head = tiles / hpw;
   s.rows_per_item = 16 * s.tiles_per_head;
   s.head_groups = group / hpw;
   return s;
@@ -75,7 +76,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (p.max_blocks_per_seq < 1)
     return fail(err, PA_ERR_INVALID_ARG, "max_blocks_per_seq %lld < 1", p.max_blocks_per_seq);
   if (p.causal != 0 && p.causal != 1) return fail(err, PA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (!std::isfinite(p.scale)) return fail(err, PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(p.scale) || !(p.scale > 0.f))
+    return fail(err, PA_ERR_INVALID_ARG, "scale must be positive and finite");
   if (p.kv_split_tokens < 0 || p.kv_split_tokens % 32 != 0)
     return fail(err, PA_ERR_INVALID_ARG, "kv_split_tokens %lld must be 0 or a positive multiple of 32",
                 p.kv_split_tokens);
@@ -150,7 +152,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (P > 0) hp.prefix_blocks.assign(block_table, block_table + P / bs);
 
   // ---- schedule
-  hp.ps = prefill_shape(g);
+  hp.ps = prefill_shape(g, use_wide_prefill(p.dtype, p.head_size) ? 16 : 8);
   const int QB = hp.ps.rows_per_item;
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;

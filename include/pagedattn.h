@@ -73,7 +73,7 @@ typedef struct pa_params {
   int32_t causal;             /* 1: key t visible to query i iff t <= c_b + i; 0: all L_b keys */
   int32_t common_prefix_len;  /* P: 0 = no cascade; else shared prefix tokens (see below) */
   int32_t kv_split_tokens;    /* 0 = automatic; else decode KV chunk per work item, multiple of 32 */
-  float scale;                /* softmax scale applied to q . k (finite) */
+  float scale;                /* softmax scale applied to q . k (positive, finite) */
 } pa_params;
 
 /* Opaque, immutable schedule for one batch; reusable across layers and calls. */
