@@ -574,13 +574,46 @@ __device__ __forceinline__ float xlane_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
+// 8 bytes of LDS through the transposing read (see the lane mapping above).
+__device__ __forceinline__ u32x2 tr_read_b64(const unsigned char* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(lds_u8*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Write one column whose accumulator tile dt holds d = 16 dt + 4 qd + i (i = 0..3).
+__device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int h, int slot, int qd,
+                                                    const f32x4 (&o)[8], float m_run, float l_run) {
+  constexpr int D = 128;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  const int pb = a.row_pbase[row];
+  if (pb < 0) {
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + ((int64_t)row * a.H + h) * D + 4 * qd;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 v = o[dt] * inv;
+      *reinterpret_cast<u32x2*>(dst + 16 * dt) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    if (qd == 0 && a.lse) a.lse[(int64_t)row * a.H + h] = lse;
+  } else {
+    const int64_t rec = (int64_t)(pb + slot) * a.H + h;
+    float* dst = a.ws_o + rec * D + 4 * qd;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt] * inv;
+    if (qd == 0) a.ws_lse[rec] = lse;
+  }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
   constexpr int D = 128, VE = 8, KS = 4;
   using O = Ops<uint16_t, VE>;
   using Frag = O::Frag;
-  using VRaw = O::VRaw;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kWideBlk];  // [stage][K | V]
+  // one array per stage, so that the compiler can tell the blocks being
+  // filled by direct-to-LDS loads apart from the block being read
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * kWideBlk];  // K | V of even blocks
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * kWideBlk];  // K | V of odd blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -631,7 +664,7 @@ __global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
       const int key = min(kb + row, kv_hi - 1);
       const int chunk = (lane & 15) ^ (row & 15);
       const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * chunk;
-      lds_u8* dst = (lds_u8*)lds + stage * 2 * kWideBlk + (8 * wave + 4 * i) * kWideRow;
+      lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + (8 * wave + 4 * i) * kWideRow;
       __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
                                        (void __attribute__((address_space(3)))*)(dst + kWideBlk), 16, 0, 0);
@@ -650,11 +683,21 @@ __global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
 
   // per-lane LDS byte offsets of the swizzled operand reads (stage and block
   // row bases are compile-time constants folded into the ds_read offsets)
-  int koff[KS], voff[4];
+  // V^T operands come from ds_read_b64_tr_b16: in each 16-lane group, lane
+  // 4a + b receives element b of the 8-byte chunks read by lanes a, a+4, a+8,
+  // a+12.  Lane j of group qd reads d = 16 dt + 4 (j % 4) .. +3 of key row
+  // 4 qd + j / 4 (+16 for the second read), so lane i ends up with d = 16 dt + i
+  // for keys 4 qd + 0..3 (and 16 + 4 qd + 0..3): the A operand of O^T += V^T P^T
+  // with the key order of P^T.
+  int koff[KS], vtoff[VE];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) koff[kk] = r * kWideRow + 16 * ((4 * kk + qd) ^ r);
+  {
+    const int vrow = 4 * qd + (r >> 2);  // block row (mod 16) this lane reads
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (4 * qd + i) * kWideRow + 16 * (r ^ (4 * qd + i));
+    for (int dt = 0; dt < VE; ++dt)
+      vtoff[dt] = vrow * kWideRow + 16 * ((2 * dt + ((r & 3) >> 1)) ^ vrow) + 8 * (r & 1);
+  }
 
   const int nblk = (kv_hi - kv_lo + kWideKT - 1) / kWideKT;
   auto block = [&](auto stage_c, int jb) {
@@ -667,21 +710,18 @@ __global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
     if (jb + 1 < nblk) issue(kb + kWideKT, STAGE ^ 1);
     if (kb > wave_max_lim) return;
 
-    const unsigned char* Kb = lds + STAGE * 2 * kWideBlk;
+    const unsigned char* Kb = STAGE ? lds1 : lds0;
     const unsigned char* Vb = Kb + kWideBlk;
     f32x4 s[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[0][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[1][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Frag kf = Frag{*reinterpret_cast<const u32x4*>(Kb + kt * 16 * kWideRow + koff[kk])};
-        O::mma(s[0][kt], kf, qf[0][kk]);
-        O::mma(s[1][kt], kf, qf[1][kk]);
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(Kb + kt * 16 * kWideRow + koff[kk]));
+        const f32x4 c0 = kk ? s[0][kt] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 c1 = kk ? s[1][kt] : f32x4{0.f, 0.f, 0.f, 0.f};
+        s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[0][kk].v), c0, 0, 0, 0);
+        s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[1][kk].v), c1, 0, 0, 0);
       }
     }
     Frag pf[2][2];
@@ -725,16 +765,14 @@ __global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      VRaw vr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vr[e] = O::load_v(reinterpret_cast<const uint16_t*>(Vb + (32 * h + 16 * (e >> 2)) * kWideRow + voff[e & 3]));
-      static_for<VE>([&](auto dtc) {
-        constexpr int dt = decltype(dtc)::value;
-        const Frag vf = O::template vtrans<dt>(vr);
+      for (int dt = 0; dt < VE; ++dt) {
+        const u32x2 lo = tr_read_b64(Vb + 32 * h * kWideRow + vtoff[dt]);
+        const u32x2 hi = tr_read_b64(Vb + (32 * h + 16) * kWideRow + vtoff[dt]);
+        const Frag vf = Frag{u32x4{lo[0], lo[1], hi[0], hi[1]}};
         O::mma(o[0][dt], vf, pf[0][h]);
         O::mma(o[1][dt], vf, pf[1][h]);
-      });
+      }
     }
   };
   if (nblk > 0) issue(kv_lo, 0);
@@ -747,7 +785,7 @@ __global__ void __launch_bounds__(512) prefill_wide_kernel(KArgs a) {
   for (int c = 0; c < 2; ++c) {
     const float l = xlane_sum(l_run[c]);
     const int pos = pos0[c] + r;
-    if (pos < it.nrows) write_column<uint16_t, VE>(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l);
+    if (pos < it.nrows) write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l);
   }
 }
 
