@@ -43,6 +43,7 @@ class pa_plan_info(ctypes.Structure):
         ("common_prefix_len", c_int32), ("num_prefix_blocks", c_int32),
         ("num_decode_items", c_int32), ("num_prefill_items", c_int32), ("num_prefix_items", c_int32),
         ("num_merge_rows", c_int32), ("num_partials", c_int32), ("kv_split_tokens", c_int32),
+        ("prefill_rows_per_item", c_int32), ("prefill_head_groups", c_int32),
         ("kv_tokens_read", c_int64), ("prefix_tokens_read", c_int64),
         ("decode_tokens_read", c_int64), ("prefill_tokens_read", c_int64),
     ]

@@ -207,6 +207,7 @@ struct KArgs {
   int head_groups;     // grid.y = Hkv * head_groups
   int heads_per_grp;   // decode: 16 columns; prefill: heads per workgroup
   int tiles_per_head;  // prefill only
+  int tiles_per_wg;    // prefill only: 2 per wave
   float scale_log2;
 };
 
@@ -549,7 +550,6 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 // instead of LDS shuffles.  The softmax scale is folded into the exponent's FMA
 // (the scale is positive, so max(scale * s) = scale * max(s)).
 // ---------------------------------------------------------------------------
-constexpr int kWideWaves = 8;
 constexpr int kWideKT = 64;                  // keys per LDS block
 constexpr int kWideRow = 256;                // bytes per key row (128 bf16)
 constexpr int kWideBlk = kWideKT * kWideRow;  // bytes per K (or V) block
@@ -605,7 +605,9 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
   }
 }
 
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+template <int NW>  // waves per workgroup: 8 (one workgroup per CU) or 4 (two per CU)
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+  constexpr int RPW = kWideKT / NW;  // block rows each wave loads (one 16-key tile or half of one)
   constexpr int D = 128, VE = 8, KS = 4;
   using O = Ops<uint16_t, VE>;
   using Frag = O::Frag;
@@ -654,17 +656,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
   const uint16_t* kvh_base = kv + (int64_t)kvh * D;
   auto issue = [&](int kb, int stage) {
-    const int ks = min(kb + 8 * wave, kv_hi - 1);
+    const int ks = min(kb + RPW * wave, kv_hi - 1);
     const int blk = ks / a.bs;
     const int pst = blk * a.bs;
     const uint16_t* page = kvh_base + (int64_t)btrow[blk] * blk_stride;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 8 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < RPW / 4; ++i) {
+      const int row = RPW * wave + 4 * i + (lane >> 4);
       const int key = min(kb + row, kv_hi - 1);
       const int chunk = (lane & 15) ^ (row & 15);
       const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * chunk;
-      lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + (8 * wave + 4 * i) * kWideRow;
+      lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + (RPW * wave + 4 * i) * kWideRow;
       __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
                                        (void __attribute__((address_space(3)))*)(dst + kWideBlk), 16, 0, 0);
@@ -889,7 +891,10 @@ int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args
 template <typename T, int D>
 int launch_prefill(const char* name, dim3 grid, void* stream, const KArgs& p) {
   if constexpr (std::is_same<T, uint16_t>::value && D == 128)
-    return launch(name, prefill_wide_kernel, grid, dim3(64 * kWideWaves), stream, p);
+  {
+    if (p.tiles_per_wg == 8) return launch(name, prefill_wide_kernel<4>, grid, dim3(256), stream, p);
+    return launch(name, prefill_wide_kernel<8>, grid, dim3(512), stream, p);
+  }
   else
     return launch(name, prefill_kernel<T, D>, grid, dim3(256), stream, p);
 }
@@ -923,6 +928,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.head_groups = g.ps.head_groups;
     p.heads_per_grp = g.ps.heads_per_wg;
     p.tiles_per_head = g.ps.tiles_per_head;
+    p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
     err = launch_prefill<T, D>(name, dim3(s.n_prefix, g.Hkv * g.ps.head_groups), stream, p);
     if (err) return err;
@@ -945,6 +951,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.head_groups = g.ps.head_groups;
     p.heads_per_grp = g.ps.heads_per_wg;
     p.tiles_per_head = g.ps.tiles_per_head;
+    p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
     err = launch_prefill<T, D>(name, dim3(s.n_prefill, g.Hkv * g.ps.head_groups), stream, p);
     if (err) return err;

@@ -13,18 +13,19 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "internal.h"
 
 namespace pa {
 
-PrefillShape prefill_shape(int group, int tiles) {
+PrefillShape prefill_shape(int group, int tiles, int max_heads) {
   PrefillShape s{};
   s.tiles = tiles;
   int hpw = 1;
   for (int c : {8, 4, 2}) {
-    if (group % c == 0) {
+    if (c <= max_heads && group % c == 0) {
       hpw = c;
       break;
     }
@@ -34,6 +35,14 @@ PrefillShape prefill_shape(int group, int tiles) {
   s.rows_per_item = 16 * s.tiles_per_head;
   s.head_groups = group / hpw;
   return s;
+}
+
+int wide_prefill_waves() {
+  static const int w = [] {
+    const char* e = std::getenv("PA_WIDE_PREFILL_WAVES");
+    return (e && std::atoi(e) == 8) ? 8 : 4;
+  }();
+  return w;
 }
 
 namespace {
@@ -152,7 +161,9 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (P > 0) hp.prefix_blocks.assign(block_table, block_table + P / bs);
 
   // ---- schedule
-  hp.ps = prefill_shape(g, use_wide_prefill(p.dtype, p.head_size) ? 16 : 8);
+  // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
+  hp.ps = use_wide_prefill(p.dtype, p.head_size) ? prefill_shape(g, 2 * wide_prefill_waves(), wide_prefill_waves())
+                                                 : prefill_shape(g, 8, 8);
   const int QB = hp.ps.rows_per_item;
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
@@ -266,6 +277,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   in.num_merge_rows = (int32_t)hp.merges.size();
   in.num_partials = hp.num_partials;
   in.kv_split_tokens = split;
+  in.prefill_rows_per_item = hp.ps.rows_per_item;
+  in.prefill_head_groups = hp.ps.head_groups;
   in.decode_tokens_read = dec_read * Hkv;
   in.prefill_tokens_read = pre_read * Hkv;
   in.prefix_tokens_read = pfx_read * Hkv;

@@ -94,6 +94,8 @@ typedef struct pa_plan_info {
   int32_t num_merge_rows;       /* token rows combined from several partial results */
   int32_t num_partials;         /* partial (out, lse) records in the workspace */
   int32_t kv_split_tokens;      /* decode KV chunk used */
+  int32_t prefill_rows_per_item; /* query positions per prefill work item */
+  int32_t prefill_head_groups;  /* prefill work items per KV head and position block */
   int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
   int64_t prefix_tokens_read;   /* of which rows of the shared prefix */
   int64_t decode_tokens_read;   /* of which by decode work items */

@@ -74,12 +74,15 @@ def test_split_items_cover_each_decode_exactly():
 
 
 def test_prefill_reads_follow_the_causal_staircase():
-    # one 100-token prompt, g = 4.  bf16 with d = 128 uses 16 column tiles per
-    # work item (64 positions): items read 64 and 100 keys.  Other element types
-    # and head sizes use 8 tiles (32 positions): 32, 64, 96 and 100 keys.
+    # one 100-token prompt, g = 4: the work item for positions [i0, i0 + Q) reads
+    # keys 0 .. i0 + Q - 1 (capped at 100), where Q is the item's position count.
     plan, info = host_plan([100], [100], H=8, Hkv=2)
-    assert info["num_prefill_items"] == 2
-    assert info["prefill_tokens_read"] == (64 + 100) * 2
+    Q = info["prefill_rows_per_item"]
+    assert Q in (32, 64) and info["prefill_head_groups"] == 1
+    starts = range(0, 100, Q)
+    assert info["num_prefill_items"] == len(starts)
+    assert info["prefill_tokens_read"] == sum(min(100, i0 + Q) for i0 in starts) * 2
+    # fp32 and head size 64 use 8 column tiles (32 positions for g = 4)
     plan, info = host_plan([100], [100], H=8, Hkv=2, dtype="fp32")
     assert info["num_prefill_items"] == 4
     assert info["prefill_tokens_read"] == (32 + 64 + 96 + 100) * 2
@@ -91,8 +94,8 @@ def test_cascade_read_counts_match_the_read_model():
     """«El especialista del plato estrella», §Qué aporta FlashInfer: the naive schedule
     reads the prefix once per request, cascade once.  With R = 50 decodes and a
     1024-token prefix: naive reads R*P + sum(s) key rows per KV head; the cascade
-    schedule reads the prefix once per 64-row column group of the bf16 / d = 128
-    prefill kernel (here one group, so exactly once) plus the suffixes."""
+    schedule reads the prefix once per column group (prefill_rows_per_item query
+    rows) plus the suffixes."""
     R, P, bs, Hkv = 50, 1024, 16, 2
     rng = np.random.default_rng(7)
     s = rng.integers(1, 300, size=R)
@@ -109,10 +112,10 @@ def test_cascade_read_counts_match_the_read_model():
     model = oracle.cascade_prefix_reads(R, P, s)
     plain, _ = host_plan([1] * R, lens, Hkv=Hkv, block_table=bt, num_blocks=nb, mbs=mbs, split=8192)
     casc, _ = host_plan([1] * R, lens, Hkv=Hkv, block_table=bt, num_blocks=nb, mbs=mbs, prefix=P, split=8192)
-    ip, ic = pa.pa_plan_get_info(plain), pa.pa_plan_get_info(casc)  # noqa: F841
+    ip, ic = pa.pa_plan_get_info(plain), pa.pa_plan_get_info(casc)
+    casc_info = ic
     assert ip["kv_tokens_read"] == model["naive"] * Hkv
-    groups = -(-R // 64)
-    assert groups == 1
+    groups = -(-R // casc_info["prefill_rows_per_item"])
     assert ic["prefix_tokens_read"] == groups * P * Hkv
     assert ic["decode_tokens_read"] == int(s.sum()) * Hkv
     assert ic["kv_tokens_read"] == (groups * P + int(s.sum())) * Hkv
