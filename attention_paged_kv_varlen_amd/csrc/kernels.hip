@@ -655,21 +655,52 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
   const uint16_t* kvh_base = kv + (int64_t)kvh * D;
-  auto issue = [&](int kb, int stage) {
-    const int ks = min(kb + RPW * wave, kv_hi - 1);
-    const int blk = ks / a.bs;
-    const int pst = blk * a.bs;
-    const uint16_t* page = kvh_base + (int64_t)btrow[blk] * blk_stride;
+  // per-lane byte offset of its 16-byte chunk inside the wave's slab of RPW
+  // rows (rows 4i + lane/16, XOR-swizzled chunk): constant across blocks
+  uint32_t loff[RPW / 4];
 #pragma unroll
-    for (int i = 0; i < RPW / 4; ++i) {
-      const int row = RPW * wave + 4 * i + (lane >> 4);
-      const int key = min(kb + row, kv_hi - 1);
-      const int chunk = (lane & 15) ^ (row & 15);
-      const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * chunk;
-      lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + (RPW * wave + 4 * i) * kWideRow;
-      __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
-                                       (void __attribute__((address_space(3)))*)(dst + kWideBlk), 16, 0, 0);
+  for (int i = 0; i < RPW / 4; ++i) {
+    const int row = RPW * wave + 4 * i + (lane >> 4);
+    loff[i] = (uint32_t)((4 * i + (lane >> 4)) * slot_stride * 2 + 16 * ((lane & 15) ^ (row & 15)));
+  }
+  // physical block of this wave's slab of the block at key kb (its first key,
+  // clamped); looked up one block ahead so the lookup's latency is covered by
+  // the wait before the next barrier
+  auto page_of = [&](int kb) { return btrow[min(kb + RPW * wave, kv_hi - 1) / a.bs]; };
+  auto issue = [&](int kb, int stage, int pid) {
+    pid = __builtin_amdgcn_readfirstlane(pid);
+    const int key0 = kb + RPW * wave;  // wave-uniform
+    lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + RPW * wave * kWideRow;
+    if (key0 + RPW - 1 < kv_hi) {
+      // whole slab valid and inside one physical block: scalar base + lane offset
+      const int blk = key0 / a.bs;
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(
+          kvh_base + (int64_t)pid * blk_stride + (int64_t)(key0 - blk * a.bs) * slot_stride);
+#pragma unroll
+      for (int i = 0; i < RPW / 4; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(base + loff[i]),
+                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(base + 2 * v_half + loff[i]),
+                                         (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
+                                         16, 0, 0);
+      }
+    } else {
+      // tail: rows past the end re-read the last valid key (masked later)
+      const int ks = min(key0, kv_hi - 1);
+      const int blk = ks / a.bs;
+      const int pst = blk * a.bs;
+      const uint16_t* page = kvh_base + (int64_t)pid * blk_stride;
+#pragma unroll
+      for (int i = 0; i < RPW / 4; ++i) {
+        const int row = RPW * wave + 4 * i + (lane >> 4);
+        const int key = min(kb + row, kv_hi - 1);
+        const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ (row & 15));
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
+                                         (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
+                                         16, 0, 0);
+      }
     }
   };
 
@@ -702,6 +733,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   }
 
   const int nblk = (kv_hi - kv_lo + kWideKT - 1) / kWideKT;
+  int pnext = 0;  // page id of this wave's slab of block jb + 1
   auto block = [&](auto stage_c, int jb) {
     constexpr int STAGE = decltype(stage_c)::value;
     const int kb = kv_lo + jb * kWideKT;
@@ -709,7 +741,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
     // have, and every wave is done reading the other stage (block jb - 1)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (jb + 1 < nblk) issue(kb + kWideKT, STAGE ^ 1);
+    if (jb + 1 < nblk) {
+      issue(kb + kWideKT, STAGE ^ 1, pnext);
+      pnext = page_of(kb + 2 * kWideKT);
+    }
     if (kb > wave_max_lim) return;
 
     const unsigned char* Kb = STAGE ? lds1 : lds0;
@@ -777,7 +812,10 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
   };
-  if (nblk > 0) issue(kv_lo, 0);
+  if (nblk > 0) {
+    issue(kv_lo, 0, page_of(kv_lo));
+    pnext = page_of(kv_lo + kWideKT);
+  }
   for (int jb = 0; jb < nblk; jb += 2) {
     block(std::integral_constant<int, 0>{}, jb);
     if (jb + 1 < nblk) block(std::integral_constant<int, 1>{}, jb + 1);
