@@ -317,17 +317,18 @@ __global__ void __launch_bounds__(256) decode_kernel(KArgs a) {
   for (int dt = 0; dt < VE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // One physical block per 16-key tile.  Keys past kv_end are clamped to the
+  // last valid key (so only pool rows of this sequence are read) and masked.
+  // The block ids of the next step's two tiles are fetched during this step.
+  auto tile_block = [&](int t) { return min(t, kv_end - 1) / a.bs; };
+  int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
   for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
-    // One physical block per 16-key tile.  Keys past kv_end are clamped to the
-    // last valid key (so only pool rows of this sequence are read) and masked.
     const T* pb[2];
     int pst[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int ks = min(t0 + 16 * tt, kv_end - 1);
-      const int blk = ks / a.bs;
-      pst[tt] = blk * a.bs;
-      pb[tt] = kvh_base + (int64_t)btrow[blk] * blk_stride;
+      pst[tt] = tile_block(t0 + 16 * tt) * a.bs;
+      pb[tt] = kvh_base + (int64_t)__builtin_amdgcn_readfirstlane(pid[tt]) * blk_stride;
     }
     Frag kf[2][KS];
 #pragma unroll
@@ -343,6 +344,10 @@ __global__ void __launch_bounds__(256) decode_kernel(KArgs a) {
       const int tt = e >> 2;
       const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
       vr[e] = O::load_v(pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r);
+    }
+    if (t0 + 32 < kv_end) {
+      pid[0] = btrow[tile_block(t0 + 32)];
+      pid[1] = btrow[tile_block(t0 + 48)];
     }
 
     f32x4 s[2];
@@ -855,28 +860,58 @@ __device__ __forceinline__ f32x4 load4<float>(const float* src) {
   return *reinterpret_cast<const f32x4*>(src);
 }
 
+// One wave per (row, head): lane s < count reads partial s's LSE, the wave
+// reduces max and sum of exponentials, then every lane accumulates D / 64
+// consecutive output elements over the partials (loads issued back to back).
 template <typename T, int D>
-__global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, const float* ws_o, const float* ws_lse,
-                                                    T* out, float* lse, int H) {
-  const MergeRow mr = rows[blockIdx.x];
-  constexpr int C4 = D / 4;
-  for (int idx = threadIdx.x; idx < H * C4; idx += blockDim.x) {
-    const int h = idx / C4, c = idx % C4;
-    float mx = -INFINITY;
-    for (int s = 0; s < mr.count; ++s) mx = fmaxf(mx, ws_lse[(int64_t)(mr.pbase + s) * H + h]);
-    const float ms = (mx == -INFINITY) ? 0.f : mx;
-    float tot = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < mr.count; ++s) {
-      const int64_t rec = (int64_t)(mr.pbase + s) * H + h;
-      const float w = __expf(ws_lse[rec] - ms);
-      tot += w;
-      acc += w * *reinterpret_cast<const f32x4*>(ws_o + rec * D + 4 * c);
-    }
-    const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    store4<T>(out + ((int64_t)mr.row * H + h) * D + 4 * c, acc * inv);
-    if (c == 0 && lse) lse[(int64_t)mr.row * H + h] = tot > 0.f ? ms + logf(tot) : -INFINITY;
+__global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, int n_rows, const float* ws_o,
+                                                    const float* ws_lse, T* out, float* lse, int H) {
+  constexpr int EPL = D / 64;  // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head) pair
+  if (unit >= n_rows * H) return;
+  const int h = unit % H;
+  const MergeRow mr = rows[unit / H];
+  float mx = -INFINITY, tot = 0.f;
+  for (int s0 = 0; s0 < mr.count; s0 += 64) {
+    const int s = s0 + lane;
+    const float ls = s < mr.count ? ws_lse[(int64_t)(mr.pbase + s) * H + h] : -INFINITY;
+    float m = ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float mnew = fmaxf(mx, m);
+    const float ms = (mnew == -INFINITY) ? 0.f : mnew;
+    float e = (ls == -INFINITY) ? 0.f : __expf(ls - ms);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
+    tot = tot * ((mx == -INFINITY) ? 0.f : __expf(mx - ms)) + e;
+    mx = mnew;
   }
+  const float ms = (mx == -INFINITY) ? 0.f : mx;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  float acc[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
+  for (int s = 0; s < mr.count; ++s) {
+    const int64_t rec = (int64_t)(mr.pbase + s) * H + h;
+    const float w = __expf(ws_lse[rec] - ms) * inv;  // -inf -> 0
+    const float* src = ws_o + rec * D + EPL * lane;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc[k] += w * src[k];
+  }
+  T* dst = out + ((int64_t)mr.row * H + h) * D + EPL * lane;
+  if constexpr (EPL == 2) {
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0], acc[1]);
+    else
+      *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
+  } else {
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16x2(acc[0], 0.f) & 0xFFFFu);
+    else
+      *dst = acc[0];
+  }
+  if (lane == 0 && lse) lse[(int64_t)mr.row * H + h] = tot > 0.f ? ms + logf(tot) : -INFINITY;
 }
 
 template <typename T>
@@ -996,7 +1031,8 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   }
   if (s.n_merge > 0) {
     snprintf(name, sizeof(name), "merge_%s_d%d", tag, D);
-    err = launch(name, merge_kernel<T, D>, dim3(s.n_merge), dim3(256), stream, s.merge,
+    const int units = s.n_merge * g.H;
+    err = launch(name, merge_kernel<T, D>, dim3((units + 3) / 4), dim3(256), stream, s.merge, s.n_merge,
                  (const float*)t.ws_o, (const float*)t.ws_lse, static_cast<T*>(t.out), t.lse, g.H);
   }
   return err;
