@@ -136,7 +136,7 @@ def time_steps(db, steps: int, warmup: int) -> dict:
     }
 
 
-def _traffic(kernel_name: str, launches_per_step: int):
+def _traffic(kernel_name: str, launches_per_step: int = 1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when it is missing or the kernel source changed since it was taken."""
     try:
@@ -221,6 +221,53 @@ def _kernel(t, prefix):
     return None, None
 
 
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str, kernels=("decode_kernel",
+                  "prefill_wide_kernel", "merge_kernel")) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into HBM bytes per launch of each kernel, each counter scaled by
+    what it reads for the plain device copy of `copy_bytes` bytes in the same
+    run, and write them to profiles/traffic_counters.json."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault((row["Kernel_Name"], row["Dispatch_Id"]), 0.0)
+            vals[(row["Kernel_Name"], row["Dispatch_Id"])] += float(row["Counter_Value"])
+        out = {}
+        for (name, _), v in vals.items():
+            out.setdefault(name, []).append(v)
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_f = [v for k, v in fetch.items() if "copy" in k.lower()]
+    copy_w = [v for k, v in write.items() if "copy" in k.lower()]
+    f_scale = copy_bytes / (max(copy_f) * 1024.0)
+    w_scale = copy_bytes / (max(copy_w) * 1024.0)
+    with open(KERNEL_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    res = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+                            "command": command}}
+    for name in fetch:
+        fam = next((k for k in kernels if k in name), None)
+        if fam is None or name not in write:
+            continue
+        family = {"decode_kernel": "decode", "prefill_wide_kernel": "prefill", "merge_kernel": "merge"}[fam]
+        tag = "bf16_d128" if "unsigned short, 128" in name or "prefill_wide" in name else None
+        if tag is None:
+            continue
+        fb = fetch[name] * 1024.0 * f_scale
+        wb = write[name] * 1024.0 * w_scale
+        res[f"{family}_{tag}"] = {"kernel": name, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                                  "bytes_per_launch": fb + wb, "kernel_source_sha256": sha}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +277,17 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-command", default="", help="command recorded with --summarize-pmc")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        res = summarize_pmc(*args.summarize_pmc, copy_bytes=args.copy_calibration_mib << 20,
+                            command=args.pmc_command)
+        print(json.dumps(res, indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of the path is described in DESIGN.md but not built.", file=sys.stderr)
@@ -241,6 +298,13 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = WORKLOADS[args.workload]
     m = measure(cfg, args.steps, args.warmup)
     batch, counts, t = m["batch"], m["counts"], m["timing"]
