@@ -41,17 +41,16 @@ static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
 // Tile j holds head (j / tiles_per_head) of the workgroup's head group and
 // positions 16 * (j % tiles_per_head) .. +15.
 struct PrefillShape {
-  int tiles;           // column tiles per workgroup: 16 (bf16, d = 128) or 8
+  int tiles;           // column tiles per workgroup (8)
   int heads_per_wg;    // 1, 2, 4 or 8, divides g, at most max_heads
   int tiles_per_head;  // tiles / heads_per_wg
   int rows_per_item;   // 16 * tiles_per_head
   int head_groups;     // g / heads_per_wg
 };
 PrefillShape prefill_shape(int group, int tiles, int max_heads);
-// The wide prefill kernel serves bf16 with head size 128, with 4 or 8 waves
-// (8 or 16 column tiles) per workgroup.
+// The wide prefill kernel serves bf16 with head size 128: 4 waves, 8 column
+// tiles per workgroup, both tiles of a wave on one head.
 inline bool use_wide_prefill(int dtype, int head_size) { return dtype == PA_BF16 && head_size == 128; }
-int wide_prefill_waves();
 
 // Everything the kernels need besides the caller's tensors.
 struct LaunchGeom {

@@ -406,9 +406,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const WorkItem it = a.items[blockIdx.x];
-  const int kvh = blockIdx.y / a.head_groups;
-  const int hgrp = blockIdx.y % a.head_groups;
+  // the KV-head group is the fastest-varying workgroup index (see launch_prefill)
+  const int nhg = a.Hkv * a.head_groups;
+  const int hgi = (int)(blockIdx.x % (unsigned)nhg);
+  const WorkItem it = a.items[blockIdx.x / (unsigned)nhg];
+  const int kvh = hgi / a.head_groups;
+  const int hgrp = hgi % a.head_groups;
   const int r = lane & 15, qd = lane >> 4;
 
   const T* q = static_cast<const T*>(a.q);
@@ -544,13 +547,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide prefill for bf16 with head size 128 (the fast path): a workgroup of 8
-// waves (two per SIMD, so one wave's softmax overlaps the other's MFMAs) owns
-// 16 column tiles; 64-key K/V blocks are double-buffered in LDS and filled with
+// Wide prefill for bf16 with head size 128 (the fast path): a workgroup owns
+// 8 column tiles; 64-key K/V blocks are double-buffered in LDS and filled with
 // global_load_lds_dwordx4, which writes lane l's 16 bytes at LDS base + 16 l
 // (no register staging, no LDS store instructions).  A 256-byte key row is 16
-// chunks of 16 bytes; chunk c of block row t sits at position c ^ (t & 15), so
-// the 16 lanes of one MFMA operand read hit 16 different bank groups.
+// chunks of 16 bytes, stored XOR-swizzled (wide_swizzle) so that neither the
+// K operand reads nor the V^T transposing reads conflict on LDS banks.
 // Cross-lane reductions over the four 16-lane groups use permlane swaps (VALU)
 // instead of LDS shuffles.  The softmax scale is folded into the exponent's FMA
 // (the scale is positive, so max(scale * s) = scale * max(s)).
@@ -560,6 +562,14 @@ constexpr int kWideRow = 256;                // bytes per key row (128 bf16)
 constexpr int kWideBlk = kWideKT * kWideRow;  // bytes per K (or V) block
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// LDS position of 16-byte chunk c of block row t is c ^ wide_swizzle(t).  The
+// map is a bijection of 0..15, so the 16 rows of one K operand read hit 16
+// different chunk positions; it sends rows 2u and 2u + 1 to positions that
+// differ in more than the last bit, so the chunk pairs {2 dt, 2 dt + 1} that
+// the V^T transposing reads take from 8 consecutive rows are all distinct
+// (no bank conflicts with 64 banks of 4 bytes).
+__device__ __forceinline__ int wide_swizzle(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
 
 __device__ __forceinline__ float xlane_max(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -610,9 +620,18 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
   }
 }
 
-template <int NW>  // waves per workgroup: 8 (one workgroup per CU) or 4 (two per CU)
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
-  constexpr int RPW = kWideKT / NW;  // block rows each wave loads (one 16-key tile or half of one)
+// Workgroup of 4 waves, two workgroups per CU (their barriers are independent,
+// so one workgroup's softmax overlaps the other's MFMAs); each wave owns two
+// column tiles of one head.  A 64-key LDS block is processed as two 32-key
+// halves.  Exponentials are taken speculatively against the running max m (no
+// cross-lane reduction): when no lane sees x * scale - m above the lazy
+// threshold the values stand; otherwise (the first half of every item, and
+// rarely after) a side path takes the exact column max, rescales O and l and
+// recomputes them.  Program order lets half 0's softmax run under half 1's
+// S^T MFMAs and half 1's softmax under half 0's O^T MFMAs.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+  constexpr int NW = 4;
+  constexpr int RPW = kWideKT / NW;  // block rows each wave loads: one 16-key tile
   constexpr int D = 128, VE = 8, KS = 4;
   using O = Ops<uint16_t, VE>;
   using Frag = O::Frag;
@@ -625,9 +644,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const WorkItem it = a.items[blockIdx.x];
-  const int kvh = blockIdx.y / a.head_groups;
-  const int hgrp = blockIdx.y % a.head_groups;
+  // the KV-head group is the fastest-varying workgroup index (see launch_prefill)
+  const int nhg = a.Hkv * a.head_groups;
+  const int hgi = (int)(blockIdx.x % (unsigned)nhg);
+  const WorkItem it = a.items[blockIdx.x / (unsigned)nhg];
+  const int kvh = hgi / a.head_groups;
+  const int hgrp = hgi % a.head_groups;
   const int r = lane & 15, qd = lane >> 4;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
@@ -652,9 +674,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
     if (pos0[c] < it.nrows)
       wave_max_lim = max(wave_max_lim, it.causal ? it.lim0 + min(pos0[c] + 15, it.nrows - 1) : kv_hi - 1);
   }
+  // blocks starting at or below this key are visible in full to every column
+  // of both tiles (wave-uniform)
+  const int full_lim = __builtin_amdgcn_readfirstlane(min(min(tmin[0], tmin[1]) - (kWideKT - 1), kv_hi - kWideKT));
 
-  // loader: wave w fills block rows 8w .. 8w+7 of K and of V (one 16-key tile,
-  // hence one physical block, per wave)
+  // loader: wave w fills block rows 16w .. 16w+15 of K and of V (one 16-key
+  // tile, hence one physical block, per wave)
   const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
   const int64_t slot_stride = (int64_t)a.Hkv * D;
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
@@ -666,7 +691,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
   for (int i = 0; i < RPW / 4; ++i) {
     const int row = RPW * wave + 4 * i + (lane >> 4);
-    loff[i] = (uint32_t)((4 * i + (lane >> 4)) * slot_stride * 2 + 16 * ((lane & 15) ^ (row & 15)));
+    loff[i] = (uint32_t)((4 * i + (lane >> 4)) * slot_stride * 2 + 16 * ((lane & 15) ^ wide_swizzle(row)));
   }
   // physical block of this wave's slab of the block at key kb (its first key,
   // clamped); looked up one block ahead so the lookup's latency is covered by
@@ -699,7 +724,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       for (int i = 0; i < RPW / 4; ++i) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
         const int key = min(kb + row, kv_hi - 1);
-        const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ (row & 15));
+        const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row));
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
@@ -729,18 +754,19 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   // with the key order of P^T.
   int koff[KS], vtoff[VE];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) koff[kk] = r * kWideRow + 16 * ((4 * kk + qd) ^ r);
+  for (int kk = 0; kk < KS; ++kk) koff[kk] = r * kWideRow + 16 * ((4 * kk + qd) ^ wide_swizzle(r));
   {
     const int vrow = 4 * qd + (r >> 2);  // block row (mod 16) this lane reads
 #pragma unroll
     for (int dt = 0; dt < VE; ++dt)
-      vtoff[dt] = vrow * kWideRow + 16 * ((2 * dt + ((r & 3) >> 1)) ^ vrow) + 8 * (r & 1);
+      vtoff[dt] = vrow * kWideRow + 16 * ((2 * dt + ((r & 3) >> 1)) ^ wide_swizzle(vrow)) + 8 * (r & 1);
   }
 
   const int nblk = (kv_hi - kv_lo + kWideKT - 1) / kWideKT;
   int pnext = 0;  // page id of this wave's slab of block jb + 1
-  auto block = [&](auto stage_c, int jb) {
+  auto block = [&](auto stage_c, auto masked_c, int jb) {
     constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
     const int kb = kv_lo + jb * kWideKT;
     // this wave's loads of block jb have landed; after the barrier everyone's
     // have, and every wave is done reading the other stage (block jb - 1)
@@ -750,80 +776,118 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       issue(kb + kWideKT, STAGE ^ 1, pnext);
       pnext = page_of(kb + 2 * kWideKT);
     }
-    if (kb > wave_max_lim) return;
+    if (MASKED && kb > wave_max_lim) return;
 
     const unsigned char* Kb = STAGE ? lds1 : lds0;
     const unsigned char* Vb = Kb + kWideBlk;
-    f32x4 s[2][4];
+    // s[h][c][j][i]: score of key kb + 32 h + 16 j + 4 qd + i for column r of tile c
+    f32x4 s[2][2][2];
+    static_for<2>([&](auto hh) {
+      constexpr int h = decltype(hh)::value;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+      for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(Kb + kt * 16 * kWideRow + koff[kk]));
-        const f32x4 c0 = kk ? s[0][kt] : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 c1 = kk ? s[1][kt] : f32x4{0.f, 0.f, 0.f, 0.f};
-        s[0][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[0][kk].v), c0, 0, 0, 0);
-        s[1][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[1][kk].v), c1, 0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8_t kf = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4*>(Kb + (2 * h + j) * 16 * kWideRow + koff[kk]));
+          const f32x4 c0 = kk ? s[h][0][j] : f32x4{0.f, 0.f, 0.f, 0.f};
+          const f32x4 c1 = kk ? s[h][1][j] : f32x4{0.f, 0.f, 0.f, 0.f};
+          s[h][0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[0][kk].v), c0, 0, 0, 0);
+          s[h][1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, __builtin_bit_cast(bf16x8_t, qf[1][kk].v), c1, 0, 0, 0);
+        }
       }
-    }
-    Frag pf[2][2];
+    });
+    static_for<2>([&](auto hh) {
+      constexpr int h = decltype(hh)::value;
+      float x[2][8], p[2][8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float x[16];
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) x[k] = s[c][k >> 2][k & 3];
-      // wave-uniform: is every key of the block visible to every column of the tile?
-      const int full = __builtin_amdgcn_readfirstlane((kb + kWideKT - 1 <= tmin[c]) && (kb + kWideKT <= kv_hi));
-      if (!full) {
-        // key kb + 16 kt + 4 qd + i is visible iff 16 kt + i <= rel
-        const int rel = min(lim[c], kv_hi - 1) - kb - 4 * qd;
+        for (int k = 0; k < 8; ++k) x[c][k] = s[h][c][k >> 2][k & 3];
+        if constexpr (MASKED) {
+          // key kb + 32 h + 16 j + 4 qd + i is visible iff 16 j + i <= rel
+          const int rel = min(lim[c], kv_hi - 1) - kb - 32 * h - 4 * qd;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) x[k] = (16 * (k >> 2) + (k & 3) <= rel) ? x[k] : -INFINITY;
+          for (int k = 0; k < 8; ++k) x[c][k] = (16 * (k >> 2) + (k & 3) <= rel) ? x[c][k] : -INFINITY;
+        }
       }
-      float m4[4];
+      // speculative exponent against the running max
+      float t = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) m4[kt] = fmaxf(fmaxf(x[4 * kt], x[4 * kt + 1]), fmaxf(x[4 * kt + 2], x[4 * kt + 3]));
-      float mb = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-      mb = xlane_max(mb) * sl2;
-      const bool need = mb > m_run[c] + kRescaleThreshold;
-      if (__any(need)) {
-        const float m_new = need ? mb : m_run[c];
-        const float alpha = need ? fast_exp2(m_run[c] - m_new) : 1.f;
-        m_run[c] = m_new;
-        l_run[c] *= alpha;
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int dt = 0; dt < VE; ++dt) o[c][dt] *= alpha;
+        for (int k = 0; k < 8; ++k) {
+          p[c][k] = __builtin_fmaf(x[c][k], sl2, -m_run[c]);
+          t = fmaxf(t, p[c][k]);
+        }
       }
-      const float mref = (m_run[c] == -INFINITY) ? 0.f : m_run[c];
-      float p[16];
+      // (the empty asm keeps the exponentials ahead of the branch, where they
+      // can run under the MFMAs, instead of letting them sink into the
+      // common-path successor)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) p[k] = fast_exp2(__builtin_fmaf(x[k], sl2, -mref));
-      float s4[4];
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) s4[kt] = (p[4 * kt] + p[4 * kt + 1]) + (p[4 * kt + 2] + p[4 * kt + 3]);
-      l_run[c] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      pf[c][0] = O::pack_p(p);
-      pf[c][1] = O::pack_p(p + 8);
-    }
+        for (int k = 0; k < 8; ++k) {
+          p[c][k] = fast_exp2(p[c][k]);
+          asm volatile("" : "+v"(p[c][k]));
+        }
+      }
+      // NaN (an infinite running max meets a masked key) also takes the side path
+      if (__any(!(t <= kRescaleThreshold))) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int c = 0; c < 2; ++c) {
+          float mb = x[c][0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) mb = fmaxf(mb, x[c][k]);
+          mb = xlane_max(mb) * sl2;
+          const bool need = mb > m_run[c] + kRescaleThreshold;
+          const float m_new = need ? mb : m_run[c];
+          const float alpha = need ? fast_exp2(m_run[c] - m_new) : 1.f;
+          m_run[c] = m_new;
+          l_run[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < VE; ++dt) o[c][dt] *= alpha;
+          const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) p[c][k] = fast_exp2(__builtin_fmaf(x[c][k], sl2, -mref));
+        }
+      }
+      Frag pf[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float s01 = (p[c][0] + p[c][1]) + (p[c][2] + p[c][3]);
+        const float s23 = (p[c][4] + p[c][5]) + (p[c][6] + p[c][7]);
+        l_run[c] += s01 + s23;
+        pf[c] = O::pack_p(p[c]);
+      }
+      // O^T += V^T P^T over the half's 32 keys
 #pragma unroll
       for (int dt = 0; dt < VE; ++dt) {
         const u32x2 lo = tr_read_b64(Vb + 32 * h * kWideRow + vtoff[dt]);
         const u32x2 hi = tr_read_b64(Vb + (32 * h + 16) * kWideRow + vtoff[dt]);
         const Frag vf = Frag{u32x4{lo[0], lo[1], hi[0], hi[1]}};
-        O::mma(o[0][dt], vf, pf[0][h]);
-        O::mma(o[1][dt], vf, pf[1][h]);
+        O::mma(o[0][dt], vf, pf[0]);
+        O::mma(o[1][dt], vf, pf[1]);
       }
-    }
+    });
   };
   if (nblk > 0) {
     issue(kv_lo, 0, page_of(kv_lo));
     pnext = page_of(kv_lo + kWideKT);
   }
-  for (int jb = 0; jb < nblk; jb += 2) {
-    block(std::integral_constant<int, 0>{}, jb);
-    if (jb + 1 < nblk) block(std::integral_constant<int, 1>{}, jb + 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // leading blocks that are visible in full, in pairs (stage 0, stage 1) ...
+  const int nfull = kv_lo <= full_lim ? min(nblk, (full_lim - kv_lo) / kWideKT + 1) : 0;
+  int jb = 0;
+  for (; jb + 1 < nfull; jb += 2) {
+    block(I0{}, std::false_type{}, jb);
+    block(I1{}, std::false_type{}, jb + 1);
+  }
+  // ... then the rest (diagonal and ragged tail) with masking; jb is even here
+  for (; jb < nblk; jb += 2) {
+    block(I0{}, std::true_type{}, jb);
+    if (jb + 1 < nblk) block(I1{}, std::true_type{}, jb + 1);
   }
 
 #pragma unroll
@@ -961,12 +1025,18 @@ int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args
   return (int)e;
 }
 
+// Prefill-type launches use a 1-D grid of n_items x (Hkv x head_groups)
+// workgroups with the head group varying fastest.  Workgroups go to the eight
+// XCDs round-robin by linear index, so with 8 | Hkv x head_groups every XCD
+// serves a fixed set of KV heads and the pages of one KV head stay in one L2.
 template <typename T, int D>
-int launch_prefill(const char* name, dim3 grid, void* stream, const KArgs& p) {
+int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) {
+  const int64_t n = (int64_t)n_items * p.Hkv * p.head_groups;
+  if (n > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)n);
   if constexpr (std::is_same<T, uint16_t>::value && D == 128)
   {
-    if (p.tiles_per_wg == 8) return launch(name, prefill_wide_kernel<4>, grid, dim3(256), stream, p);
-    return launch(name, prefill_wide_kernel<8>, grid, dim3(512), stream, p);
+    return launch(name, prefill_wide_kernel, grid, dim3(256), stream, p);
   }
   else
     return launch(name, prefill_kernel<T, D>, grid, dim3(256), stream, p);
@@ -1003,7 +1073,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.tiles_per_head = g.ps.tiles_per_head;
     p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, dim3(s.n_prefix, g.Hkv * g.ps.head_groups), stream, p);
+    err = launch_prefill<T, D>(name, s.n_prefix, stream, p);
     if (err) return err;
   }
   if (s.n_decode > 0) {
@@ -1026,7 +1096,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.tiles_per_head = g.ps.tiles_per_head;
     p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, dim3(s.n_prefill, g.Hkv * g.ps.head_groups), stream, p);
+    err = launch_prefill<T, D>(name, s.n_prefill, stream, p);
     if (err) return err;
   }
   if (s.n_merge > 0) {

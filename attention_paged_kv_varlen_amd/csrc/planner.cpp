@@ -37,14 +37,6 @@ PrefillShape prefill_shape(int group, int tiles, int max_heads) {
   return s;
 }
 
-int wide_prefill_waves() {
-  static const int w = [] {
-    const char* e = std::getenv("PA_WIDE_PREFILL_WAVES");
-    return (e && std::atoi(e) == 8) ? 8 : 4;
-  }();
-  return w;
-}
-
 namespace {
 
 constexpr int kPrefixChunk = 1024;  // shared-prefix keys per cascade work item
@@ -162,8 +154,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
 
   // ---- schedule
   // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
-  hp.ps = use_wide_prefill(p.dtype, p.head_size) ? prefill_shape(g, 2 * wide_prefill_waves(), wide_prefill_waves())
-                                                 : prefill_shape(g, 8, 8);
+  hp.ps = use_wide_prefill(p.dtype, p.head_size) ? prefill_shape(g, 8, 4) : prefill_shape(g, 8, 8);
   const int QB = hp.ps.rows_per_item;
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
@@ -223,8 +214,10 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     }
   }
   if (P > 0) {
-    for (int r0 = 0; r0 < hp.T; r0 += QB) {
-      for (int j = 0; j < n_pc; ++j) {
+    // chunk-major: the row groups that read one prefix chunk are dispatched
+    // back to back (on the same XCD), so the chunk is fetched once into L2
+    for (int j = 0; j < n_pc; ++j) {
+      for (int r0 = 0; r0 < hp.T; r0 += QB) {
         WorkItem it{};
         it.seq = 0;
         it.row0 = r0;
@@ -241,12 +234,21 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     }
   }
   // longest work first, so the tail of each launch is short items
-  auto longer = [](const WorkItem& a, const WorkItem& b) {
-    const int64_t ca = (int64_t)(a.kv_end - a.kv_begin), cb = (int64_t)(b.kv_end - b.kv_begin);
-    return ca > cb;
-  };
-  std::stable_sort(hp.decode_items.begin(), hp.decode_items.end(), longer);
-  std::stable_sort(hp.prefill_items.begin(), hp.prefill_items.end(), longer);
+  auto span = [](const WorkItem& a) { return (int64_t)(a.kv_end - a.kv_begin); };
+  std::stable_sort(hp.decode_items.begin(), hp.decode_items.end(),
+                   [&](const WorkItem& a, const WorkItem& b) { return span(a) > span(b); });
+  // prefill: sequences by their longest item, then each sequence's items
+  // longest first; the workgroups in flight on one XCD then share the pages
+  // of one or two sequences instead of the heads of many
+  {
+    std::vector<int64_t> seq_span(B, 0);
+    for (const WorkItem& it : hp.prefill_items) seq_span[it.seq] = std::max(seq_span[it.seq], span(it));
+    std::stable_sort(hp.prefill_items.begin(), hp.prefill_items.end(), [&](const WorkItem& a, const WorkItem& b) {
+      if (seq_span[a.seq] != seq_span[b.seq]) return seq_span[a.seq] > seq_span[b.seq];
+      if (a.seq != b.seq) return a.seq < b.seq;
+      return span(a) > span(b);
+    });
+  }
 
   // partial records: one range per row that merges several contributions
   hp.row_pbase.assign(hp.T, -1);
