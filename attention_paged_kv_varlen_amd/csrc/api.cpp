@@ -19,6 +19,11 @@ struct pa_plan {
   void* dev_buf = nullptr;
   pa::DeviceSchedule ds{};
   size_t ws_bytes = 0;
+  // side stream and fork/join events, created with the plan when it holds both
+  // decode work and prefill or shared-prefix work, so that the MFMA-bound
+  // launches overlap the HBM-bound decode
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -184,6 +189,15 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
       ds.n_merge = (int)hp.merges.size();
       ds.row_pbase = reinterpret_cast<const int32_t*>(base + o_row);
       ds.num_partials = hp.num_partials;
+      if (!hp.decode_items.empty() && (!hp.prefill_items.empty() || !hp.prefix_items.empty())) {
+        e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);
+        if (e != hipSuccess) {
+          pa_plan_destroy(plan);
+          return hip_err(e, "stream/event creation");
+        }
+      }
     }
   }
   *plan_out = plan;
@@ -255,7 +269,8 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, c
   }
   DeviceGuard guard(plan->device);
   if (!guard.ok) return set_err(PA_ERR_HIP, "hipSetDevice failed");
-  const int e = pa::launch_forward(g, plan->ds, t, stream);
+  const pa::Streams st{stream, plan->aux, plan->ev_fork, plan->ev_join};
+  const int e = pa::launch_forward(g, plan->ds, t, st);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }
@@ -295,9 +310,12 @@ pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int
 
 void pa_plan_destroy(pa_plan* plan) {
   if (!plan) return;
-  if (plan->dev_buf) {
+  if (plan->dev_buf || plan->aux || plan->ev_fork || plan->ev_join) {
     DeviceGuard guard(plan->device);
-    (void)hipFree(plan->dev_buf);
+    if (plan->ev_join) (void)hipEventDestroy(plan->ev_join);
+    if (plan->ev_fork) (void)hipEventDestroy(plan->ev_fork);
+    if (plan->aux) (void)hipStreamDestroy(plan->aux);
+    if (plan->dev_buf) (void)hipFree(plan->dev_buf);
   }
   delete plan;
 }

@@ -82,8 +82,19 @@ struct Tensors {
   float* ws_lse;  // [num_partials, H]
 };
 
+// The caller's stream, plus an optional side stream with fork/join events: when
+// present, prefill and shared-prefix launches go to the side stream after it
+// waits for the caller's stream, and the caller's stream waits for them before
+// the merge.
+struct Streams {
+  void* main;
+  void* aux;      // may be null: everything runs on `main`
+  void* ev_fork;
+  void* ev_join;
+};
+
 // Launchers (kernels.hip).  Each returns a HIP error code (0 = success).
-int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream);
+int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, const Streams& st);
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o,
                         float* l, int n_tok, int n_heads, int head_size, int dtype, void* stream);
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,

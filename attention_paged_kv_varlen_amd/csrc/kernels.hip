@@ -1043,7 +1043,7 @@ int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) 
 }
 
 template <typename T, int D>
-int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream, const char* tag) {
+int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, const Streams& st, const char* tag) {
   KArgs a{};
   a.q = t.q;
   a.kv = t.kv;
@@ -1062,8 +1062,19 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   char name[48];
   int err = 0;
 
-  // cascade prefix pass (all rows against the shared prefix), then decodes,
-  // then prefills, then the LSE merge of rows with several parts
+  // cascade prefix pass (all rows against the shared prefix) and prefills
+  // first, on the side stream when there is one (the MFMA-bound workgroups
+  // are then resident before the decode's fill the machine), decodes on the
+  // caller's stream, then the LSE merge of rows with several parts
+  void* stream = st.main;
+  const bool fork = st.aux && s.n_decode > 0 && (s.n_prefill > 0 || s.n_prefix > 0);
+  void* mstream = fork ? st.aux : stream;
+  if (fork) {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_fork), static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+      e = hipStreamWaitEvent(static_cast<hipStream_t>(st.aux), static_cast<hipEvent_t>(st.ev_fork), 0);
+    if (e != hipSuccess) return (int)e;
+  }
   if (s.n_prefix > 0) {
     KArgs p = a;
     p.items = s.prefix;
@@ -1073,7 +1084,19 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.tiles_per_head = g.ps.tiles_per_head;
     p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, s.n_prefix, stream, p);
+    err = launch_prefill<T, D>(name, s.n_prefix, mstream, p);
+    if (err) return err;
+  }
+  if (s.n_prefill > 0) {
+    KArgs p = a;
+    p.items = s.prefill;
+    p.n_items = s.n_prefill;
+    p.head_groups = g.ps.head_groups;
+    p.heads_per_grp = g.ps.heads_per_wg;
+    p.tiles_per_head = g.ps.tiles_per_head;
+    p.tiles_per_wg = g.ps.tiles;
+    snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
+    err = launch_prefill<T, D>(name, s.n_prefill, mstream, p);
     if (err) return err;
   }
   if (s.n_decode > 0) {
@@ -1087,17 +1110,11 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     err = launch(name, decode_kernel<T, D>, dim3((s.n_decode + 3) / 4, g.Hkv * d.head_groups), dim3(256), stream, d);
     if (err) return err;
   }
-  if (s.n_prefill > 0) {
-    KArgs p = a;
-    p.items = s.prefill;
-    p.n_items = s.n_prefill;
-    p.head_groups = g.ps.head_groups;
-    p.heads_per_grp = g.ps.heads_per_wg;
-    p.tiles_per_head = g.ps.tiles_per_head;
-    p.tiles_per_wg = g.ps.tiles;
-    snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, s.n_prefill, stream, p);
-    if (err) return err;
+  if (fork) {
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_join), static_cast<hipStream_t>(st.aux));
+    if (e == hipSuccess)
+      e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(st.ev_join), 0);
+    if (e != hipSuccess) return (int)e;
   }
   if (s.n_merge > 0) {
     snprintf(name, sizeof(name), "merge_%s_d%d", tag, D);
@@ -1110,12 +1127,11 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
 
 }  // namespace
 
-int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, void* stream) {
+int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, const Streams& st) {
   if (g.dtype == PA_BF16) {
-    return g.D == 128 ? forward_impl<uint16_t, 128>(g, s, t, stream, "bf16")
-                      : forward_impl<uint16_t, 64>(g, s, t, stream, "bf16");
+    return g.D == 128 ? forward_impl<uint16_t, 128>(g, s, t, st, "bf16") : forward_impl<uint16_t, 64>(g, s, t, st, "bf16");
   }
-  return g.D == 128 ? forward_impl<float, 128>(g, s, t, stream, "fp32") : forward_impl<float, 64>(g, s, t, stream, "fp32");
+  return g.D == 128 ? forward_impl<float, 128>(g, s, t, st, "fp32") : forward_impl<float, 64>(g, s, t, st, "fp32");
 }
 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,
