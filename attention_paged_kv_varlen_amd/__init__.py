@@ -12,6 +12,8 @@ script.  Entry points keep their C names::
 from ._capi import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
+    PA_ARRAY_DECODE_LISTS,
+    PA_ARRAY_DECODE_SPANS,
     PA_ARRAY_IS_DECODE,
     PA_ARRAY_ORDER,
     PA_ARRAY_PREFIX_BLOCKS,

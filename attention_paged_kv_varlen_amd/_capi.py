@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_BF16, PA_FP32 = 0, 1
-PA_ARRAY_ORDER, PA_ARRAY_IS_DECODE, PA_ARRAY_PREFIX_BLOCKS, PA_ARRAY_ROW_PARTIALS = range(4)
+(PA_ARRAY_ORDER, PA_ARRAY_IS_DECODE, PA_ARRAY_PREFIX_BLOCKS, PA_ARRAY_ROW_PARTIALS, PA_ARRAY_DECODE_LISTS,
+ PA_ARRAY_DECODE_SPANS) = range(6)
 
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
@@ -44,6 +45,7 @@ class pa_plan_info(ctypes.Structure):
         ("num_decode_items", c_int32), ("num_prefill_items", c_int32), ("num_prefix_items", c_int32),
         ("num_merge_rows", c_int32), ("num_partials", c_int32), ("kv_split_tokens", c_int32),
         ("prefill_rows_per_item", c_int32), ("prefill_head_groups", c_int32),
+        ("num_decode_lists", c_int32), ("decode_list_tokens", c_int32),
         ("kv_tokens_read", c_int64), ("prefix_tokens_read", c_int64),
         ("decode_tokens_read", c_int64), ("prefill_tokens_read", c_int64),
     ]

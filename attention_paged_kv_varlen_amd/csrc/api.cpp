@@ -131,10 +131,22 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
     if (e != hipSuccess) return hip_err(e, "hipDeviceGetAttribute");
   }
 
+  // resident decode workgroups per CU (for the balanced decode lists); a
+  // host-only plan assumes one
+  int dec_wgs = 1;
+  if (device >= 0 && params->num_kv_heads >= 1 && params->num_heads >= params->num_kv_heads &&
+      params->num_heads % params->num_kv_heads == 0) {
+    const int g = params->num_heads / params->num_kv_heads;
+    const int nw = pa::decode_waves_per_wg(params->num_kv_heads * ((g + 15) / 16));
+    DeviceGuard guard(device);
+    dec_wgs = guard.ok ? pa::decode_workgroups_per_cu(params->dtype, params->head_size, nw) : 0;
+  }
+
   pa_plan* plan = new (std::nothrow) pa_plan();
   if (!plan) return set_err(PA_ERR_OOM, "host allocation failed");
   std::string err;
-  pa_status st = pa::build_host_plan(*params, query_start_loc, seq_lens, block_table, num_cus, plan->hp, err);
+  pa_status st =
+      pa::build_host_plan(*params, query_start_loc, seq_lens, block_table, num_cus, dec_wgs, plan->hp, err);
   if (st != PA_OK) {
     delete plan;
     return set_err(st, err);
@@ -152,8 +164,10 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
     const size_t b_pfx = hp.prefix_items.size() * sizeof(pa::WorkItem);
     const size_t b_mrg = hp.merges.size() * sizeof(pa::MergeRow);
     const size_t b_row = hp.row_pbase.size() * sizeof(int32_t);
+    const size_t b_lst = hp.decode_lists.size() * sizeof(int32_t);
     const size_t o_dec = 0, o_pre = o_dec + align256(b_dec), o_pfx = o_pre + align256(b_pre),
-                 o_mrg = o_pfx + align256(b_pfx), o_row = o_mrg + align256(b_mrg), total = o_row + align256(b_row);
+                 o_mrg = o_pfx + align256(b_pfx), o_row = o_mrg + align256(b_mrg), o_lst = o_row + align256(b_row),
+                 total = o_lst + align256(b_lst);
     if (total > 0) {
       DeviceGuard guard(device);
       if (!guard.ok) {
@@ -166,6 +180,7 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
       std::memcpy(host.data() + o_pfx, hp.prefix_items.data(), b_pfx);
       std::memcpy(host.data() + o_mrg, hp.merges.data(), b_mrg);
       std::memcpy(host.data() + o_row, hp.row_pbase.data(), b_row);
+      std::memcpy(host.data() + o_lst, hp.decode_lists.data(), b_lst);
       hipError_t e = hipMalloc(&plan->dev_buf, total);
       if (e != hipSuccess) {
         delete plan;
@@ -181,6 +196,8 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
       pa::DeviceSchedule& ds = plan->ds;
       ds.decode = reinterpret_cast<const pa::WorkItem*>(base + o_dec);
       ds.n_decode = (int)hp.decode_items.size();
+      ds.decode_lists = reinterpret_cast<const int32_t*>(base + o_lst);
+      ds.n_decode_lists = hp.decode_lists.empty() ? 0 : (int)hp.decode_lists.size() - 1;
       ds.prefill = reinterpret_cast<const pa::WorkItem*>(base + o_pre);
       ds.n_prefill = (int)hp.prefill_items.size();
       ds.prefix = reinterpret_cast<const pa::WorkItem*>(base + o_pfx);
@@ -215,11 +232,22 @@ pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, in
   g_err.clear();
   if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
   const std::vector<int32_t>* v = nullptr;
+  std::vector<int32_t> spans;
   switch (which) {
     case PA_ARRAY_ORDER: v = &plan->hp.order; break;
     case PA_ARRAY_IS_DECODE: v = &plan->hp.is_decode; break;
     case PA_ARRAY_PREFIX_BLOCKS: v = &plan->hp.prefix_blocks; break;
     case PA_ARRAY_ROW_PARTIALS: v = &plan->hp.row_partials; break;
+    case PA_ARRAY_DECODE_LISTS: v = &plan->hp.decode_lists; break;
+    case PA_ARRAY_DECODE_SPANS:
+      spans.reserve(3 * plan->hp.decode_items.size());
+      for (const pa::WorkItem& it : plan->hp.decode_items) {
+        spans.push_back(it.seq);
+        spans.push_back(it.kv_begin);
+        spans.push_back(it.kv_end);
+      }
+      v = &spans;
+      break;
     default: return set_err(PA_ERR_INVALID_ARG, "unknown plan array");
   }
   if (count) *count = (int64_t)v->size();

@@ -62,6 +62,8 @@ struct LaunchGeom {
 struct DeviceSchedule {
   const WorkItem* decode;
   int n_decode;
+  const int32_t* decode_lists;  // [n_decode_lists + 1] first item of each list
+  int n_decode_lists;
   const WorkItem* prefill;
   int n_prefill;
   const WorkItem* prefix;
@@ -110,14 +112,28 @@ struct HostPlan {
   int32_t T = 0;
   std::vector<int32_t> order, is_decode, prefix_blocks, row_partials, row_pbase;
   std::vector<WorkItem> decode_items, prefill_items, prefix_items;
+  std::vector<int32_t> decode_lists;  // [lists + 1]
   std::vector<MergeRow> merges;
   pa_plan_info info{};
   PrefillShape ps{};
   int num_partials = 0;
 };
 
-// Returns PA_OK or an error with `err` filled in.
+// Decode launch shape: the Hkv x ceil(g / 16) units of an item are run by
+// workgroups of this many waves (the largest divisor of the unit count up to 8).
+inline int decode_waves_per_wg(int units) {
+  int nw = 8;
+  while (units % nw != 0) --nw;
+  return nw;
+}
+// Decode workgroups of `waves` waves that fit on one CU at once (kernels.hip;
+// the device must be current), or 0 if the query fails.
+int decode_workgroups_per_cu(int dtype, int head_size, int waves);
+
+// Returns PA_OK or an error with `err` filled in.  decode_wgs_per_cu: resident
+// decode workgroups per CU (0 = unknown: no balanced decode lists).
 pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t* seq_lens,
-                          const int32_t* block_table, int num_cus, HostPlan& out, std::string& err);
+                          const int32_t* block_table, int num_cus, int decode_wgs_per_cu, HostPlan& out,
+                          std::string& err);
 
 }  // namespace pa

@@ -201,10 +201,11 @@ struct KArgs {
   float* ws_o;
   float* ws_lse;
   const WorkItem* items;
+  const int32_t* lists;  // decode: first item of each list, [n_lists + 1]
   const int32_t* row_pbase;
   int n_items;
   int H, Hkv, g, bs, max_blocks;
-  int head_groups;     // grid.y = Hkv * head_groups
+  int head_groups;     // units per item and KV head (prefill: head groups; decode: 16-column groups)
   int heads_per_grp;   // decode: 16 columns; prefill: heads per workgroup
   int tiles_per_head;  // prefill only
   int tiles_per_wg;    // prefill only: 2 per wave
@@ -275,7 +276,7 @@ __device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int
 // the columns are the query heads of that KV head (up to 16 per head group).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(256) decode_kernel(KArgs a) {
+__global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
   constexpr int VE = D / 16;
   constexpr int KS = D / 32;
   using O = Ops<T, VE>;
@@ -284,100 +285,110 @@ __global__ void __launch_bounds__(256) decode_kernel(KArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int idx = blockIdx.x * 4 + wave;
-  if (idx >= a.n_items) return;
-  const int kvh = blockIdx.y / a.head_groups;
-  const int hgrp = blockIdx.y % a.head_groups;
-  const WorkItem it = a.items[idx];
-  const int r = lane & 15, qd = lane >> 4;
+  // the waves of a workgroup take consecutive (KV head, head group) units of
+  // one list, so the Hkv slices of a page row (one contiguous 2 KB row at
+  // Hkv = 8, d = 128) are read by one CU at about the same time; the list's
+  // items run one after the other
+  const int nw = (int)(blockDim.x >> 6);
+  const int nhg = a.Hkv * a.head_groups;
+  const int wgs_per_list = nhg / nw;
+  const int list = (int)(blockIdx.x / (unsigned)wgs_per_list);
+  const int hgi = (int)(blockIdx.x % (unsigned)wgs_per_list) * nw + wave;
+  const int kvh = hgi / a.head_groups;
+  const int hgrp = hgi % a.head_groups;
+  const int item_end = a.lists[list + 1];
+  for (int idx = a.lists[list]; idx < item_end; ++idx) {
+    const WorkItem it = a.items[idx];
+    const int r = lane & 15, qd = lane >> 4;
 
-  const T* q = static_cast<const T*>(a.q);
-  const T* kv = static_cast<const T*>(a.kv);
+    const T* q = static_cast<const T*>(a.q);
+    const T* kv = static_cast<const T*>(a.kv);
 
-  // Q^T operand: column r = query head kvh * g + hgrp * 16 + r
-  const int hcol = hgrp * 16 + r;
-  const bool colv = hcol < a.g;
-  const int head = kvh * a.g + (colv ? hcol : 0);
-  Frag qf[KS];
-  {
-    const T* qp = q + ((int64_t)it.row0 * a.H + head) * D + 8 * qd;
+    // Q^T operand: column r = query head kvh * g + hgrp * 16 + r
+    const int hcol = hgrp * 16 + r;
+    const bool colv = hcol < a.g;
+    const int head = kvh * a.g + (colv ? hcol : 0);
+    Frag qf[KS];
+    {
+      const T* qp = q + ((int64_t)it.row0 * a.H + head) * D + 8 * qd;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = colv ? O::load(qp + 32 * kk) : O::zero();
+      for (int kk = 0; kk < KS; ++kk) qf[kk] = colv ? O::load(qp + 32 * kk) : O::zero();
+    }
+
+    const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
+    const int64_t slot_stride = (int64_t)a.Hkv * D;
+    const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
+    const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
+    const T* kvh_base = kv + (int64_t)kvh * D;
+    const int kv_end = it.kv_end;
+
+    f32x4 o[VE];
+#pragma unroll
+    for (int dt = 0; dt < VE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // One physical block per 16-key tile.  Keys past kv_end are clamped to the
+    // last valid key (so only pool rows of this sequence are read) and masked.
+    // The block ids of the next step's two tiles are fetched during this step.
+    auto tile_block = [&](int t) { return min(t, kv_end - 1) / a.bs; };
+    int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
+    for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
+      const T* pb[2];
+      int pst[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        pst[tt] = tile_block(t0 + 16 * tt) * a.bs;
+        pb[tt] = kvh_base + (int64_t)__builtin_amdgcn_readfirstlane(pid[tt]) * blk_stride;
+      }
+      Frag kf[2][KS];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int key = min(t0 + 16 * tt + r, kv_end - 1);
+        const T* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
+      }
+      VRaw vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tt = e >> 2;
+        const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
+        vr[e] = O::load_v(pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r);
+      }
+      if (t0 + 32 < kv_end) {
+        pid[0] = btrow[tile_block(t0 + 32)];
+        pid[1] = btrow[tile_block(t0 + 48)];
+      }
+
+      f32x4 s[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) O::mma(s[tt], kf[tt][kk], qf[kk]);
+      }
+      float x[8];
+      const bool full = t0 + 32 <= kv_end;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = t0 + 16 * (e >> 2) + 4 * qd + (e & 3);
+        const float sv = s[e >> 2][e & 3] * a.scale_log2;
+        x[e] = (full || key < kv_end) ? sv : -INFINITY;
+      }
+      float p[8];
+      softmax_step<VE>(x, m_run, l_run, o, p);
+      const Frag pf = O::pack_p(p);
+      static_for<VE>([&](auto dtc) {
+        constexpr int dt = decltype(dtc)::value;
+        const Frag vf = O::template vtrans<dt>(vr);
+        O::mma(o[dt], vf, pf);
+      });
+    }
+
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run);
   }
-
-  const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
-  const int64_t slot_stride = (int64_t)a.Hkv * D;
-  const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
-  const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-  const T* kvh_base = kv + (int64_t)kvh * D;
-  const int kv_end = it.kv_end;
-
-  f32x4 o[VE];
-#pragma unroll
-  for (int dt = 0; dt < VE; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // One physical block per 16-key tile.  Keys past kv_end are clamped to the
-  // last valid key (so only pool rows of this sequence are read) and masked.
-  // The block ids of the next step's two tiles are fetched during this step.
-  auto tile_block = [&](int t) { return min(t, kv_end - 1) / a.bs; };
-  int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
-  for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
-    const T* pb[2];
-    int pst[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      pst[tt] = tile_block(t0 + 16 * tt) * a.bs;
-      pb[tt] = kvh_base + (int64_t)__builtin_amdgcn_readfirstlane(pid[tt]) * blk_stride;
-    }
-    Frag kf[2][KS];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int key = min(t0 + 16 * tt + r, kv_end - 1);
-      const T* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
-    }
-    VRaw vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tt = e >> 2;
-      const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
-      vr[e] = O::load_v(pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r);
-    }
-    if (t0 + 32 < kv_end) {
-      pid[0] = btrow[tile_block(t0 + 32)];
-      pid[1] = btrow[tile_block(t0 + 48)];
-    }
-
-    f32x4 s[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) O::mma(s[tt], kf[tt][kk], qf[kk]);
-    }
-    float x[8];
-    const bool full = t0 + 32 <= kv_end;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = t0 + 16 * (e >> 2) + 4 * qd + (e & 3);
-      const float sv = s[e >> 2][e & 3] * a.scale_log2;
-      x[e] = (full || key < kv_end) ? sv : -INFINITY;
-    }
-    float p[8];
-    softmax_step<VE>(x, m_run, l_run, o, p);
-    const Frag pf = O::pack_p(p);
-    static_for<VE>([&](auto dtc) {
-      constexpr int dt = decltype(dtc)::value;
-      const Frag vf = O::template vtrans<dt>(vr);
-      O::mma(o[dt], vf, pf);
-    });
-  }
-
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,7 +1118,12 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     d.heads_per_grp = 16;
     d.tiles_per_head = 1;
     snprintf(name, sizeof(name), "decode_%s_d%d", tag, D);
-    err = launch(name, decode_kernel<T, D>, dim3((s.n_decode + 3) / 4, g.Hkv * d.head_groups), dim3(256), stream, d);
+    const int nhg = g.Hkv * d.head_groups;
+    const int nw = decode_waves_per_wg(nhg);
+    d.lists = s.decode_lists;
+    const int64_t nwg = (int64_t)s.n_decode_lists * (nhg / nw);
+    if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+    err = launch(name, decode_kernel<T, D>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
     if (err) return err;
   }
   if (fork) {
@@ -1132,6 +1148,21 @@ int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& 
     return g.D == 128 ? forward_impl<uint16_t, 128>(g, s, t, st, "bf16") : forward_impl<uint16_t, 64>(g, s, t, st, "bf16");
   }
   return g.D == 128 ? forward_impl<float, 128>(g, s, t, st, "fp32") : forward_impl<float, 64>(g, s, t, st, "fp32");
+}
+
+int decode_workgroups_per_cu(int dtype, int head_size, int waves) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  const int threads = 64 * waves;
+  if (dtype == PA_BF16 && head_size == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, 128>, threads, 0);
+  else if (dtype == PA_BF16 && head_size == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, 64>, threads, 0);
+  else if (dtype == PA_FP32 && head_size == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, 128>, threads, 0);
+  else if (dtype == PA_FP32 && head_size == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, 64>, threads, 0);
+  return e == hipSuccess ? n : 0;
 }
 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,

@@ -55,7 +55,8 @@ pa_status fail(std::string& err, pa_status st, const char* fmt, long long a = 0,
 }  // namespace
 
 pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t* seq_lens,
-                          const int32_t* block_table, int num_cus, HostPlan& hp, std::string& err) {
+                          const int32_t* block_table, int num_cus, int decode_wgs_per_cu, HostPlan& hp,
+                          std::string& err) {
   // ---- validation («FlashAttention y FlashInfer», §Límites y fallos;
   //      «AttentionBackend: capa de abstracción», §Límites y fallos)
   const int B = p.num_seqs;
@@ -159,24 +160,77 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
 
-  // decode KV chunk: explicit, or sized so that the decode work spreads over
-  // several waves per CU (items x Hkv ~ 32 per CU) without tiny items.
+  // Decode schedule.  A batch of decodes alone with the automatic split gets
+  // balanced work lists: the decode keys, sequence after sequence, are cut
+  // into as many equal lists as groups of waves are resident at once, so all
+  // of them finish together (a list may end one sequence and start the next;
+  // each piece is an item with its own partial record).  Otherwise (explicit
+  // split, or prefill or shared-prefix work running beside the decodes) each
+  // decode is cut into equal parts of at most `split` keys, one item per list,
+  // longest first, sized so that the work spreads over several waves per CU
+  // (items x Hkv ~ 32 per CU) without tiny items.
   int64_t dec_tokens = 0;
   for (int i = 0; i < nd; ++i) dec_tokens += seq_lens[hp.order[i]] - P;
+  const int dec_units = Hkv * ((g + 15) / 16);
+  const int dec_nw = decode_waves_per_wg(dec_units);
+  const bool balanced = p.kv_split_tokens == 0 && np == 0 && P == 0 && nd > 0 && decode_wgs_per_cu > 0;
   int split = p.kv_split_tokens;
-  if (split == 0) {
+  int list_tokens = 0;
+  if (balanced) {
+    // resident list groups: workgroups per CU x CUs / workgroups per list
+    const int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * std::max(num_cus, 1) * dec_nw / dec_units);
+    const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
+    list_tokens = (int)round_up(ceil_div(dec_tokens, n_lists), 32);
+    split = list_tokens;
+  } else if (split == 0) {
     const int64_t target_items = std::max<int64_t>(1, (int64_t)32 * std::max(num_cus, 1) / Hkv);
     split = (int)std::min<int64_t>(8192, std::max<int64_t>(256, round_up(ceil_div(dec_tokens, target_items), 32)));
   }
 
   std::vector<int32_t> contrib(hp.T, 0);
   int64_t dec_read = 0, pre_read = 0, pfx_read = 0;
+  if (balanced) {
+    // Cuts inside a sequence fall on multiples of 32 keys (the decode kernel's
+    // 16-key tiles must not straddle a physical block); a list is closed once
+    // less than 32 keys of room are left.
+    int filled = 0;  // keys in the open list
+    hp.decode_lists.push_back(0);
+    for (int oi = 0; oi < nd; ++oi) {
+      const int b = hp.order[oi];
+      const int L = seq_lens[b];
+      int part = 0;
+      for (int k0 = 0; k0 < L;) {
+        const int room = list_tokens - filled;  // >= 32
+        const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
+        WorkItem it{};
+        it.seq = b;
+        it.row0 = qsl[b];
+        it.nrows = 1;
+        it.lim0 = L - 1;
+        it.kv_begin = k0;
+        it.kv_end = k0 + take;
+        it.slot = part++;
+        it.causal = 0;
+        hp.decode_items.push_back(it);
+        dec_read += take;
+        k0 += take;
+        filled += take;
+        if (list_tokens - filled < 32) {
+          hp.decode_lists.push_back((int32_t)hp.decode_items.size());
+          filled = 0;
+        }
+      }
+      contrib[qsl[b]] = part;
+    }
+    if (filled > 0) hp.decode_lists.push_back((int32_t)hp.decode_items.size());
+  }
   for (int oi = 0; oi < B; ++oi) {
     const int b = hp.order[oi];
     const int qb = qsl[b + 1] - qsl[b];
     const int L = seq_lens[b];
     const int ctx = L - qb;
     if (qb == 1) {
+      if (balanced) continue;
       const int span = L - P;
       const int n = (int)ceil_div(span, split);
       const int part = (int)round_up(ceil_div(span, n), 32);
@@ -235,8 +289,12 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   }
   // longest work first, so the tail of each launch is short items
   auto span = [](const WorkItem& a) { return (int64_t)(a.kv_end - a.kv_begin); };
-  std::stable_sort(hp.decode_items.begin(), hp.decode_items.end(),
-                   [&](const WorkItem& a, const WorkItem& b) { return span(a) > span(b); });
+  if (!balanced) {
+    std::stable_sort(hp.decode_items.begin(), hp.decode_items.end(),
+                     [&](const WorkItem& a, const WorkItem& b) { return span(a) > span(b); });
+    hp.decode_lists.resize(hp.decode_items.size() + 1);
+    for (size_t i = 0; i < hp.decode_lists.size(); ++i) hp.decode_lists[i] = (int32_t)i;
+  }
   // prefill: sequences by their longest item, then each sequence's items
   // longest first; the workgroups in flight on one XCD then share the pages
   // of one or two sequences instead of the heads of many
@@ -249,6 +307,13 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
       return span(a) > span(b);
     });
   }
+
+  // the kernels read keys in 16-key tiles that must lie in one physical block
+  for (const auto* v : {&hp.decode_items, &hp.prefill_items, &hp.prefix_items})
+    for (const WorkItem& it : *v)
+      if (it.kv_begin % 16 != 0 || it.kv_end <= it.kv_begin)
+        return fail(err, PA_ERR_INVALID_ARG, "internal: work item keys [%lld, %lld) not 16-aligned or empty",
+                    it.kv_begin, it.kv_end);
 
   // partial records: one range per row that merges several contributions
   hp.row_pbase.assign(hp.T, -1);
@@ -281,6 +346,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   in.kv_split_tokens = split;
   in.prefill_rows_per_item = hp.ps.rows_per_item;
   in.prefill_head_groups = hp.ps.head_groups;
+  in.num_decode_lists = hp.decode_lists.empty() ? 0 : (int32_t)hp.decode_lists.size() - 1;
+  in.decode_list_tokens = list_tokens;
   in.decode_tokens_read = dec_read * Hkv;
   in.prefill_tokens_read = pre_read * Hkv;
   in.prefix_tokens_read = pfx_read * Hkv;

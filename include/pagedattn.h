@@ -72,7 +72,9 @@ typedef struct pa_params {
   int32_t dtype;              /* pa_dtype */
   int32_t causal;             /* 1: key t visible to query i iff t <= c_b + i; 0: all L_b keys */
   int32_t common_prefix_len;  /* P: 0 = no cascade; else shared prefix tokens (see below) */
-  int32_t kv_split_tokens;    /* 0 = automatic; else decode KV chunk per work item, multiple of 32 */
+  int32_t kv_split_tokens;    /* 0 = automatic; else decode KV chunk per work item, multiple of 32
+                                 (automatic on a batch of decodes only: balanced work lists, see
+                                 pa_plan_info.num_decode_lists) */
   float scale;                /* softmax scale applied to q . k (positive, finite) */
 } pa_params;
 
@@ -93,9 +95,12 @@ typedef struct pa_plan_info {
   int32_t num_prefix_items;     /* cascade prefix work items per KV head and head group */
   int32_t num_merge_rows;       /* token rows combined from several partial results */
   int32_t num_partials;         /* partial (out, lse) records in the workspace */
-  int32_t kv_split_tokens;      /* decode KV chunk used */
+  int32_t kv_split_tokens;      /* decode KV chunk used (largest decode work item, keys) */
   int32_t prefill_rows_per_item; /* query positions per prefill work item */
   int32_t prefill_head_groups;  /* prefill work items per KV head and position block */
+  int32_t num_decode_lists;     /* decode work lists: each is run by one group of waves (one
+                                   wave per KV head) in order; one item per list unless balanced */
+  int32_t decode_list_tokens;   /* balanced lists: keys per list (equal up to the last); else 0 */
   int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
   int64_t prefix_tokens_read;   /* of which rows of the shared prefix */
   int64_t decode_tokens_read;   /* of which by decode work items */
@@ -107,7 +112,10 @@ typedef enum pa_plan_array {
   PA_ARRAY_ORDER = 0,         /* int32[B]: decode-first stable order of sequence ids */
   PA_ARRAY_IS_DECODE = 1,     /* int32[B]: 1 if the sequence is a decode */
   PA_ARRAY_PREFIX_BLOCKS = 2, /* int32[P/bs]: the shared prefix's physical block ids */
-  PA_ARRAY_ROW_PARTIALS = 3   /* int32[T]: partial records combined for each row (0 = direct write) */
+  PA_ARRAY_ROW_PARTIALS = 3,  /* int32[T]: partial records combined for each row (0 = direct write) */
+  PA_ARRAY_DECODE_LISTS = 4,  /* int32[num_decode_lists + 1]: first decode item of each list */
+  PA_ARRAY_DECODE_SPANS = 5   /* int32[3 * num_decode_items]: (sequence, first key, end key) of each
+                                 decode item, in schedule order */
 } pa_plan_array;
 
 /* Per-kernel timing gathered by pa_profile_start/stop. */

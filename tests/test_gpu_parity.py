@@ -7,6 +7,7 @@ size (finite outputs, cascade = non-cascade).  Gathers are bit-exact.
 import numpy as np
 import pytest
 
+import attention_paged_kv_varlen_amd as pa
 import oracle
 from tests.gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, oracle_full, run_gpu, sample_rows
 from workloads import config_batch, f32_to_bf16_bits, make_batch
@@ -78,6 +79,9 @@ def test_split_kv_invariance(split):
     announce(f"split_kv split={split}")
     ref_o, ref_l = oracle_full(batch)
     out, lse, db = run_gpu(batch, kv_split_tokens=split)
+    if split == 0:  # decodes alone, automatic split: balanced lists, some items share a list
+        info = pa.pa_plan_get_info(db.plan)
+        assert info["decode_list_tokens"] > 0 and info["num_decode_lists"] < info["num_decode_items"]
     assert_close(out, lse, ref_o, ref_l, f"split {split}")
     base_o, base_l, _ = run_gpu(batch, kv_split_tokens=4096)
     assert_close(out, lse, base_o, base_l, f"split {split} vs one split")

@@ -174,3 +174,52 @@ def test_workspace_size_accounts_for_partials():
     assert n == 2 + 16
     ws = pa.pa_plan_workspace_bytes(plan)
     assert ws >= n * 8 * 128 * 4 + n * 8 * 4
+
+
+def _decode_schedule(plan, info):
+    lists = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_LISTS)
+    spans = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_SPANS).reshape(-1, 3)
+    assert len(lists) == info["num_decode_lists"] + 1 and len(spans) == info["num_decode_items"]
+    assert lists[0] == 0 and lists[-1] == len(spans) and np.all(np.diff(lists) >= 1)
+    return lists, spans
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_balanced_decode_lists_partition_the_keys(seed):
+    """A batch of decodes alone, automatic split: the lists cut the decode keys,
+    sequence after sequence in decode-first order, into equal runs; every key
+    of every sequence is covered exactly once, in order."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 60))
+    lens = rng.integers(1, 9000, size=B)
+    plan, info = host_plan([1] * B, lens, H=32, Hkv=8)
+    lists, spans = _decode_schedule(plan, info)
+    W = info["decode_list_tokens"]
+    assert W > 0 and W % 32 == 0 and info["kv_split_tokens"] == W
+    sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
+    assert np.all(sizes[:-1] > W - 32) and np.all(sizes <= W) and sizes[-1] > 0
+    # items start on 32-key boundaries of their sequence (16-key tiles never
+    # straddle a physical block)
+    assert np.all(spans[:, 1] % 32 == 0)
+    assert info["num_decode_lists"] <= 256  # one list per resident group of waves (host plans: 256 CUs)
+    order = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER)
+    pos = 0
+    for b in order:  # all decodes: the spans walk the sequences in order
+        k = 0
+        while k < lens[b]:
+            seq, k0, k1 = spans[pos]
+            assert seq == b and k0 == k and k1 > k0
+            k = k1
+            pos += 1
+    assert pos == len(spans)
+    parts = np.bincount(spans[:, 0], minlength=B)
+    assert np.array_equal(pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS), np.where(parts > 1, parts, 0))
+    assert info["decode_tokens_read"] == int(lens.sum()) * 8
+
+
+def test_decode_lists_are_single_items_beside_prefills_or_with_a_split():
+    lens = [100, 5000, 40, 700]
+    for qlens, split in (([1, 1, 16, 1], 0), ([1, 1, 1, 1], 64)):
+        plan, info = host_plan(qlens, lens, split=split)
+        lists, spans = _decode_schedule(plan, info)
+        assert np.array_equal(lists, np.arange(len(spans) + 1)) and info["decode_list_tokens"] == 0
