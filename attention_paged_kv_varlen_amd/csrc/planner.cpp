@@ -199,7 +199,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
       const int b = hp.order[oi];
       const int L = seq_lens[b];
       int part = 0;
-      for (int k0 = 0; k0 < L;) {
+      for (int k0 = P; k0 < L;) {
         const int room = list_tokens - filled;  // >= 32
         const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
         WorkItem it{};
@@ -209,7 +209,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
         it.lim0 = L - 1;
         it.kv_begin = k0;
         it.kv_end = k0 + take;
-        it.slot = part++;
+        it.slot = n_pc + part++;
         it.causal = 0;
         hp.decode_items.push_back(it);
         dec_read += take;
@@ -220,7 +220,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
           filled = 0;
         }
       }
-      contrib[qsl[b]] = part;
+      contrib[qsl[b]] = n_pc + part;
     }
     if (filled > 0) hp.decode_lists.push_back((int32_t)hp.decode_items.size());
   }
