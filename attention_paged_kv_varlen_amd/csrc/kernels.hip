@@ -46,6 +46,10 @@ constexpr float kLn2 = 0.69314718055994531f;
 // Lazy rescaling: the running max used for exponentiation is only raised when
 // a block's max exceeds it by more than this (log2 units), so P <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+// The wide prefill keeps exponentials taken against a stale running max as
+// long as each lane's sum of them stays below this (P <= 2^64: far from fp32
+// overflow in P, l and O, and bf16 P keeps its relative precision at any scale).
+constexpr float kSpecLimit = 18446744073709551616.0f;  // 2^64
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -823,14 +827,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
       // speculative exponent against the running max
-      float t = -INFINITY;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          p[c][k] = __builtin_fmaf(x[c][k], sl2, -m_run[c]);
-          t = fmaxf(t, p[c][k]);
-        }
+        for (int k = 0; k < 8; ++k) p[c][k] = __builtin_fmaf(x[c][k], sl2, -m_run[c]);
       }
       // (the empty asm keeps the exponentials ahead of the branch, where they
       // can run under the MFMAs, instead of letting them sink into the
@@ -843,8 +843,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
           asm volatile("" : "+v"(p[c][k]));
         }
       }
-      // NaN (an infinite running max meets a masked key) also takes the side path
-      if (__any(!(t <= kRescaleThreshold))) {
+      float ps[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        ps[c] = ((p[c][0] + p[c][1]) + (p[c][2] + p[c][3])) + ((p[c][4] + p[c][5]) + (p[c][6] + p[c][7]));
+      // The values stand unless some lane's sum leaves [0, kSpecLimit]: scores
+      // far above the running max (P may not overflow), or NaN / inf when an
+      // infinite running max (first block) meets the keys.
+      if (__any(!(ps[0] + ps[1] <= kSpecLimit))) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           float mb = x[c][0];
@@ -861,14 +867,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
           const float mref = (m_new == -INFINITY) ? 0.f : m_new;
 #pragma unroll
           for (int k = 0; k < 8; ++k) p[c][k] = fast_exp2(__builtin_fmaf(x[c][k], sl2, -mref));
+          ps[c] = ((p[c][0] + p[c][1]) + (p[c][2] + p[c][3])) + ((p[c][4] + p[c][5]) + (p[c][6] + p[c][7]));
         }
       }
       Frag pf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float s01 = (p[c][0] + p[c][1]) + (p[c][2] + p[c][3]);
-        const float s23 = (p[c][4] + p[c][5]) + (p[c][6] + p[c][7]);
-        l_run[c] += s01 + s23;
+        l_run[c] += ps[c];
         pf[c] = O::pack_p(p[c]);
       }
       // O^T += V^T P^T over the half's 32 keys
