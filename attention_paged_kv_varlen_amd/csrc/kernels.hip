@@ -941,13 +941,15 @@ __device__ __forceinline__ f32x4 load4<float>(const float* src) {
 }
 
 // One wave per (row, head): lane s < count reads partial s's LSE, the wave
-// reduces max and sum of exponentials, then every lane accumulates D / 64
-// consecutive output elements over the partials (loads issued back to back).
+// reduces max and sum of exponentials; then each half-wave takes every other
+// partial (lanes 32 h + j load elements 4 j .. 4 j + 3 of D = 128, 16-byte
+// loads, four partials in flight per half), and the halves are added at the end.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, int n_rows, const float* ws_o,
                                                     const float* ws_lse, T* out, float* lse, int H) {
-  constexpr int EPL = D / 64;  // output elements per lane
+  constexpr int EPL = D / 32;  // output elements per lane of a half-wave
   const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, j = lane & 31;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head) pair
   if (unit >= n_rows * H) return;
   const int h = unit % H;
@@ -972,24 +974,40 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, int n_
   float acc[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
-  for (int s = 0; s < mr.count; ++s) {
+  auto add = [&](int s) {
     const int64_t rec = (int64_t)(mr.pbase + s) * H + h;
     const float w = __expf(ws_lse[rec] - ms) * inv;  // -inf -> 0
-    const float* src = ws_o + rec * D + EPL * lane;
+    const float* src = ws_o + rec * D + EPL * j;
+    if constexpr (EPL == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) acc[k] += w * src[k];
+      for (int k = 0; k < 4; ++k) acc[k] += w * v[k];
+    } else {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(src);
+      acc[0] += w * v[0];
+      acc[1] += w * v[1];
+    }
+  };
+  int s = half;
+  for (; s + 6 < mr.count; s += 8) {
+    add(s);
+    add(s + 2);
+    add(s + 4);
+    add(s + 6);
   }
-  T* dst = out + ((int64_t)mr.row * H + h) * D + EPL * lane;
-  if constexpr (EPL == 2) {
-    if constexpr (sizeof(T) == 2)
-      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0], acc[1]);
-    else
-      *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
-  } else {
-    if constexpr (sizeof(T) == 2)
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(pack_bf16x2(acc[0], 0.f) & 0xFFFFu);
-    else
-      *dst = acc[0];
+  for (; s < mr.count; s += 2) add(s);
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) acc[k] += __shfl_xor(acc[k], 32);
+  if (half == 0) {
+    T* dst = out + ((int64_t)mr.row * H + h) * D + EPL * j;
+    if constexpr (EPL == 4) {
+      store4<T>(dst, f32x4{acc[0], acc[1], acc[2], acc[3]});
+    } else {
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0], acc[1]);
+      else
+        *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
+    }
   }
   if (lane == 0 && lse) lse[(int64_t)mr.row * H + h] = tot > 0.f ? ms + logf(tot) : -INFINITY;
 }
