@@ -55,6 +55,32 @@ def test_small_batch_matches_oracle(name):
     assert_close(out, lse, ref_o, ref_l, name)
 
 
+# Batches of decodes alone with the automatic split: balanced work lists that
+# cross sequence boundaries, under every decode launch shape (waves per
+# workgroup = the largest divisor of Hkv x ceil(g / 16) up to 8).
+DECODE_ONLY = {
+    "g4_hkv2_bs16": dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=16),
+    "g8_hkv8_bs64": dict(num_heads=64, num_kv_heads=8, head_size=128, block_size=64),
+    "g1_hkv6_bs48": dict(num_heads=6, num_kv_heads=6, head_size=128, block_size=48),
+    "g32_hkv1_bs16": dict(num_heads=32, num_kv_heads=1, head_size=128, block_size=16),
+    "g3_hkv3_d64": dict(num_heads=9, num_kv_heads=3, head_size=64, block_size=32),
+    "g2_hkv4_fp32": dict(num_heads=8, num_kv_heads=4, head_size=128, block_size=16, dtype="fp32"),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_ONLY))
+def test_decode_only_balanced_lists_match_oracle(name):
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 1500, size=9).tolist() + [1, 33, 2048]
+    batch = make_batch([1] * len(lens), lens, seed=32, **DECODE_ONLY[name])
+    announce(f"decode_only {name} B={batch.num_seqs}")
+    out, lse, db = run_gpu(batch)
+    info = pa.pa_plan_get_info(db.plan)
+    assert info["decode_list_tokens"] > 0 and info["num_decode_lists"] < info["num_decode_items"]
+    ref_o, ref_l = oracle_full(batch)
+    assert_close(out, lse, ref_o, ref_l, name)
+
+
 def test_cascade_small_matches_oracle_and_non_cascade():
     P = 128
     qlens = [1, 1, 1, 1, 1, 1, 20, 9]
