@@ -14,7 +14,8 @@ Pages it follows (cited by title and section):
     block size a multiple of 16;
   - §Responsabilidades: Q/out are ``[num_tokens, num_heads, head_size]``; the
     metadata carries ``query_start_loc``, ``seq_lens`` and the block table; the
-    FlashInfer builder splits decodes from prefills and moves decodes to the front.
+    FlashInfer builder splits decodes from prefills and moves decodes to the front;
+    the new tokens' K/V are written into the cache by an operation of its own.
 * «El especialista del plato estrella: el backend de atención de vLLM»
   - §Por qué prefill y decode son problemas opuestos: prefill = many queries
     against many keys, decode = one query against all accumulated keys;
@@ -40,5 +41,7 @@ from .attention import (  # noqa: F401
     kv_cache_shape,
     merge_states,
     metadata,
+    slot_mapping,
     to_f64,
+    write_kv,
 )

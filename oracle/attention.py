@@ -136,6 +136,46 @@ def gather(kv_cache: np.ndarray, block_table_row, seq_len: int):
 
 
 # ---------------------------------------------------------------------------
+# Cache write
+# ---------------------------------------------------------------------------
+
+def slot_mapping(query_start_loc, seq_lens, block_table, block_size: int):
+    """Pool slot of every new token, in token order (``int64[T]``).
+
+    «FlashAttention y FlashInfer», §Responsabilidades: putting the new tokens'
+    K/V into the paged cache is an operation of its own, separate from the
+    attention forward.  Query token ``i`` of sequence ``b`` is key position
+    ``c_b + i``; it is stored where the gather reads that position: block
+    ``block_table[b][(c_b + i) // bs]`` at offset ``(c_b + i) % bs``.  The slot
+    number is ``block * bs + offset``.
+    """
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    L = np.asarray(seq_lens, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    out = np.empty(int(qsl[-1]) if len(qsl) else 0, dtype=np.int64)
+    for b in range(len(L)):
+        qb = int(qsl[b + 1] - qsl[b])
+        pos = (int(L[b]) - qb) + np.arange(qb)
+        out[qsl[b]:qsl[b + 1]] = bt[b, pos // block_size] * block_size + pos % block_size
+    return out
+
+
+def write_kv(kv_cache: np.ndarray, key: np.ndarray, value: np.ndarray, slots):
+    """A copy of the pool with token ``t``'s K row ``key[t]`` (``[Hkv, d]``) at slot
+    ``slots[t]`` of the K half and its V row in the V half; a negative slot skips
+    the token.  Slot ``s`` is block ``s // bs``, offset ``s % bs``.
+    """
+    pool = np.array(kv_cache, copy=True)
+    bs = pool.shape[2]
+    for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0:
+            continue
+        pool[s // bs, 0, s % bs] = key[t]
+        pool[s // bs, 1, s % bs] = value[t]
+    return pool
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 

@@ -390,6 +390,55 @@ def check_bf16_widening(O):
     assert list(v[:4]) == [1.0, -2.0, 0.15625, 2.0 ** -126] and np.isnan(v[4])
 
 
+def check_write_kv_fills_pages(O):
+    # Whole prompts written token by token through the slot mapping into an
+    # all-NaN pool reproduce, bit for bit (NaNs included), the pool that the
+    # reshape-based writer builds from the same contiguous K/V and placement.
+    for bs, lens in ((16, [1, 15, 16, 17, 50]), (48, [100, 47, 3])):
+        Ks, Vs = _random_logical(lens, 2, 8, seed=70 + bs)
+        ref, bt = pool_from_logical(Ks, Vs, bs, seed=71 + bs)
+        qsl = _qsl(lens)  # every token is new: q_b = L_b, no context
+        slots = O.slot_mapping(qsl, lens, bt, bs)
+        assert slots.shape == (sum(lens),)
+        got = O.write_kv(np.full_like(ref, np.nan), np.concatenate(Ks), np.concatenate(Vs), slots)
+        assert np.array_equal(got, ref, equal_nan=True)
+
+
+def check_write_kv_chunks_follow_context(O):
+    # Chunks and decodes: new token i of sequence b is key position c_b + i.
+    # Writing fresh rows for the new tokens changes exactly those positions of
+    # the gathered sequence; the context rows and every other slot stay put;
+    # a token with slot -1 is skipped.
+    lens = MIX_L
+    Ks, Vs = _random_logical(lens, 2, 8, seed=80)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=81)
+    qsl = _qsl(MIX_Q)
+    slots = O.slot_mapping(qsl, lens, bt, 16)
+    rng = np.random.default_rng(82)
+    T = int(qsl[-1])
+    newK = rng.standard_normal((T, 2, 8)).astype(np.float32)
+    newV = rng.standard_normal((T, 2, 8)).astype(np.float32)
+    skip = 3  # a token of the third sequence is not written
+    slots_skip = slots.copy()
+    slots_skip[skip] = -1
+    out = O.write_kv(pool, newK, newV, slots_skip)
+    for b, L in enumerate(lens):
+        K, V = O.gather(out, bt[b], L)
+        c = L - MIX_Q[b]
+        want_K, want_V = Ks[b].copy(), Vs[b].copy()
+        for i in range(MIX_Q[b]):
+            t = qsl[b] + i
+            if t != skip:
+                want_K[c + i], want_V[c + i] = newK[t], newV[t]
+        assert np.array_equal(K, want_K) and np.array_equal(V, want_V)
+    written = np.zeros(pool.shape[:3], dtype=bool)
+    for s in slots_skip[slots_skip >= 0]:
+        written[s // 16, :, s % 16] = True
+    assert np.array_equal(out[~written], pool[~written], equal_nan=True)
+    # a lone skipped token leaves the whole pool as it was
+    assert np.array_equal(O.write_kv(pool, newK[:1], newV[:1], np.array([-1])), pool, equal_nan=True)
+
+
 ALL_CHECKS = [
     check_kv_cache_shape,
     check_gather_roundtrip,
@@ -409,4 +458,6 @@ ALL_CHECKS = [
     check_merge_states,
     check_decode_intensity_golden,
     check_bf16_widening,
+    check_write_kv_fills_pages,
+    check_write_kv_chunks_follow_context,
 ]

@@ -41,6 +41,13 @@ MUTANTS = {
                             "if block_size % 8 != 0:\n        raise ValueError(\"block size must"),
     "bf16_widen_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "intensity_drops_pv": ("flops = g * 4 * L * d", "flops = g * 2 * L * d"),
+    "slot_ignores_context": ("pos = (int(L[b]) - qb) + np.arange(qb)", "pos = np.arange(qb)"),
+    "slot_position_off_by_one": ("pos = (int(L[b]) - qb) + np.arange(qb)", "pos = (int(L[b]) - qb) + np.arange(1, qb + 1)"),
+    "slot_block_offset_swapped": ("bt[b, pos // block_size] * block_size + pos % block_size",
+                                  "bt[b, pos % block_size] * block_size + pos // block_size"),
+    "write_kv_halves_swapped": ("pool[s // bs, 0, s % bs] = key[t]\n        pool[s // bs, 1, s % bs] = value[t]",
+                                "pool[s // bs, 1, s % bs] = key[t]\n        pool[s // bs, 0, s % bs] = value[t]"),
+    "write_kv_no_skip": ("        if s < 0:\n            continue\n", ""),
 }
 
 
