@@ -43,5 +43,6 @@ from ._capi import (  # noqa: F401
     pa_profile_start,
     pa_profile_stop,
     pa_status_string,
+    pa_write_kv,
 )
 from .device import DeviceBatch, to_device  # noqa: F401

@@ -23,7 +23,7 @@ PA_BF16, PA_FP32 = 0, 1
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
     "pa_kv_cache_shape", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
-    "pa_plan_workspace_bytes", "pa_forward", "pa_merge_states", "pa_gather_kv",
+    "pa_plan_workspace_bytes", "pa_forward", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
     "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start", "pa_profile_stop",
 )
 
@@ -84,6 +84,7 @@ def lib():
     L.pa_merge_states.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                   c_int32, c_int32, c_void_p]
     L.pa_gather_kv.argtypes = [c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p, c_void_p]
+    L.pa_write_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p]
     L.pa_plan_destroy.argtypes = [c_void_p]
     L.pa_plan_destroy.restype = None
     L.pa_status_string.argtypes = [c_int]
@@ -222,6 +223,11 @@ def pa_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out=None, *, num_tokens=N
 def pa_gather_kv(kv_cache, block_table_row, seq_len: int, params: pa_params, k_out, v_out, stream=None) -> None:
     _check(lib().pa_gather_kv(_ptr(kv_cache), _ptr(block_table_row), int(seq_len), ctypes.byref(params),
                               _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def pa_write_kv(key, value, slot_mapping, num_tokens: int, params: pa_params, kv_cache, stream=None) -> None:
+    _check(lib().pa_write_kv(_ptr(key), _ptr(value), _ptr(slot_mapping), int(num_tokens), ctypes.byref(params),
+                             _ptr(kv_cache), _stream(stream)))
 
 
 def pa_plan_destroy(plan: Plan) -> None:

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <map>
 #include <new>
@@ -332,6 +333,31 @@ pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int
   if (!kv_cache || !block_table_row || !k_out || !v_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
   const int e = pa::launch_gather(kv_cache, block_table_row, seq_len, params->block_size, params->num_kv_heads,
                                   params->head_size, params->dtype, k_out, v_out, stream);
+  if (e != 0) return hip_err((hipError_t)e, "kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
+                      const pa_params* params, void* kv_cache, void* stream) {
+  g_err.clear();
+  if (!params) return set_err(PA_ERR_INVALID_ARG, "params is NULL");
+  if (num_tokens < 0) return set_err(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (params->block_size < 16 || params->block_size % 16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "block size must be a positive multiple of 16");
+  if (params->num_kv_heads < 1 || params->head_size < 1 || params->num_blocks < 1)
+    return set_err(PA_ERR_INVALID_ARG, "num_kv_heads, head_size and num_blocks must be >= 1");
+  if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
+  const int64_t row_bytes =
+      (int64_t)params->num_kv_heads * params->head_size * (params->dtype == PA_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0 || row_bytes > INT32_MAX / 2)
+    return set_err(PA_ERR_UNSUPPORTED, "a K row (num_kv_heads * head_size elements) must be a multiple of 16 bytes");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping || !kv_cache) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(kv_cache)) %
+          16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "key, value and kv_cache must be 16-byte aligned");
+  const int e = pa::launch_write_kv(key, value, slot_mapping, num_tokens, (int)row_bytes, params->block_size,
+                                    (int64_t)params->num_blocks * params->block_size, kv_cache, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }

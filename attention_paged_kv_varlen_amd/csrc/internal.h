@@ -101,6 +101,8 @@ int launch_merge_states(const void* oa, const float* la, const void* ob, const f
                         float* l, int n_tok, int n_heads, int head_size, int dtype, void* stream);
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,
                   int dtype, void* k_out, void* v_out, void* stream);
+int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int row_bytes, int bs,
+                    int64_t n_slots, void* kv, void* stream);
 
 // Launch bookkeeping for pa_profile_* (api.cpp).
 void profile_before(const char* name, void* stream);

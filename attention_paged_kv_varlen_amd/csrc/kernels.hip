@@ -1046,6 +1046,29 @@ __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* kv, co
 }
 
 // ---------------------------------------------------------------------------
+// Cache write: thread i copies 16-byte chunk i % (2 C) of token i / (2 C)
+// (C chunks per K or V row; the first C of the K row, then the V row) to the
+// token's slot.  Consecutive threads move consecutive bytes of one row, so
+// reads and writes are coalesced.
+__global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, const unsigned char* v,
+                                                       const int64_t* slots, int n_tok, int row_bytes, int bs,
+                                                       int64_t n_slots, unsigned char* kv) {
+  const int chunks = row_bytes / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_tok * 2 * chunks) return;
+  const int t = (int)(i / (2 * chunks));
+  const int c = (int)(i % (2 * chunks));
+  const int half = c / chunks;
+  const int off = (c % chunks) * 16;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= n_slots) return;
+  const int64_t blk = s / bs, in = s % bs;
+  const unsigned char* src = (half ? v : k) + (int64_t)t * row_bytes + off;
+  unsigned char* dst = kv + ((blk * 2 + half) * bs + in) * (int64_t)row_bytes + off;
+  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch helpers
 // ---------------------------------------------------------------------------
 template <typename K, typename... Args>
@@ -1186,6 +1209,16 @@ int decode_workgroups_per_cu(int dtype, int head_size, int waves) {
   else if (dtype == PA_FP32 && head_size == 64)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, 64>, threads, 0);
   return e == hipSuccess ? n : 0;
+}
+
+int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int row_bytes, int bs,
+                    int64_t n_slots, void* kv, void* stream) {
+  const int64_t n = (int64_t)n_tok * 2 * (row_bytes / 16);
+  const int64_t nblk = (n + 255) / 256;
+  if (nblk > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+  return launch("write_kv", write_kv_kernel, dim3((unsigned)nblk), dim3(256), stream,
+                static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), slots, n_tok, row_bytes, bs,
+                n_slots, static_cast<unsigned char*>(kv));
 }
 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,

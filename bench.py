@@ -268,12 +268,78 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
     return res
 
 
+def kvwrite_line(steps: int, warmup: int, cpu: bool) -> dict:
+    """The cache write on its own: every token of the causal varlen prefill batch
+    (a fresh K and V row each) written to its slot.  HBM-bound: each row is read
+    once and written once."""
+    import torch
+
+    import attention_paged_kv_varlen_amd as pa
+    from workloads import config_batch, f32_to_bf16_bits
+    batch = config_batch(3, poison=False)
+    T, Hkv, d, bs = batch.num_tokens, batch.num_kv_heads, batch.head_size, batch.block_size
+    qsl, L, bt = batch.query_start_loc, batch.seq_lens, batch.block_table
+    # the caller's slot mapping: query token i of sequence b is key position c_b + i
+    slots = np.empty(T, dtype=np.int64)
+    for b in range(batch.num_seqs):
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        pos = int(L[b]) - (q1 - q0) + np.arange(q1 - q0)
+        slots[q0:q1] = bt[b, pos // bs].astype(np.int64) * bs + pos % bs
+    rng = np.random.default_rng(30)
+    k = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d), dtype=np.float32))
+    dev = "cuda:0"
+    tk = torch.from_numpy(k).view(torch.bfloat16).to(dev)
+    tv = torch.from_numpy(v).view(torch.bfloat16).to(dev)
+    ts = torch.from_numpy(slots).to(dev)
+    pool = torch.from_numpy(batch.kv_cache).view(torch.bfloat16).to(dev)
+    params = pa.make_params(num_seqs=batch.num_seqs, num_heads=batch.num_heads, num_kv_heads=Hkv, head_size=d,
+                            block_size=bs, num_blocks=batch.num_blocks, max_blocks_per_seq=batch.max_blocks_per_seq,
+                            dtype="bf16", scale=batch.scale)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pa.pa_write_kv(tk, tv, ts, T, params, pool, stream)
+    torch.cuda.synchronize()
+    pa.pa_profile_start(steps + 8)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pa.pa_write_kv(tk, tv, ts, T, params, pool, stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = pa.pa_profile_stop()
+    us = {x["name"]: 1e3 * x["total_ms"] / max(x["launches"], 1) for x in kern}
+    nbytes = 2 * T * 2 * Hkv * d * 2  # K and V rows, read once and written once
+    ach = nbytes / (us["write_kv"] * 1e-6) / 1e9
+    line = {
+        "metric": "KV-cache write GB/s (% HBM peak)", "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V rows)",
+        "config": {"workload": f"cache write of the {T} tokens of the causal varlen prefill batch "
+                               f"({Hkv} kv heads, d={d}, bs={bs}, random page placement)", "num_tokens": T},
+        "kernels_us": {n: round(x, 3) for n, x in us.items()},
+        "roofline": {"bound": "hbm", "kernel": "write_kv", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "algorithmic": {"bytes": nbytes},
+    }
+    if cpu:
+        import oracle
+        n = min(T, 4096)
+        host_pool = batch.kv_cache
+        t1 = time.perf_counter()
+        oracle.write_kv(host_pool, k[:n], v[:n], slots[:n])
+        dt = time.perf_counter() - t1
+        line["cpu_baseline"] = {"value": 2 * n * 2 * Hkv * d * 2 / dt / 1e9, "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "seconds": round(dt, 3),
+                                "sample": f"{n} of {T} tokens (numpy, one pool copy included)"}
+    return line
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["kvwrite"], default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -305,6 +371,9 @@ def main(argv=None) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "kvwrite":
+        print(json.dumps(kvwrite_line(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        return 0
     cfg = WORKLOADS[args.workload]
     m = measure(cfg, args.steps, args.warmup)
     batch, counts, t = m["batch"], m["counts"], m["timing"]

@@ -220,6 +220,27 @@ pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, 
                           int32_t head_size, int32_t dtype, void* stream);
 
 /*
+ * Write the new tokens' K and V rows into their pages: the cache update that
+ * comes before attention and is an operation of its own, outside pa_forward
+ * («FlashAttention y FlashInfer», §Responsabilidades).  Query token i of
+ * sequence b is key position c_b + i, which lives in block
+ * block_table[b][(c_b + i) / bs] at offset (c_b + i) % bs; its slot number is
+ * block * bs + offset.
+ *  key, value    device [num_tokens, num_kv_heads, head_size] of params->dtype,
+ *                16-byte aligned.
+ *  slot_mapping  device int64[num_tokens]; a negative slot skips the token, and
+ *                so does a slot at or past num_blocks * block_size.
+ *  kv_cache      device pool (num_blocks, 2, bs, Hkv, d) of params->dtype, 16-byte
+ *                aligned, written in place; slots not named keep their contents.
+ * Uses params->num_kv_heads, head_size, block_size, num_blocks and dtype.  Two
+ * tokens with the same slot race.  Asynchronous on `stream`, copies bit for bit.
+ * Errors: INVALID_ARG (sizes, NULL or misaligned pointers), UNSUPPORTED (dtype,
+ * a K row that is not a whole number of 16-byte chunks), HIP.
+ */
+pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
+                      const pa_params* params, void* kv_cache, void* stream);
+
+/*
  * Copy one sequence's K and V out of the pool, contiguous, bit for bit.
  * «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
  * token t is slot t % bs of block block_table_row[t / bs].

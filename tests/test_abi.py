@@ -51,3 +51,26 @@ def test_status_strings_and_last_error():
 def test_profile_stop_without_session_is_an_error():
     with pytest.raises(pa.PagedAttnError):
         pa.pa_profile_stop()
+
+
+def test_write_kv_validates_before_any_launch():
+    """pa_write_kv checks its arguments on the host: nothing runs on a device."""
+    import attention_paged_kv_varlen_amd as pa
+    p = pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4,
+                       max_blocks_per_seq=4, dtype="bf16", scale=0.1)
+    pa.pa_write_kv(None, None, None, 0, p, None, stream=0)  # no tokens: nothing to do
+    for args, status in (
+        ((16, 16, 16, -1, p), pa.PA_ERR_INVALID_ARG),          # negative count
+        ((None, 16, 16, 3, p), pa.PA_ERR_INVALID_ARG),         # NULL key
+        ((8, 16, 16, 3, p), pa.PA_ERR_INVALID_ARG),            # key not 16-byte aligned
+        ((16, 16, 16, 3, pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=2, head_size=128, block_size=24,
+                                        num_blocks=4, max_blocks_per_seq=4, dtype="bf16", scale=0.1)),
+         pa.PA_ERR_INVALID_ARG),                               # block size not a multiple of 16
+        ((16, 16, 16, 3, pa.make_params(num_seqs=1, num_heads=1, num_kv_heads=1, head_size=4, block_size=16,
+                                        num_blocks=4, max_blocks_per_seq=4, dtype="bf16", scale=0.1)),
+         pa.PA_ERR_UNSUPPORTED),                               # 8-byte K row
+    ):
+        key, value, slots, n, params = args
+        with pytest.raises(pa.PagedAttnError) as ei:
+            pa.pa_write_kv(key, value, slots, n, params, kv_cache=16, stream=0)
+        assert ei.value.status == status, args

@@ -306,3 +306,69 @@ def test_full_config5_cascade():
     ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
                                          batch.seq_lens, batch.scale, rows, dtype=batch.dtype)
     assert_close(co[rows], cl[rows], ref_o, ref_l, f"config 5 cascade ({len(rows)} rows)")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_write_kv_is_bit_exact(dtype):
+    """Random tokens into a NaN-poisoned pool: the pool after pa_write_kv equals
+    the oracle's write_kv bit for bit; negative and out-of-pool slots are skipped."""
+    import torch
+    announce(f"write_kv {dtype}")
+    rng = np.random.default_rng(41)
+    nb, bs, Hkv, d, T = 40, 16, 4, 128, 300
+    shape = (nb, 2, bs, Hkv, d)
+    if dtype == "bf16":
+        pool = np.full(shape, 0x7FC0, dtype=np.uint16)
+        k = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32))
+        v = f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32))
+    else:
+        pool = np.full(shape, np.nan, dtype=np.float32)
+        k = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+        v = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)  # distinct slots
+    slots[::17] = -1
+    slots[5] = nb * bs + 3  # past the pool: skipped
+    want = oracle.write_kv(pool, k, v, np.where(slots >= nb * bs, -1, slots))
+
+    def dev(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.int16) if a.dtype == np.uint16 else t).to("cuda:0")
+    tp, tk, tv, ts = dev(pool), dev(k), dev(v), dev(slots)
+    params = pa.make_params(num_seqs=1, num_heads=Hkv, num_kv_heads=Hkv, head_size=d, block_size=bs, num_blocks=nb,
+                            max_blocks_per_seq=1, dtype=dtype, scale=0.1)
+    pa.pa_write_kv(tk, tv, ts, T, params, tp)
+    torch.cuda.synchronize()
+    got = tp.cpu().numpy()
+    if dtype == "bf16":
+        assert np.array_equal(got.view(np.uint16), want)
+    else:
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_write_kv_then_attention_matches_oracle():
+    """The new tokens of a mixed batch, erased from the pool and written back
+    through the slot mapping with pa_write_kv, give back the same pool and the
+    oracle's attention."""
+    import torch
+    batch = SMALL["mixed_bf16_d128_g4_bs16"]()
+    announce("write_kv then attention")
+    slots = oracle.slot_mapping(batch.query_start_loc, batch.seq_lens, batch.block_table, batch.block_size)
+    T = batch.num_tokens
+    Hkv, d, bs = batch.num_kv_heads, batch.head_size, batch.block_size
+    k = np.empty((T, Hkv, d), dtype=np.uint16)
+    v = np.empty((T, Hkv, d), dtype=np.uint16)
+    erased = batch.kv_cache.copy()
+    for t, s in enumerate(slots):
+        k[t], v[t] = batch.kv_cache[s // bs, 0, s % bs], batch.kv_cache[s // bs, 1, s % bs]
+        erased[s // bs, :, s % bs] = 0x7FC0
+    tp = torch.from_numpy(erased).view(torch.int16).to("cuda:0")
+    params = pa.make_params(num_seqs=batch.num_seqs, num_heads=batch.num_heads, num_kv_heads=Hkv, head_size=d,
+                            block_size=bs, num_blocks=batch.num_blocks, max_blocks_per_seq=batch.max_blocks_per_seq,
+                            dtype="bf16", scale=batch.scale)
+    pa.pa_write_kv(torch.from_numpy(k).view(torch.int16).to("cuda:0"), torch.from_numpy(v).view(torch.int16).to("cuda:0"),
+                   torch.from_numpy(slots).to("cuda:0"), T, params, tp)
+    torch.cuda.synchronize()
+    assert np.array_equal(tp.cpu().numpy().view(np.uint16), batch.kv_cache)
+    out, lse, _ = run_gpu(batch, kv_cache=tp.cpu().numpy().view(np.uint16))
+    ref_o, ref_l = oracle_full(batch)
+    assert_close(out, lse, ref_o, ref_l, "write_kv then attention")
