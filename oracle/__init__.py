@@ -26,6 +26,9 @@ Pages it follows (cited by title and section):
 * «AttentionBackend: capa de abstracción de backends de atención»
   - §Motivación de diseño and §Límites y fallos: partial attentions are combined
     through their softmax log-sum-exp, whose base (natural log here) must match.
+* FP8 KV cache: «FlashAttention y FlashInfer», §Motivación de diseño and
+  §Límites y fallos (an ``fp8_e4m3`` cache and per-head quantisation scales);
+  the format and the readings are in :mod:`oracle.fp8`.
 
 Every public function has a pin in ``tests/`` that checks it against something
 other than itself (closed forms, invariants, brute force, a library special
@@ -44,4 +47,12 @@ from .attention import (  # noqa: F401
     slot_mapping,
     to_f64,
     write_kv,
+)
+from .fp8 import (  # noqa: F401
+    dequantize_pool,
+    e4m3_decode,
+    e4m3_encode,
+    quantize,
+    scales_per_head,
+    write_kv_fp8,
 )

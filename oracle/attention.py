@@ -24,6 +24,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .fp8 import e4m3_decode, scales_per_head
+
 
 # ---------------------------------------------------------------------------
 # Pool shape and element conversion
@@ -210,8 +212,22 @@ def _dims(q: np.ndarray, kv_cache: np.ndarray):
     return H, Hkv, H // Hkv
 
 
+def _kv_values(K, V, dtype: str, kv_dtype, k_scale, v_scale):
+    """Exact float64 values of gathered K/V rows ``[L, Hkv, d]``: the pool's
+    element type, or e4m3 codes times their K / V scale (one per KV head or one
+    for the tensor; see :mod:`oracle.fp8`)."""
+    if kv_dtype in (None, "same"):
+        return to_f64(K, dtype), to_f64(V, dtype)
+    if kv_dtype != "fp8_e4m3":
+        raise ValueError(f"kv_dtype {kv_dtype!r}")
+    Hkv = K.shape[1]
+    ks = scales_per_head(k_scale, Hkv)
+    vs = scales_per_head(v_scale, Hkv)
+    return e4m3_decode(K) * ks[None, :, None], e4m3_decode(V) * vs[None, :, None]
+
+
 def attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale, rows,
-                   *, dtype: str = "bf16", causal: bool = True):
+                   *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Output and log-sum-exp of the chosen token rows only (any order).
 
     Same definition as :func:`attention`; used where the whole batch is too large
@@ -232,7 +248,7 @@ def attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale, r
         cb = Lb - qb
         i = rows[sel] - qsl[b]                                # query index in the sequence
         K, V = gather(kv_cache, block_table[b], Lb)
-        K, V = to_f64(K, dtype), to_f64(V, dtype)
+        K, V = _kv_values(K, V, dtype, kv_dtype, k_scale, v_scale)
         t = np.arange(Lb)
         if causal:
             visible = t[None, :] <= (cb + i)[:, None]
@@ -248,7 +264,7 @@ def attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale, r
 
 
 def attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
-              *, dtype: str = "bf16", causal: bool = True):
+              *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Exact attention for every token row of a mixed varlen batch.
 
     For row ``r = query_start_loc[b] + i``, head ``h`` and KV head ``h // g``, the
@@ -260,12 +276,17 @@ def attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
     against many keys) and decode rows (one query against the whole KV) follow
     the same definition; only the number of rows differs.
 
+    With ``kv_dtype="fp8_e4m3"`` the pool holds e4m3 codes and the keys and
+    values are ``decode(code) * k_scale`` and ``decode(code) * v_scale`` (one scale,
+    or one per KV head); queries keep ``dtype``.
+
     Returns ``out [T, H, d]`` and ``lse [T, H]`` in float64, rows in the
     caller's order.
     """
     T = int(np.asarray(query_start_loc)[-1])
     return attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
-                          np.arange(T), dtype=dtype, causal=causal)
+                          np.arange(T), dtype=dtype, causal=causal, kv_dtype=kv_dtype,
+                          k_scale=k_scale, v_scale=v_scale)
 
 
 def merge_states(o1, lse1, o2, lse2):
@@ -293,7 +314,8 @@ def merge_states(o1, lse1, o2, lse2):
 
 
 def cascade_attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
-                      common_prefix_len: int, *, dtype: str = "bf16", causal: bool = True):
+                      common_prefix_len: int, *, dtype: str = "bf16", causal: bool = True,
+                      kv_dtype=None, k_scale=1.0, v_scale=1.0):
     """Cascade form: shared prefix once, each sequence's own suffix, merged by LSE.
 
     «El especialista del plato estrella», §Qué aporta FlashInfer: when the batch
@@ -315,7 +337,7 @@ def cascade_attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale
 
     # prefix: every query row of the batch against keys 0 .. P-1
     Kp, Vp = gather(kv_cache, md["prefix_blocks"], P)
-    Kp, Vp = to_f64(Kp, dtype), to_f64(Vp, dtype)
+    Kp, Vp = _kv_values(Kp, Vp, dtype, kv_dtype, k_scale, v_scale)
     o1 = np.zeros((T, H, d))
     l1 = np.full((T, H), -np.inf)
     vis_p = np.ones((T, P), dtype=bool)
@@ -333,7 +355,7 @@ def cascade_attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale
         r0, r1 = int(qsl[b]), int(qsl[b + 1])
         cb = Lb - (r1 - r0)
         K, V = gather(kv_cache, block_table[b], Lb)
-        K, V = to_f64(K[P:], dtype), to_f64(V[P:], dtype)
+        K, V = _kv_values(K[P:], V[P:], dtype, kv_dtype, k_scale, v_scale)
         t = np.arange(P, Lb)
         i = np.arange(r1 - r0)
         if causal:

@@ -439,6 +439,162 @@ def check_write_kv_chunks_follow_context(O):
     assert np.array_equal(O.write_kv(pool, newK[:1], newV[:1], np.array([-1])), pool, equal_nan=True)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) KV cache
+# ---------------------------------------------------------------------------
+
+def _code_pool(lens, Hkv, d, seed, bs=16):
+    """An e4m3 pool holding random finite codes for each sequence's K/V, placed
+    by the reshape-based writer; unused slots hold the NaN code 0x7F.  Returns
+    the pool, the block table and the per-sequence code arrays."""
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    Kc = [rng.choice(finite, size=(L, Hkv, d)) for L in lens]
+    Vc = [rng.choice(finite, size=(L, Hkv, d)) for L in lens]
+    pf, bt = pool_from_logical([k.astype(np.float32) for k in Kc], [v.astype(np.float32) for v in Vc], bs,
+                               seed=seed + 1)
+    pool = np.where(np.isnan(pf), 0x7F, pf).astype(np.uint8)
+    return pool, bt, Kc, Vc
+
+
+def check_e4m3_decode_library(O):
+    # Every code against the float8_e4m3fn dtype of the PyTorch CPU library
+    # (the same OCP E4M3 format): equal values, NaN at the same codes (0x7F, 0xFF).
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert list(np.flatnonzero(np.isnan(got))) == [0x7F, 0xFF]
+    # closed forms: 1.0, the largest finite 448, the smallest normal and subnormal
+    assert O.e4m3_decode([0x38, 0x7E, 0x08, 0x01, 0x80]).tolist() == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9, 0.0]
+
+
+def check_e4m3_encode(O):
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    # every finite value encodes back to its own code (+0 and -0 included)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(finite)), finite)
+    # round to nearest, ties to even: PyTorch's float8_e4m3fn conversion on random
+    # in-range float32 values and on every midpoint between neighbouring values
+    import torch
+    rng = np.random.default_rng(90)
+    vals = np.sort(O.e4m3_decode(finite[finite < 0x80]))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.02, 0.02, 1000), mids, -mids]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), ref)
+    # readings: saturation at +-448, NaN -> 0x7F, the sign of zero is kept
+    got = O.e4m3_encode(np.array([449.0, 1e9, -1e9, np.nan, -0.0, -2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -10]))
+    assert got.tolist() == [0x7E, 0x7E, 0xFE, 0x7F, 0x80, 0x80, 0x00, 0x02]
+
+
+def check_quantize_divides_in_float32(O):
+    # The written code is encode(float32(x / s)): find x, s with x / s just above
+    # the tie 1.0625 (between 1.0 = 0x38 and 1.125 = 0x39) but within half a
+    # float32 ulp of it, so the float32 quotient is the tie itself and rounds to
+    # the even code 0x38, whereas rounding the exact quotient would give 0x39.
+    rng = np.random.default_rng(91)
+    for _ in range(20000):
+        s = np.float32(rng.uniform(1.5, 3.0))
+        x = np.float32(np.float32(1.0625) * s)
+        for k in range(-3, 4):
+            xx = np.nextafter(x, np.float32(np.inf) if k > 0 else np.float32(-np.inf)) if k else x
+            exact = float(xx) / float(s)
+            if 0 < exact - 1.0625 < 2.0 ** -25 and np.float32(xx) / s == np.float32(1.0625):
+                assert O.quantize(xx, s) == 0x38
+                assert O.e4m3_encode(exact) == 0x39
+                # per-tensor and per-head scales give the same vector
+                assert np.array_equal(O.scales_per_head(s, 3), np.full(3, float(s)))
+                assert np.array_equal(O.scales_per_head([1, 2, 4], 3), [1.0, 2.0, 4.0])
+                return
+    raise AssertionError("no test value found")
+
+
+def check_fp8_attention_reduces_to_fp32(O):
+    # With power-of-two scales, code * scale is exact in float32, so attention
+    # over the e4m3 pool must equal attention over the float32 pool of those
+    # values (the already pinned fp32 definition).  K and V scales differ, and
+    # differ per KV head, so a swapped or misapplied scale changes the result.
+    lens, qlens = [17, 33, 40, 64], [1, 1, 9, 64]
+    Hkv, g, d = 2, 2, 16
+    pool, bt, Kc, Vc = _code_pool(lens, Hkv, d, seed=92)
+    ks = np.array([2.0 ** -6, 2.0 ** -4], dtype=np.float32)
+    vs = np.array([2.0 ** -3, 2.0 ** -7], dtype=np.float32)
+    Kf = [(O.e4m3_decode(k) * ks[None, :, None]).astype(np.float32) for k in Kc]
+    Vf = [(O.e4m3_decode(v) * vs[None, :, None]).astype(np.float32) for v in Vc]
+    pool32, bt2 = pool_from_logical(Kf, Vf, 16, seed=93)
+    rng = np.random.default_rng(94)
+    q = rng.standard_normal((sum(qlens), Hkv * g, d)).astype(np.float32)
+    qb = (q.view(np.uint32) >> np.uint32(16)).astype(np.uint16)       # truncate to bf16 patterns
+    q32 = (qb.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    out8, lse8 = O.attention(qb, pool, bt, _qsl(qlens), np.array(lens), 0.25, dtype="bf16",
+                             kv_dtype="fp8_e4m3", k_scale=ks, v_scale=vs)
+    out32, lse32 = O.attention(q32, pool32, bt2, _qsl(qlens), np.array(lens), 0.25, dtype="fp32")
+    assert np.abs(out8 - out32).max() < 1e-12 and np.abs(lse8 - lse32).max() < 1e-12
+    # the dequantised pool is the same float32 pool up to placement
+    deq = O.dequantize_pool(pool, ks, vs)
+    for b, L in enumerate(lens):
+        K, V = O.gather(deq, bt[b], L)
+        assert np.array_equal(K, Kf[b].astype(np.float64)) and np.array_equal(V, Vf[b].astype(np.float64))
+    # cascade over the e4m3 pool agrees with the full definition
+    P = 32
+    cl = [P + 5, P + 20, P + 1]
+    poolc, btc, _, _ = _code_pool_shared(cl, Hkv, d, seed=95, prefix_blocks=P // 16)
+    qc = (rng.standard_normal((3, Hkv * g, d)).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    full = O.attention(qc, poolc, btc, _qsl([1, 1, 1]), np.array(cl), 0.3, kv_dtype="fp8_e4m3", k_scale=ks, v_scale=vs)
+    casc = O.cascade_attention(qc, poolc, btc, _qsl([1, 1, 1]), np.array(cl), 0.3, P, kv_dtype="fp8_e4m3",
+                               k_scale=ks, v_scale=vs)
+    assert np.abs(full[0] - casc[0]).max() < 1e-12 and np.abs(full[1] - casc[1]).max() < 1e-12
+
+
+def _code_pool_shared(lens, Hkv, d, seed, prefix_blocks):
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    Kc = [rng.choice(finite, size=(L, Hkv, d)) for L in lens]
+    Vc = [rng.choice(finite, size=(L, Hkv, d)) for L in lens]
+    pf, bt = pool_from_logical([k.astype(np.float32) for k in Kc], [v.astype(np.float32) for v in Vc], 16,
+                               seed=seed + 1, shared_prefix_blocks=prefix_blocks)
+    return np.where(np.isnan(pf), 0x7F, pf).astype(np.uint8), bt, Kc, Vc
+
+
+def check_write_kv_fp8(O):
+    # Values that are exactly code * scale (power-of-two per-head scales) written
+    # through the slot mapping come back as those codes; values beyond the range
+    # saturate; a skipped token and the other slots keep the pool's bytes.
+    lens, qlens = [17, 40], [1, 8]
+    Hkv, d = 2, 8
+    pool, bt, Kc, Vc = _code_pool(lens, Hkv, d, seed=96)
+    qsl = _qsl(qlens)
+    slots = O.slot_mapping(qsl, lens, bt, 16)
+    T = int(qsl[-1])
+    rng = np.random.default_rng(97)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    newKc = rng.choice(finite, size=(T, Hkv, d))
+    newVc = rng.choice(finite, size=(T, Hkv, d))
+    ks = np.array([0.5, 4.0], dtype=np.float32)
+    vs = np.array([0.125, 2.0], dtype=np.float32)
+    newK = O.e4m3_decode(newKc) * ks[None, :, None]
+    newV = O.e4m3_decode(newVc) * vs[None, :, None]
+    newK[0, 1, 0] = 1e6                      # saturates to 448 * 4 -> code 0x7E
+    slots_skip = slots.copy()
+    slots_skip[2] = -1
+    out = O.write_kv_fp8(pool, newK, newV, slots_skip, ks, vs)
+    want = pool.copy()
+    for t, sl in enumerate(slots_skip):
+        if sl < 0:
+            continue
+        want[sl // 16, 0, sl % 16] = newKc[t]
+        want[sl // 16, 1, sl % 16] = newVc[t]
+    want[slots_skip[0] // 16, 0, slots_skip[0] % 16, 1, 0] = 0x7E
+    assert np.array_equal(out, want)
+    # one scale for the whole tensor broadcasts to every head
+    one = O.write_kv_fp8(pool, newK[:1] * 0 + 3.0, newV[:1] * 0 - 3.0, slots[:1], [2.0], [2.0])
+    sl = slots[0]
+    assert (one[sl // 16, 0, sl % 16] == 0x3C).all() and (one[sl // 16, 1, sl % 16] == 0xBC).all()
+
+
 ALL_CHECKS = [
     check_kv_cache_shape,
     check_gather_roundtrip,
@@ -458,6 +614,11 @@ ALL_CHECKS = [
     check_merge_states,
     check_decode_intensity_golden,
     check_bf16_widening,
+    check_e4m3_decode_library,
+    check_e4m3_encode,
+    check_quantize_divides_in_float32,
+    check_fp8_attention_reduces_to_fp32,
+    check_write_kv_fp8,
     check_write_kv_fills_pages,
     check_write_kv_chunks_follow_context,
 ]

@@ -11,7 +11,10 @@ import pytest
 
 from tests import oracle_pins
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "attention.py")
+SRC_FP8 = os.path.join(ORACLE_DIR, "fp8.py")
+FP8_IMPORT = "from .fp8 import e4m3_decode, scales_per_head\n"
 
 MUTANTS = {
     "causal_off_by_one": ("visible = t[None, :] <= (cb + i)[:, None]\n        else:\n            visible = np.ones((len(i), Lb)",
@@ -51,9 +54,46 @@ MUTANTS = {
 }
 
 
-def _load(src: str):
+# Mutations of the e4m3 module (format, rounding, scales, quantised write) and
+# of the attention module's use of it.
+MUTANTS_FP8 = {
+    "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    "e4m3_subnormal_step": ("subnormal = sign * m * 2.0 ** -9", "subnormal = sign * m * 2.0 ** -10"),
+    "e4m3_mantissa_bits": ("(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),
+    "e4m3_inf_codes_nan": ("(e == 15) & (m == 7)", "(e == 15)"),
+    "e4m3_ties_away": ("best = best[codes[best] % 2 == 0]", "best = best[-1:]"),
+    "e4m3_nan_saturates": ("            out[n] = 0x7F\n            continue", "            out[n] = 0x7E\n            continue"),
+    "e4m3_zero_sign_lost": ("neg = v < 0 or (v == 0 and np.signbit(v))", "neg = v < 0"),
+    "quantize_in_float64": ("y = np.asarray(x, dtype=np.float32) / np.float32(scale)\n    return e4m3_encode(y.astype(np.float32))",
+                            "y = np.asarray(x, dtype=np.float64) / float(scale)\n    return e4m3_encode(y)"),
+    "quantize_multiplies": ("/ np.float32(scale)", "* np.float32(scale)"),
+    "per_tensor_scale_ignored": ("return np.full(num_kv_heads, s[0])", "return np.full(num_kv_heads, 1.0)"),
+    "dequantize_scales_swapped": ("out[:, 0] *= ks[None, None, :, None]\n    out[:, 1] *= vs[None, None, :, None]",
+                                  "out[:, 0] *= vs[None, None, :, None]\n    out[:, 1] *= ks[None, None, :, None]"),
+    "write_fp8_v_with_k_scale": ("quantize(value[t, h], vs[h])", "quantize(value[t, h], ks[h])"),
+    "write_fp8_no_skip": ("        if s < 0:\n            continue\n        for h", "        for h"),
+}
+MUTANTS_ATT_FP8 = {
+    "attention_kv_scales_swapped": ("e4m3_decode(K) * ks[None, :, None], e4m3_decode(V) * vs[None, :, None]",
+                                    "e4m3_decode(K) * vs[None, :, None], e4m3_decode(V) * ks[None, :, None]"),
+    "attention_scale_reversed_heads": ("e4m3_decode(K) * ks[None, :, None]", "e4m3_decode(K) * ks[None, ::-1, None]"),
+}
+MUTANTS.update(MUTANTS_ATT_FP8)
+
+
+def _load(src: str, fp8_src: str | None = None):
+    """The attention module from ``src`` with the e4m3 helpers of ``fp8_src``
+    (the real module's source unless given) in its namespace; the combined
+    namespace also exposes the e4m3 functions the pins call."""
+    if fp8_src is None:
+        with open(SRC_FP8) as f:
+            fp8_src = f.read()
+    m8 = types.ModuleType("oracle_fp8_mutant")
+    exec(compile(fp8_src, "oracle_fp8_mutant", "exec"), m8.__dict__)
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    mod.__dict__.update({k: v for k, v in m8.__dict__.items() if not k.startswith("__")})
+    assert src.count(FP8_IMPORT) == 1
+    exec(compile(src.replace(FP8_IMPORT, ""), "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
 
@@ -62,6 +102,27 @@ def test_unmutated_copy_passes():
         mod = _load(f.read())
     for check in oracle_pins.ALL_CHECKS:
         check(mod)
+
+
+def _caught(mod):
+    failed = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:  # any failure (assertion or crash) counts as caught
+            failed.append(check.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_FP8))
+def test_fp8_mutant_is_caught(name):
+    old, new = MUTANTS_FP8[name]
+    with open(SRC_FP8) as f:
+        src8 = f.read()
+    assert src8.count(old) >= 1, f"mutation site for {name} not found"
+    with open(SRC) as f:
+        mod = _load(f.read(), src8.replace(old, new, 1))
+    assert _caught(mod), f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
