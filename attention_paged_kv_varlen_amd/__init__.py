@@ -24,12 +24,15 @@ from ._capi import (  # noqa: F401
     PA_ERR_OOM,
     PA_ERR_UNSUPPORTED,
     PA_FP32,
+    PA_KV_FP8_E4M3,
+    PA_KV_SAME,
     PA_OK,
     PagedAttnError,
     Plan,
     lib,
     make_params,
     pa_forward,
+    pa_forward_fp8,
     pa_gather_kv,
     pa_kv_cache_shape,
     pa_last_error,
@@ -44,5 +47,6 @@ from ._capi import (  # noqa: F401
     pa_profile_stop,
     pa_status_string,
     pa_write_kv,
+    pa_write_kv_fp8,
 )
 from .device import DeviceBatch, to_device  # noqa: F401

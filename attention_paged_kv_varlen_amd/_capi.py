@@ -17,14 +17,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_BF16, PA_FP32 = 0, 1
+PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
 (PA_ARRAY_ORDER, PA_ARRAY_IS_DECODE, PA_ARRAY_PREFIX_BLOCKS, PA_ARRAY_ROW_PARTIALS, PA_ARRAY_DECODE_LISTS,
  PA_ARRAY_DECODE_SPANS) = range(6)
 
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
     "pa_kv_cache_shape", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
-    "pa_plan_workspace_bytes", "pa_forward", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
-    "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start", "pa_profile_stop",
+    "pa_plan_workspace_bytes", "pa_forward", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
+    "pa_write_kv_fp8", "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start",
+    "pa_profile_stop",
 )
 
 
@@ -34,6 +36,7 @@ class pa_params(ctypes.Structure):
         ("head_size", c_int32), ("block_size", c_int32), ("num_blocks", c_int32),
         ("max_blocks_per_seq", c_int32), ("dtype", c_int32), ("causal", c_int32),
         ("common_prefix_len", c_int32), ("kv_split_tokens", c_int32), ("scale", c_float),
+        ("kv_dtype", c_int32),
     ]
 
 
@@ -85,6 +88,10 @@ def lib():
                                   c_int32, c_int32, c_void_p]
     L.pa_gather_kv.argtypes = [c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p, c_void_p]
     L.pa_write_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p]
+    L.pa_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                 c_void_p, c_void_p, c_size_t, c_void_p]
+    L.pa_write_kv_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p,
+                                  c_int32, c_void_p, c_void_p]
     L.pa_plan_destroy.argtypes = [c_void_p]
     L.pa_plan_destroy.restype = None
     L.pa_status_string.argtypes = [c_int]
@@ -147,11 +154,12 @@ class Plan:
 
 
 def make_params(*, num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq,
-                dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0) -> pa_params:
+                dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0, kv_dtype="same") -> pa_params:
     dt = {"bf16": PA_BF16, "fp32": PA_FP32}.get(dtype, dtype)
+    kvt = {"same": PA_KV_SAME, None: PA_KV_SAME, "fp8_e4m3": PA_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
     return pa_params(int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size), int(block_size),
                      int(num_blocks), int(max_blocks_per_seq), int(dt), int(bool(causal)),
-                     int(common_prefix_len), int(kv_split_tokens), float(scale))
+                     int(common_prefix_len), int(kv_split_tokens), float(scale), int(kvt))
 
 
 # ---------------------------------------------------------------------------
@@ -209,6 +217,17 @@ def pa_forward(plan: Plan, q, kv_cache, block_table, out, lse=None, workspace=No
                             _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def pa_forward_fp8(plan: Plan, q, kv_cache, block_table, k_scale, v_scale, out, lse=None, workspace=None,
+                   workspace_bytes=None, num_scales=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if num_scales is None:
+        num_scales = int(k_scale.numel())
+    _check(lib().pa_forward_fp8(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(k_scale),
+                                _ptr(v_scale), int(num_scales), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace_bytes, _stream(stream)))
+
+
 def pa_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out=None, *, num_tokens=None, num_heads=None,
                     head_size=None, dtype=None, stream=None) -> None:
     if num_tokens is None:
@@ -228,6 +247,14 @@ def pa_gather_kv(kv_cache, block_table_row, seq_len: int, params: pa_params, k_o
 def pa_write_kv(key, value, slot_mapping, num_tokens: int, params: pa_params, kv_cache, stream=None) -> None:
     _check(lib().pa_write_kv(_ptr(key), _ptr(value), _ptr(slot_mapping), int(num_tokens), ctypes.byref(params),
                              _ptr(kv_cache), _stream(stream)))
+
+
+def pa_write_kv_fp8(key, value, slot_mapping, num_tokens: int, params: pa_params, k_scale, v_scale, kv_cache,
+                    num_scales=None, stream=None) -> None:
+    if num_scales is None:
+        num_scales = int(k_scale.numel())
+    _check(lib().pa_write_kv_fp8(_ptr(key), _ptr(value), _ptr(slot_mapping), int(num_tokens), ctypes.byref(params),
+                                 _ptr(k_scale), _ptr(v_scale), int(num_scales), _ptr(kv_cache), _stream(stream)))
 
 
 def pa_plan_destroy(plan: Plan) -> None:

@@ -140,7 +140,7 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
     const int g = params->num_heads / params->num_kv_heads;
     const int nw = pa::decode_waves_per_wg(params->num_kv_heads * ((g + 15) / 16));
     DeviceGuard guard(device);
-    dec_wgs = guard.ok ? pa::decode_workgroups_per_cu(params->dtype, params->head_size, nw) : 0;
+    dec_wgs = guard.ok ? pa::decode_workgroups_per_cu(params->dtype, params->kv_dtype, params->head_size, nw) : 0;
   }
 
   pa_plan* plan = new (std::nothrow) pa_plan();
@@ -262,11 +262,10 @@ pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, in
 
 size_t pa_plan_workspace_bytes(const pa_plan* plan) { return plan ? plan->ws_bytes : 0; }
 
-pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table, void* out,
-                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
-  if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
+// The forward of pa_forward and pa_forward_fp8 after their own checks.
+static pa_status forward_common(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                                const float* k_scale, const float* v_scale, int n_scales) {
   const pa::HostPlan& hp = plan->hp;
   if (hp.T == 0) return PA_OK;
   if (!q || !kv_cache || !block_table || !out) return set_err(PA_ERR_INVALID_ARG, "q/kv_cache/block_table/out is NULL");
@@ -282,6 +281,7 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, c
   g.bs = p.block_size;
   g.max_blocks = p.max_blocks_per_seq;
   g.dtype = p.dtype;
+  g.kv_dtype = p.kv_dtype;
   g.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
   g.ps = hp.ps;
 
@@ -291,6 +291,9 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, c
   t.block_table = block_table;
   t.out = out;
   t.lse = lse;
+  t.k_scale = k_scale;
+  t.v_scale = v_scale;
+  t.n_scales = n_scales;
   if (plan->ws_bytes > 0) {
     unsigned char* w = static_cast<unsigned char*>(workspace);
     t.ws_o = reinterpret_cast<float*>(w);
@@ -302,6 +305,36 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, c
   const int e = pa::launch_forward(g, plan->ds, t, st);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
+}
+
+pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
+  if (plan->hp.p.kv_dtype != PA_KV_SAME)
+    return set_err(PA_ERR_INVALID_ARG, "the plan's pool holds e4m3 codes: use pa_forward_fp8 with its scales");
+  return forward_common(plan, q, kv_cache, block_table, out, lse, workspace, workspace_bytes, stream, nullptr,
+                        nullptr, 0);
+}
+
+pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                         const float* k_scale, const float* v_scale, int32_t num_scales, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
+  const pa_params& p = plan->hp.p;
+  if (p.kv_dtype != PA_KV_FP8_E4M3)
+    return set_err(PA_ERR_INVALID_ARG, "pa_forward_fp8 needs a plan made with kv_dtype = PA_KV_FP8_E4M3");
+  if (num_scales != 1 && num_scales != p.num_kv_heads)
+    return set_err(PA_ERR_INVALID_ARG, "num_scales must be 1 or num_kv_heads");
+  if (plan->hp.T == 0) return PA_OK;
+  if (!k_scale || !v_scale) return set_err(PA_ERR_INVALID_ARG, "k_scale / v_scale is NULL");
+  if (reinterpret_cast<uintptr_t>(kv_cache) % 16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
+  return forward_common(plan, q, kv_cache, block_table, out, lse, workspace, workspace_bytes, stream, k_scale,
+                        v_scale, num_scales);
 }
 
 pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o_out,
@@ -329,10 +362,15 @@ pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int
   if (params->num_kv_heads < 1 || params->head_size < 1 || params->head_size % 8 != 0)
     return set_err(PA_ERR_INVALID_ARG, "num_kv_heads >= 1 and head_size a positive multiple of 8 required");
   if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
+  if (params->kv_dtype != PA_KV_SAME && params->kv_dtype != PA_KV_FP8_E4M3)
+    return set_err(PA_ERR_INVALID_ARG, "kv_dtype must be PA_KV_SAME or PA_KV_FP8_E4M3");
+  const int elem = params->kv_dtype == PA_KV_FP8_E4M3 ? 1 : params->dtype == PA_BF16 ? 2 : 4;
+  if ((int64_t)params->num_kv_heads * params->head_size * elem % 16 != 0)
+    return set_err(PA_ERR_UNSUPPORTED, "a K row (num_kv_heads * head_size elements) must be a multiple of 16 bytes");
   if (seq_len == 0) return PA_OK;
   if (!kv_cache || !block_table_row || !k_out || !v_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
   const int e = pa::launch_gather(kv_cache, block_table_row, seq_len, params->block_size, params->num_kv_heads,
-                                  params->head_size, params->dtype, k_out, v_out, stream);
+                                  params->head_size, elem, k_out, v_out, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }
@@ -347,6 +385,8 @@ pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_ma
   if (params->num_kv_heads < 1 || params->head_size < 1 || params->num_blocks < 1)
     return set_err(PA_ERR_INVALID_ARG, "num_kv_heads, head_size and num_blocks must be >= 1");
   if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
+  if (params->kv_dtype != PA_KV_SAME)
+    return set_err(PA_ERR_INVALID_ARG, "an e4m3 pool is written by pa_write_kv_fp8 (with its scales)");
   const int64_t row_bytes =
       (int64_t)params->num_kv_heads * params->head_size * (params->dtype == PA_BF16 ? 2 : 4);
   if (row_bytes % 16 != 0 || row_bytes > INT32_MAX / 2)
@@ -358,6 +398,36 @@ pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_ma
     return set_err(PA_ERR_INVALID_ARG, "key, value and kv_cache must be 16-byte aligned");
   const int e = pa::launch_write_kv(key, value, slot_mapping, num_tokens, (int)row_bytes, params->block_size,
                                     (int64_t)params->num_blocks * params->block_size, kv_cache, stream);
+  if (e != 0) return hip_err((hipError_t)e, "kernel launch");
+  return PA_OK;
+}
+
+pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
+                          const pa_params* params, const float* k_scale, const float* v_scale, int32_t num_scales,
+                          void* kv_cache, void* stream) {
+  g_err.clear();
+  if (!params) return set_err(PA_ERR_INVALID_ARG, "params is NULL");
+  if (num_tokens < 0) return set_err(PA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (params->block_size < 16 || params->block_size % 16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "block size must be a positive multiple of 16");
+  if (params->num_kv_heads < 1 || params->head_size < 1 || params->num_blocks < 1)
+    return set_err(PA_ERR_INVALID_ARG, "num_kv_heads, head_size and num_blocks must be >= 1");
+  if (params->kv_dtype != PA_KV_FP8_E4M3) return set_err(PA_ERR_INVALID_ARG, "params->kv_dtype is not PA_KV_FP8_E4M3");
+  if (params->dtype != PA_BF16) return set_err(PA_ERR_UNSUPPORTED, "e4m3 writes take bf16 key/value");
+  if (params->head_size % 16 != 0) return set_err(PA_ERR_UNSUPPORTED, "head_size must be a multiple of 16");
+  if ((int64_t)params->num_kv_heads * params->head_size > INT32_MAX / 4)
+    return set_err(PA_ERR_INVALID_ARG, "K row too large");
+  if (num_scales != 1 && num_scales != params->num_kv_heads)
+    return set_err(PA_ERR_INVALID_ARG, "num_scales must be 1 or num_kv_heads");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !slot_mapping || !kv_cache || !k_scale || !v_scale)
+    return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(kv_cache)) %
+          16 != 0)
+    return set_err(PA_ERR_INVALID_ARG, "key, value and kv_cache must be 16-byte aligned");
+  const int e = pa::launch_write_kv_fp8(key, value, slot_mapping, num_tokens, params->num_kv_heads, params->head_size,
+                                        params->block_size, (int64_t)params->num_blocks * params->block_size, k_scale,
+                                        v_scale, num_scales, kv_cache, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }

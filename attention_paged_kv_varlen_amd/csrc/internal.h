@@ -48,13 +48,17 @@ struct PrefillShape {
   int head_groups;     // g / heads_per_wg
 };
 PrefillShape prefill_shape(int group, int tiles, int max_heads);
-// The wide prefill kernel serves bf16 with head size 128: 4 waves, 8 column
-// tiles per workgroup, both tiles of a wave on one head.
-inline bool use_wide_prefill(int dtype, int head_size) { return dtype == PA_BF16 && head_size == 128; }
+// The wide prefill kernel serves bf16 with head size 128 on a bf16 pool: 4
+// waves, 8 column tiles per workgroup, both tiles of a wave on one head.  An
+// e4m3 pool goes through the general prefill kernel, which widens the codes to
+// bf16 while it stages them in LDS.
+inline bool use_wide_prefill(int dtype, int head_size, int kv_dtype) {
+  return dtype == PA_BF16 && head_size == 128 && kv_dtype == PA_KV_SAME;
+}
 
 // Everything the kernels need besides the caller's tensors.
 struct LaunchGeom {
-  int H, Hkv, g, D, bs, max_blocks, dtype;
+  int H, Hkv, g, D, bs, max_blocks, dtype, kv_dtype;
   float scale_log2;  // scale * log2(e)
   PrefillShape ps;
 };
@@ -82,6 +86,9 @@ struct Tensors {
   float* lse;
   float* ws_o;    // [num_partials, H, D]
   float* ws_lse;  // [num_partials, H]
+  const float* k_scale;  // e4m3 pool: [n_scales] K and V scales (1 or Hkv); else null
+  const float* v_scale;
+  int n_scales;
 };
 
 // The caller's stream, plus an optional side stream with fork/join events: when
@@ -100,9 +107,12 @@ int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o,
                         float* l, int n_tok, int n_heads, int head_size, int dtype, void* stream);
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,
-                  int dtype, void* k_out, void* v_out, void* stream);
+                  int elem_bytes, void* k_out, void* v_out, void* stream);
 int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int row_bytes, int bs,
                     int64_t n_slots, void* kv, void* stream);
+int launch_write_kv_fp8(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int D, int bs,
+                        int64_t n_slots, const float* k_scale, const float* v_scale, int n_scales, void* kv,
+                        void* stream);
 
 // Launch bookkeeping for pa_profile_* (api.cpp).
 void profile_before(const char* name, void* stream);
@@ -130,7 +140,7 @@ inline int decode_waves_per_wg(int units) {
 }
 // Decode workgroups of `waves` waves that fit on one CU at once (kernels.hip;
 // the device must be current), or 0 if the query fails.
-int decode_workgroups_per_cu(int dtype, int head_size, int waves);
+int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves);
 
 // Returns PA_OK or an error with `err` filled in.  decode_wgs_per_cu: resident
 // decode workgroups per CU (0 = unknown: no balanced decode lists).

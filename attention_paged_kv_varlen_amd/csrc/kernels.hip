@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// e4m3 codes -> bf16, exactly (every e4m3 value is a bf16 value): the two codes
+// in bytes 0-1 (HI = false) or 2-3 (HI = true) of w, first code in the low half.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight codes (two dwords, code i in byte i) -> eight bf16 in element order.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return u32x4{e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo), e4m3x2_to_bf16x2<false>(hi),
+               e4m3x2_to_bf16x2<true>(hi)};
+}
+
 // ---------------------------------------------------------------------------
 // Element-type operations.  A Frag is the 8 contraction elements one lane
 // supplies to a 16x16 MFMA step of K = 32 (bf16: one 16x16x32; fp32: eight
@@ -214,7 +226,13 @@ struct KArgs {
   int tiles_per_head;  // prefill only
   int tiles_per_wg;    // prefill only: 2 per wave
   float scale_log2;
+  const float* k_scale;  // e4m3 pool: K / V scales, one (n_scales = 1) or one per KV head
+  const float* v_scale;
+  int n_scales;
 };
+
+// Scale of KV head kvh from a per-tensor (n = 1) or per-head scale array.
+__device__ __forceinline__ float kv_scale_of(const float* sc, int n, int kvh) { return sc[n > 1 ? kvh : 0]; }
 
 // Online-softmax update of one 16-column tile with the 8 scores (log2 units,
 // masked = -inf) a lane holds for its column.  Returns P in `p`.
@@ -244,11 +262,12 @@ __device__ __forceinline__ void softmax_step(float (&x)[8], float& m_run, float&
 }
 
 // Normalise and write one column's result: to out/lse directly, or as a
-// partial record (fp32 o and lse) when the row merges several parts.
+// partial record (fp32 o and lse) when the row merges several parts.  omul
+// multiplies the output (the V scale of an e4m3 pool, else 1).
 template <typename T, int VE>
 __device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int slot, int qd,
-                                             const f32x4 (&o)[VE], float m_run, float l_run) {
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+                                             const f32x4 (&o)[VE], float m_run, float l_run, float omul) {
+  const float inv = l_run > 0.f ? omul / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   constexpr int D = 16 * VE;
   const int pb = a.row_pbase[row];
@@ -278,9 +297,14 @@ __device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int
 // ---------------------------------------------------------------------------
 // Decode: one wave per work item (a KV range of one sequence for one KV head);
 // the columns are the query heads of that KV head (up to 16 per head group).
+// KV is the pool's element type: T, or uint8_t for e4m3 codes (bf16 queries),
+// which are widened to bf16 in registers; the K scale joins the softmax scale
+// and the V scale multiplies the output.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename KV, int D>
 __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
+  constexpr bool F8 = std::is_same<KV, uint8_t>::value;
+  static_assert(!F8 || std::is_same<T, uint16_t>::value, "e4m3 pools take bf16 queries");
   constexpr int VE = D / 16;
   constexpr int KS = D / 32;
   using O = Ops<T, VE>;
@@ -300,30 +324,35 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
   const int hgi = (int)(blockIdx.x % (unsigned)wgs_per_list) * nw + wave;
   const int kvh = hgi / a.head_groups;
   const int hgrp = hgi % a.head_groups;
+  const float sl2 = F8 ? a.scale_log2 * kv_scale_of(a.k_scale, a.n_scales, kvh) : a.scale_log2;
+  const float omul = F8 ? kv_scale_of(a.v_scale, a.n_scales, kvh) : 1.f;
   const int item_end = a.lists[list + 1];
   for (int idx = a.lists[list]; idx < item_end; ++idx) {
     const WorkItem it = a.items[idx];
     const int r = lane & 15, qd = lane >> 4;
 
     const T* q = static_cast<const T*>(a.q);
-    const T* kv = static_cast<const T*>(a.kv);
+    const KV* kv = static_cast<const KV*>(a.kv);
 
-    // Q^T operand: column r = query head kvh * g + hgrp * 16 + r
+    // Q^T operand: column r = query head kvh * g + hgrp * 16 + r.  Lane group qd
+    // supplies contraction elements d = 8 qd + 32 kk + e (e4m3: d = D/4 qd +
+    // 8 kk + e, so that its K elements are D/4 contiguous bytes of the row)
     const int hcol = hgrp * 16 + r;
     const bool colv = hcol < a.g;
     const int head = kvh * a.g + (colv ? hcol : 0);
     Frag qf[KS];
     {
-      const T* qp = q + ((int64_t)it.row0 * a.H + head) * D + 8 * qd;
+      const T* qp = q + ((int64_t)it.row0 * a.H + head) * D;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) qf[kk] = colv ? O::load(qp + 32 * kk) : O::zero();
+      for (int kk = 0; kk < KS; ++kk)
+        qf[kk] = colv ? O::load(qp + (F8 ? (D / 4) * qd + 8 * kk : 8 * qd + 32 * kk)) : O::zero();
     }
 
     const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
     const int64_t slot_stride = (int64_t)a.Hkv * D;
     const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
     const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-    const T* kvh_base = kv + (int64_t)kvh * D;
+    const KV* kvh_base = kv + (int64_t)kvh * D;
     const int kv_end = it.kv_end;
 
     f32x4 o[VE];
@@ -337,7 +366,7 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
     auto tile_block = [&](int t) { return min(t, kv_end - 1) / a.bs; };
     int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
     for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
-      const T* pb[2];
+      const KV* pb[2];
       int pst[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -348,16 +377,41 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int key = min(t0 + 16 * tt + r, kv_end - 1);
-        const T* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
+        if constexpr (F8) {
+          // D/4 contiguous codes, 16 per load (two k-steps)
+          const KV* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + (D / 4) * qd;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
+          for (int j = 0; j < KS / 2; ++j) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 16 * j);
+            kf[tt][2 * j] = Frag{e4m3x8_to_bf16(w[0], w[1])};
+            kf[tt][2 * j + 1] = Frag{e4m3x8_to_bf16(w[2], w[3])};
+          }
+        } else {
+          const KV* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
+        }
       }
       VRaw vr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tt = e >> 2;
         const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
-        vr[e] = O::load_v(pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r);
+        const KV* vp = pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r;
+        if constexpr (F8) {
+          if constexpr (VE == 8) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(vp);
+            const u32x4 b = e4m3x8_to_bf16(w[0], w[1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vr[e].w[j] = b[j];
+          } else {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
+            vr[e].w[0] = e4m3x2_to_bf16x2<false>(w);
+            vr[e].w[1] = e4m3x2_to_bf16x2<true>(w);
+          }
+        } else {
+          vr[e] = O::load_v(vp);
+        }
       }
       if (t0 + 32 < kv_end) {
         pid[0] = btrow[tile_block(t0 + 32)];
@@ -376,7 +430,7 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = t0 + 16 * (e >> 2) + 4 * qd + (e & 3);
-        const float sv = s[e >> 2][e & 3] * a.scale_log2;
+        const float sv = s[e >> 2][e & 3] * sl2;
         x[e] = (full || key < kv_end) ? sv : -INFINITY;
       }
       float p[8];
@@ -391,7 +445,7 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run);
+    if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run, omul);
   }
 }
 
@@ -399,17 +453,21 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 // Prefill (and the cascade prefix pass): a workgroup of 4 waves owns 128
 // columns, 8 tiles of 16 (tile j: head j / tiles_per_head of the head group,
 // positions 16 * (j % tiles_per_head) ..); wave w takes tiles 2w and 2w + 1.
-// 64-key (32 for fp32) K/V blocks are gathered into LDS once per workgroup.
+// 64-key (32 for fp32) K/V blocks are gathered into LDS once per workgroup;
+// e4m3 codes (KV = uint8_t) are widened to bf16 on the way.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, typename KV, int D>
 __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
+  constexpr bool F8 = std::is_same<KV, uint8_t>::value;
+  static_assert(!F8 || std::is_same<T, uint16_t>::value, "e4m3 pools take bf16 queries");
   constexpr int VE = D / 16;
   constexpr int KS = D / 32;
   constexpr int KT = sizeof(T) == 2 ? 64 : 32;          // keys per LDS block
-  constexpr int ROWB = D * (int)sizeof(T) + 16;         // padded LDS row, bytes
-  constexpr int CPR = D * (int)sizeof(T) / 16;          // 16-byte chunks per key row
+  constexpr int ROWB = D * (int)sizeof(T) + 16;         // padded LDS row (element type T), bytes
+  constexpr int CPR = D * (int)sizeof(KV) / 16;         // 16-byte chunks per key row in the pool
   constexpr int RPI = 256 / CPR;                        // key rows per load step
   constexpr int NLD = KT / RPI;                         // load steps per block
+  constexpr int LCH = 16 * (int)(sizeof(T) / sizeof(KV));  // LDS bytes per pool chunk
   using O = Ops<T, VE>;
   using Frag = typename O::Frag;
   using VRaw = typename O::VRaw;
@@ -430,8 +488,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
   const int r = lane & 15, qd = lane >> 4;
 
   const T* q = static_cast<const T*>(a.q);
-  const T* kv = static_cast<const T*>(a.kv);
+  const KV* kv = static_cast<const KV*>(a.kv);
   const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
+  const float sl2 = F8 ? a.scale_log2 * kv_scale_of(a.k_scale, a.n_scales, kvh) : a.scale_log2;
+  const float omul = F8 ? kv_scale_of(a.v_scale, a.n_scales, kvh) : 1.f;
 
   // the wave's two column tiles
   int head[2], pos0[2], lim[2], tile_min_lim[2];
@@ -458,7 +518,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
   const int64_t slot_stride = (int64_t)a.Hkv * D;
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-  const T* kvh_base = kv + (int64_t)kvh * D;
+  const KV* kvh_base = kv + (int64_t)kvh * D;
   const int chunk = tid % CPR;
 
   u32x4 stK[NLD], stV[NLD];
@@ -467,7 +527,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
     for (int j = 0; j < NLD; ++j) {
       const int key = min(kb + tid / CPR + j * RPI, kv_hi - 1);
       const int blk = key / a.bs;
-      const T* base = kvh_base + (int64_t)btrow[blk] * blk_stride + (int64_t)(key - blk * a.bs) * slot_stride;
+      const KV* base = kvh_base + (int64_t)btrow[blk] * blk_stride + (int64_t)(key - blk * a.bs) * slot_stride;
       stK[j] = reinterpret_cast<const u32x4*>(base)[chunk];
       stV[j] = reinterpret_cast<const u32x4*>(base + v_half)[chunk];
     }
@@ -476,8 +536,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int kr = tid / CPR + j * RPI;
-      *reinterpret_cast<u32x4*>(ldsK + kr * ROWB + 16 * chunk) = stK[j];
-      *reinterpret_cast<u32x4*>(ldsV + kr * ROWB + 16 * chunk) = stV[j];
+      unsigned char* dk = ldsK + kr * ROWB + LCH * chunk;
+      unsigned char* dv = ldsV + kr * ROWB + LCH * chunk;
+      if constexpr (F8) {
+        *reinterpret_cast<u32x4*>(dk) = e4m3x8_to_bf16(stK[j][0], stK[j][1]);
+        *reinterpret_cast<u32x4*>(dk + 16) = e4m3x8_to_bf16(stK[j][2], stK[j][3]);
+        *reinterpret_cast<u32x4*>(dv) = e4m3x8_to_bf16(stV[j][0], stV[j][1]);
+        *reinterpret_cast<u32x4*>(dv + 16) = e4m3x8_to_bf16(stV[j][2], stV[j][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(dk) = stK[j];
+        *reinterpret_cast<u32x4*>(dv) = stV[j];
+      }
     }
   };
 
@@ -530,7 +599,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = k0 + 16 * (e >> 2) + 4 * qd + (e & 3);
-          const float sv = s[c][e >> 2][e & 3] * a.scale_log2;
+          const float sv = s[c][e >> 2][e & 3] * sl2;
           x[e] = (full || (key <= lim[c] && key < kv_hi)) ? sv : -INFINITY;
         }
         float p[8];
@@ -557,7 +626,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     const int pos = pos0[c] + r;
-    if (pos < it.nrows) write_column<T, VE>(a, it.row0 + pos, head[c], it.slot, qd, o[c], m_run[c], l);
+    if (pos < it.nrows) write_column<T, VE>(a, it.row0 + pos, head[c], it.slot, qd, o[c], m_run[c], l, omul);
   }
 }
 
@@ -1068,6 +1137,58 @@ __global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, c
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+// Quantising cache write into an e4m3 pool: one thread per 16 elements of a
+// token's K or V row (16 consecutive elements never straddle two KV heads,
+// since the head size is a multiple of 16).  Code = nearest e4m3 value of the
+// float32 quotient x / scale (round to nearest even in the conversion), with the
+// quotient clamped to +-448 first so that large values saturate; NaN -> 0x7F.
+__global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                                                           int n_tok, int Hkv, int D, int bs, int64_t n_slots,
+                                                           const float* ks, const float* vs, int n_scales,
+                                                           unsigned char* kv) {
+  const int row = Hkv * D;  // elements per K row = bytes per pool row
+  const int chunks = row / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n_tok * 2 * chunks) return;
+  const int t = (int)(i / (2 * chunks));
+  const int c = (int)(i % (2 * chunks));
+  const int half = c / chunks;
+  const int off = (c % chunks) * 16;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= n_slots) return;
+  const float sc = kv_scale_of(half ? vs : ks, n_scales, off / D);
+  const uint16_t* src = (half ? v : k) + (int64_t)t * row + off;
+  const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
+  const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    y[2 * j] = __uint_as_float(w0[j] << 16);
+    y[2 * j + 1] = __uint_as_float(w0[j] & 0xFFFF0000u);
+    y[8 + 2 * j] = __uint_as_float(w1[j] << 16);
+    y[8 + 2 * j + 1] = __uint_as_float(w1[j] & 0xFFFF0000u);
+  }
+  u32x4 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = y[4 * j + e] / sc;
+      q[e] = x != x ? x : fminf(fmaxf(x, -448.f), 448.f);
+    }
+    uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)pk, true);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (q[e] != q[e]) pk = (pk & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+    out[j] = pk;
+  }
+  const int64_t blk = s / bs, in = s % bs;
+  unsigned char* dst = kv + ((blk * 2 + half) * bs + in) * (int64_t)row + off;
+  *reinterpret_cast<u32x4*>(dst) = out;
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch helpers
 // ---------------------------------------------------------------------------
@@ -1086,20 +1207,20 @@ int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args
 // workgroups with the head group varying fastest.  Workgroups go to the eight
 // XCDs round-robin by linear index, so with 8 | Hkv x head_groups every XCD
 // serves a fixed set of KV heads and the pages of one KV head stay in one L2.
-template <typename T, int D>
+template <typename T, typename KV, int D>
 int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) {
   const int64_t n = (int64_t)n_items * p.Hkv * p.head_groups;
   if (n > INT32_MAX) return (int)hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)n);
-  if constexpr (std::is_same<T, uint16_t>::value && D == 128)
+  if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint16_t>::value && D == 128)
   {
     return launch(name, prefill_wide_kernel, grid, dim3(256), stream, p);
   }
   else
-    return launch(name, prefill_kernel<T, D>, grid, dim3(256), stream, p);
+    return launch(name, prefill_kernel<T, KV, D>, grid, dim3(256), stream, p);
 }
 
-template <typename T, int D>
+template <typename T, typename KV, int D>
 int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, const Streams& st, const char* tag) {
   KArgs a{};
   a.q = t.q;
@@ -1116,6 +1237,9 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   a.bs = g.bs;
   a.max_blocks = g.max_blocks;
   a.scale_log2 = g.scale_log2;
+  a.k_scale = t.k_scale;
+  a.v_scale = t.v_scale;
+  a.n_scales = t.n_scales;
   char name[48];
   int err = 0;
 
@@ -1141,7 +1265,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.tiles_per_head = g.ps.tiles_per_head;
     p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, s.n_prefix, mstream, p);
+    err = launch_prefill<T, KV, D>(name, s.n_prefix, mstream, p);
     if (err) return err;
   }
   if (s.n_prefill > 0) {
@@ -1153,7 +1277,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     p.tiles_per_head = g.ps.tiles_per_head;
     p.tiles_per_wg = g.ps.tiles;
     snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
-    err = launch_prefill<T, D>(name, s.n_prefill, mstream, p);
+    err = launch_prefill<T, KV, D>(name, s.n_prefill, mstream, p);
     if (err) return err;
   }
   if (s.n_decode > 0) {
@@ -1169,7 +1293,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     d.lists = s.decode_lists;
     const int64_t nwg = (int64_t)s.n_decode_lists * (nhg / nw);
     if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-    err = launch(name, decode_kernel<T, D>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
+    err = launch(name, decode_kernel<T, KV, D>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
     if (err) return err;
   }
   if (fork) {
@@ -1190,24 +1314,34 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
 }  // namespace
 
 int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t, const Streams& st) {
-  if (g.dtype == PA_BF16) {
-    return g.D == 128 ? forward_impl<uint16_t, 128>(g, s, t, st, "bf16") : forward_impl<uint16_t, 64>(g, s, t, st, "bf16");
+  if (g.dtype == PA_BF16 && g.kv_dtype == PA_KV_FP8_E4M3) {
+    return g.D == 128 ? forward_impl<uint16_t, uint8_t, 128>(g, s, t, st, "bf16_e4m3")
+                      : forward_impl<uint16_t, uint8_t, 64>(g, s, t, st, "bf16_e4m3");
   }
-  return g.D == 128 ? forward_impl<float, 128>(g, s, t, st, "fp32") : forward_impl<float, 64>(g, s, t, st, "fp32");
+  if (g.dtype == PA_BF16) {
+    return g.D == 128 ? forward_impl<uint16_t, uint16_t, 128>(g, s, t, st, "bf16")
+                      : forward_impl<uint16_t, uint16_t, 64>(g, s, t, st, "bf16");
+  }
+  return g.D == 128 ? forward_impl<float, float, 128>(g, s, t, st, "fp32") : forward_impl<float, float, 64>(g, s, t, st, "fp32");
 }
 
-int decode_workgroups_per_cu(int dtype, int head_size, int waves) {
+int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   const int threads = 64 * waves;
-  if (dtype == PA_BF16 && head_size == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, 128>, threads, 0);
+  const bool f8 = kv_dtype == PA_KV_FP8_E4M3;
+  if (dtype == PA_BF16 && f8 && head_size == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 128>, threads, 0);
+  else if (dtype == PA_BF16 && f8 && head_size == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 64>, threads, 0);
+  else if (dtype == PA_BF16 && head_size == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 128>, threads, 0);
   else if (dtype == PA_BF16 && head_size == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, 64>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 64>, threads, 0);
   else if (dtype == PA_FP32 && head_size == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, 128>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 128>, threads, 0);
   else if (dtype == PA_FP32 && head_size == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, 64>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 64>, threads, 0);
   return e == hipSuccess ? n : 0;
 }
 
@@ -1219,6 +1353,17 @@ int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_to
   return launch("write_kv", write_kv_kernel, dim3((unsigned)nblk), dim3(256), stream,
                 static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), slots, n_tok, row_bytes, bs,
                 n_slots, static_cast<unsigned char*>(kv));
+}
+
+int launch_write_kv_fp8(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int D, int bs,
+                        int64_t n_slots, const float* k_scale, const float* v_scale, int n_scales, void* kv,
+                        void* stream) {
+  const int64_t n = (int64_t)n_tok * 2 * (Hkv * D / 16);
+  const int64_t nblk = (n + 255) / 256;
+  if (nblk > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+  return launch("write_kv_e4m3", write_kv_fp8_kernel, dim3((unsigned)nblk), dim3(256), stream,
+                static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slots, n_tok, Hkv, D, bs, n_slots,
+                k_scale, v_scale, n_scales, static_cast<unsigned char*>(kv));
 }
 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,
@@ -1233,9 +1378,9 @@ int launch_merge_states(const void* oa, const float* la, const void* ob, const f
                 (const float*)ob, lb, (float*)o, l, n4, head_size);
 }
 
-int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D, int dtype, void* k_out,
-                  void* v_out, void* stream) {
-  const int64_t row_bytes = (int64_t)Hkv * D * (dtype == PA_BF16 ? 2 : 4);
+int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D, int elem_bytes,
+                  void* k_out, void* v_out, void* stream) {
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes;
   const int64_t n = (int64_t)seq_len * (row_bytes / 16);
   if (n == 0) return 0;
   return launch("gather", gather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), stream,

@@ -74,6 +74,10 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     return fail(err, PA_ERR_UNSUPPORTED, "head_size %lld not built (64, 128)", p.head_size);
   if (p.dtype != PA_BF16 && p.dtype != PA_FP32)
     return fail(err, PA_ERR_UNSUPPORTED, "dtype %lld not built (PA_BF16, PA_FP32)", p.dtype);
+  if (p.kv_dtype != PA_KV_SAME && p.kv_dtype != PA_KV_FP8_E4M3)
+    return fail(err, PA_ERR_INVALID_ARG, "kv_dtype %lld (PA_KV_SAME, PA_KV_FP8_E4M3)", p.kv_dtype);
+  if (p.kv_dtype == PA_KV_FP8_E4M3 && p.dtype != PA_BF16)
+    return fail(err, PA_ERR_UNSUPPORTED, "an e4m3 pool is built for bf16 queries only");
   if (p.num_blocks < 1) return fail(err, PA_ERR_INVALID_ARG, "num_blocks %lld < 1", p.num_blocks);
   if (p.max_blocks_per_seq < 1)
     return fail(err, PA_ERR_INVALID_ARG, "max_blocks_per_seq %lld < 1", p.max_blocks_per_seq);
@@ -155,7 +159,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
 
   // ---- schedule
   // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
-  hp.ps = use_wide_prefill(p.dtype, p.head_size) ? prefill_shape(g, 8, 4) : prefill_shape(g, 8, 8);
+  hp.ps = use_wide_prefill(p.dtype, p.head_size, p.kv_dtype) ? prefill_shape(g, 8, 4) : prefill_shape(g, 8, 8);
   const int QB = hp.ps.rows_per_item;
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;

@@ -38,7 +38,9 @@
  *  - Calls that launch work are asynchronous on the given HIP stream (NULL = the
  *    default stream); they neither allocate nor synchronise.
  *  - Element types: PA_BF16 (bfloat16, stored as 16-bit patterns) or PA_FP32.
- *    q, kv_cache and out share one element type; lse is always float32.
+ *    q and out share one element type; lse is always float32.  kv_cache has
+ *    the same element type, or holds 8-bit e4m3 codes with K and V scales
+ *    (pa_params.kv_dtype = PA_KV_FP8_E4M3, bf16 queries; see pa_forward_fp8).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -60,6 +62,17 @@ typedef enum pa_status {
 
 typedef enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 } pa_dtype;
 
+/*
+ * Element type of the paged pool.  PA_KV_FP8_E4M3: one byte per element, an
+ * OCP 8-bit float with 4 exponent bits (bias 7) and 3 mantissa bits (largest
+ * finite value 448, NaN only at 0x7F and 0xFF, no infinities); a K entry stands
+ * for decode(code) * k_scale and a V entry for decode(code) * v_scale, with one
+ * scale per tensor or one per KV head.  «FlashAttention y FlashInfer»,
+ * §Motivación de diseño and §Límites y fallos: an fp8 (e4m3) KV cache with
+ * per-head quantisation scales; the pages give no formula, this is the reading.
+ */
+typedef enum pa_kv_dtype { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+
 /* Sizes of one batch.  All fields are read by pa_plan_create only. */
 typedef struct pa_params {
   int32_t num_seqs;           /* B >= 0 */
@@ -76,6 +89,8 @@ typedef struct pa_params {
                                  (automatic on a batch of decodes only: balanced work lists, see
                                  pa_plan_info.num_decode_lists) */
   float scale;                /* softmax scale applied to q . k (positive, finite) */
+  int32_t kv_dtype;           /* pa_kv_dtype: 0 = the pool has element type dtype; PA_KV_FP8_E4M3
+                                 needs dtype PA_BF16 (else PA_ERR_UNSUPPORTED) */
 } pa_params;
 
 /* Opaque, immutable schedule for one batch; reusable across layers and calls. */
@@ -198,12 +213,33 @@ size_t pa_plan_workspace_bytes(const pa_plan* plan);
  * for `stream` and which `stream` waits for before the final merge (event
  * record/wait only, so the call can be captured into a graph).  Concurrent calls
  * on one plan need separate workspaces, and their side-stream work serialises.
- * Errors: INVALID_ARG (host-only plan, NULL pointers, small workspace),
- * HIP (launch failure).
+ * Errors: INVALID_ARG (host-only plan, NULL pointers, small workspace, a plan
+ * whose pool holds e4m3 codes: those run through pa_forward_fp8), HIP (launch
+ * failure).
  */
 pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
                      const int32_t* block_table, void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * pa_forward over a pool of e4m3 codes (plan made with kv_dtype =
+ * PA_KV_FP8_E4M3): the keys and values are decode(code) * k_scale and
+ * decode(code) * v_scale («FlashAttention y FlashInfer», §Motivación de diseño
+ * and §Límites y fallos: fp8 KV cache, per-head quantisation scales).
+ *  q, out      device bf16 [T, H, d].
+ *  kv_cache    device uint8 [num_blocks, 2, bs, Hkv, d], 16-byte aligned.
+ *  k_scale, v_scale  device float32[num_scales]; num_scales is 1 (one scale for
+ *              the tensor) or Hkv (one per KV head); read by the kernels, so
+ *              they may change between calls without a new plan.  Positive and
+ *              finite (not checked on the device).
+ * Everything else as pa_forward.  Errors: INVALID_ARG (as pa_forward, a plan
+ * without an e4m3 pool, NULL scales, num_scales not 1 or Hkv, misaligned pool),
+ * HIP.
+ */
+pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cache,
+                         const int32_t* block_table, const float* k_scale, const float* v_scale,
+                         int32_t num_scales, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * Combine two partial attentions over disjoint key sets by their LSE.
@@ -234,20 +270,39 @@ pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, 
  *                aligned, written in place; slots not named keep their contents.
  * Uses params->num_kv_heads, head_size, block_size, num_blocks and dtype.  Two
  * tokens with the same slot race.  Asynchronous on `stream`, copies bit for bit.
- * Errors: INVALID_ARG (sizes, NULL or misaligned pointers), UNSUPPORTED (dtype,
- * a K row that is not a whole number of 16-byte chunks), HIP.
+ * Errors: INVALID_ARG (sizes, NULL or misaligned pointers, an e4m3 pool: see
+ * pa_write_kv_fp8), UNSUPPORTED (dtype, a K row that is not a whole number of
+ * 16-byte chunks), HIP.
  */
 pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
                       const pa_params* params, void* kv_cache, void* stream);
 
 /*
+ * pa_write_kv into a pool of e4m3 codes (params->kv_dtype = PA_KV_FP8_E4M3):
+ * element x of a K row of KV head h is stored as the code nearest to the
+ * float32 quotient x / k_scale[h] (ties to the even code, saturating at +-448;
+ * NaN is stored as 0x7F), V likewise with v_scale.  The pages name the fp8
+ * cache and its scales but not the rounding; this is the reading.
+ *  key, value    device bf16 [num_tokens, num_kv_heads, head_size], 16-byte aligned.
+ *  k_scale, v_scale  device float32[num_scales], num_scales 1 or num_kv_heads.
+ *  kv_cache      device uint8 pool, 16-byte aligned, written in place.
+ * Slots as in pa_write_kv.  Errors: INVALID_ARG (as pa_write_kv, a pool that
+ * is not e4m3, NULL scales, num_scales), UNSUPPORTED (dtype other than bf16,
+ * head_size not a multiple of 16), HIP.
+ */
+pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
+                          const pa_params* params, const float* k_scale, const float* v_scale,
+                          int32_t num_scales, void* kv_cache, void* stream);
+
+/*
  * Copy one sequence's K and V out of the pool, contiguous, bit for bit.
  * «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
  * token t is slot t % bs of block block_table_row[t / bs].
- *  kv_cache        device pool of params->dtype.
+ *  kv_cache        device pool of params->dtype (e4m3 codes when params->kv_dtype
+ *                  is PA_KV_FP8_E4M3).
  *  block_table_row device int32[ceil(seq_len / bs)].
- *  k_out, v_out    device [seq_len, Hkv, d] each.
- * Uses params->block_size, num_kv_heads, head_size, dtype.  The ids are not
+ *  k_out, v_out    device [seq_len, Hkv, d] each, the pool's element type.
+ * Uses params->block_size, num_kv_heads, head_size, dtype, kv_dtype.  The ids are not
  * checked on the device: they must be in [0, num_blocks).
  * Errors: INVALID_ARG (sizes, NULL pointers), UNSUPPORTED (dtype).
  */

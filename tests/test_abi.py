@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (pa_[a-z_]+)\b", nm))
+    exported = set(re.findall(r"\bT (pa_[a-z0-9_]+)\b", nm))
     assert set(declared_functions()) <= exported
 
 
@@ -74,3 +74,55 @@ def test_write_kv_validates_before_any_launch():
         with pytest.raises(pa.PagedAttnError) as ei:
             pa.pa_write_kv(key, value, slots, n, params, kv_cache=16, stream=0)
         assert ei.value.status == status, args
+
+
+def _fp8_params(**kw):
+    base = dict(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=8,
+                max_blocks_per_seq=4, dtype="bf16", scale=0.1, kv_dtype="fp8_e4m3")
+    base.update(kw)
+    return pa.make_params(**base)
+
+
+def test_e4m3_pool_plan_checks():
+    """An e4m3 pool is a plan property: bf16 queries only, a known kv_dtype, and
+    the general prefill tiling (the wide kernel reads bf16 pools only)."""
+    qsl, sl = [0, 1, 65], [40, 64]
+    # group of 8: the wide kernel takes 4 heads x 32 positions per workgroup,
+    # the general one 8 heads x 16 positions
+    plan = pa.pa_plan_create(_fp8_params(num_heads=16), qsl, sl, device=-1)
+    same = pa.pa_plan_create(_fp8_params(num_heads=16, kv_dtype="same"), qsl, sl, device=-1)
+    info, info_same = pa.pa_plan_get_info(plan), pa.pa_plan_get_info(same)
+    assert info["num_decodes"] == 1 and info["num_prefills"] == 1
+    assert (info["prefill_rows_per_item"], info_same["prefill_rows_per_item"]) == (16, 32)
+    for kw, status in ((dict(dtype="fp32"), pa.PA_ERR_UNSUPPORTED), (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG)):
+        with pytest.raises(pa.PagedAttnError) as ei:
+            pa.pa_plan_create(_fp8_params(**kw), qsl, sl, device=-1)
+        assert ei.value.status == status, kw
+
+
+def test_e4m3_write_validates_before_any_launch():
+    p = _fp8_params()
+    pa.pa_write_kv_fp8(None, None, None, 0, p, None, None, None, num_scales=1, stream=0)
+    for args, status in (
+        ((16, 16, 16, 3, p, 16, 16, 3), pa.PA_ERR_INVALID_ARG),                  # 3 scales for 2 heads
+        ((16, 16, 16, 3, p, None, 16, 1), pa.PA_ERR_INVALID_ARG),                # NULL scale
+        ((16, 8, 16, 3, p, 16, 16, 1), pa.PA_ERR_INVALID_ARG),                   # value not 16-byte aligned
+        ((16, 16, 16, 3, _fp8_params(kv_dtype="same"), 16, 16, 1), pa.PA_ERR_INVALID_ARG),  # not an e4m3 pool
+        ((16, 16, 16, 3, _fp8_params(dtype="fp32"), 16, 16, 1), pa.PA_ERR_UNSUPPORTED),    # fp32 inputs
+        ((16, 16, 16, 3, _fp8_params(head_size=8), 16, 16, 1), pa.PA_ERR_UNSUPPORTED),     # 8-element heads
+    ):
+        key, value, slots, n, params, ks, vs, ns = args
+        with pytest.raises(pa.PagedAttnError) as ei:
+            pa.pa_write_kv_fp8(key, value, slots, n, params, ks, vs, kv_cache=16, num_scales=ns, stream=0)
+        assert ei.value.status == status, args
+    # the plain write refuses an e4m3 pool
+    with pytest.raises(pa.PagedAttnError) as ei:
+        pa.pa_write_kv(16, 16, 16, 3, p, kv_cache=16, stream=0)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_e4m3_forward_needs_a_device_plan_and_scales():
+    plan = pa.pa_plan_create(_fp8_params(), [0, 1, 65], [40, 64], device=-1)
+    with pytest.raises(pa.PagedAttnError) as ei:
+        pa.pa_forward_fp8(plan, 16, 16, 16, 16, 16, 16, num_scales=2, stream=0)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG

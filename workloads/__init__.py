@@ -17,7 +17,13 @@ declares in «FlashAttention y FlashInfer», §Flujo de datos):
                    new query tokens
 
 bf16 arrays are stored as their raw 16-bit patterns (``np.uint16``) because numpy
-has no bfloat16 type; fp32 arrays are ``np.float32``.
+has no bfloat16 type; fp32 arrays are ``np.float32``.  An e4m3 pool
+(``kv_dtype="fp8_e4m3"``) holds 8-bit codes (``np.uint8``) drawn directly as
+random bit fields (sign uniform, exponent field uniform in 5..15, mantissa
+uniform, the NaN mantissa 7 of exponent 15 replaced by 6, so codes reach the
+largest value 448), with K and V scales drawn per KV head, uniform in
+[0.005, 0.007], so the largest value stands for about 3 and the RMS is about
+1.3, like the N(0, 1) values of the other pools; no value is quantised here.
 
 Draw order for one batch (each step uses its own child of ``SeedSequence(seed)``):
 lengths (drawn by the caller, see ``config_lengths``), page placement, Q, then K/V
@@ -69,6 +75,9 @@ class Batch:
     common_prefix_len: int = 0
     name: str = "custom"
     meta: dict = field(default_factory=dict)
+    kv_dtype: str = "same"          # "same" or "fp8_e4m3"
+    k_scale: np.ndarray | None = None  # e4m3 pool: float32 [num_kv_heads]
+    v_scale: np.ndarray | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -117,6 +126,7 @@ def make_batch(
     causal: bool = True,
     name: str = "custom",
     max_blocks_per_seq: int | None = None,
+    kv_dtype: str = "same",
 ) -> Batch:
     """Draw a batch for the given per-sequence query lengths and KV lengths.
 
@@ -127,6 +137,9 @@ def make_batch(
     """
     if dtype not in ("bf16", "fp32"):
         raise ValueError(f"dtype {dtype!r}")
+    if kv_dtype not in ("same", "fp8_e4m3") or (kv_dtype == "fp8_e4m3" and dtype != "bf16"):
+        raise ValueError(f"kv_dtype {kv_dtype!r} with dtype {dtype!r}")
+    f8 = kv_dtype == "fp8_e4m3"
     qlens = np.asarray(query_lens, dtype=np.int64)
     lens = np.asarray(seq_lens, dtype=np.int64)
     if qlens.shape != lens.shape:
@@ -173,7 +186,10 @@ def make_batch(
 
     # (4) K/V values, page by page in fixed chunks
     shape = (num_blocks, 2, bs, num_kv_heads, head_size)
-    if dtype == "bf16":
+    if f8:
+        pool = np.empty(shape, dtype=np.uint8)
+        fill = np.uint8(0x7F) if poison else np.uint8(0)
+    elif dtype == "bf16":
         pool = np.empty(shape, dtype=np.uint16)
         fill = BF16_NAN if poison else np.uint16(0)
     else:
@@ -185,6 +201,14 @@ def make_batch(
     def fill_chunk(ci: int) -> None:
         ids = used_ids[ci * _PAGE_CHUNK:(ci + 1) * _PAGE_CHUNK]
         g = np.random.Generator(np.random.PCG64(kids[ci]))
+        if f8:
+            fshape = (len(ids),) + shape[1:]
+            sign = g.integers(0, 2, size=fshape, dtype=np.uint8)
+            expo = g.integers(5, 16, size=fshape, dtype=np.uint8)
+            mant = g.integers(0, 8, size=fshape, dtype=np.uint8)
+            mant = np.where((expo == 15) & (mant == 7), np.uint8(6), mant)
+            pool[ids] = (sign << np.uint8(7)) | (expo << np.uint8(3)) | mant
+            return
         vals = g.standard_normal((len(ids),) + shape[1:], dtype=np.float32)
         pool[ids] = f32_to_bf16_bits(vals) if dtype == "bf16" else vals
 
@@ -202,6 +226,11 @@ def make_batch(
 
     qsl = np.zeros(B + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(qlens)
+    k_scale = v_scale = None
+    if f8:
+        rs = np.random.Generator(np.random.PCG64(ss.spawn(1)[0]))
+        k_scale = rs.uniform(0.005, 0.007, size=num_kv_heads).astype(np.float32)
+        v_scale = rs.uniform(0.005, 0.007, size=num_kv_heads).astype(np.float32)
     return Batch(
         num_heads=num_heads,
         num_kv_heads=num_kv_heads,
@@ -218,6 +247,9 @@ def make_batch(
         common_prefix_len=sp * bs,
         name=name,
         meta={"pad_block_id": pad_id, "total_pages": total_pages, "seed": seed},
+        kv_dtype=kv_dtype,
+        k_scale=k_scale,
+        v_scale=v_scale,
     )
 
 
@@ -268,8 +300,9 @@ def config_lengths(cfg: int, seed: int | None = None):
     raise ValueError(f"unknown configuration {cfg}")
 
 
-def config_batch(cfg: int, seed: int | None = None, poison: bool = True) -> Batch:
-    """Draw the full-size batch of configuration ``cfg`` (1..5)."""
+def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtype: str = "same") -> Batch:
+    """Draw the full-size batch of configuration ``cfg`` (1..5); ``kv_dtype``
+    "fp8_e4m3" gives the same lengths and placement over an e4m3 pool."""
     seed = cfg if seed is None else seed
     qlens, lens, sp = config_lengths(cfg, seed)
     shape = CONFIG_SHAPES[cfg]
@@ -279,5 +312,5 @@ def config_batch(cfg: int, seed: int | None = None, poison: bool = True) -> Batc
         kw["scale"] = 1.0 / 8.0
     return make_batch(
         qlens, lens, seed=seed, shared_prefix_blocks=sp, poison=poison,
-        name=CONFIG_NAMES[cfg], **shape, **kw,
+        name=CONFIG_NAMES[cfg], kv_dtype=kv_dtype, **shape, **kw,
     )
