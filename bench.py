@@ -9,7 +9,9 @@ uniformly from [512, 8192], 32 query / 8 KV heads, head size 128, block size 16,
 bf16 (the decode half of the metric); the line also carries a secondary
 measurement of the causal varlen prefill workload (16 prompts of 512..4096
 tokens, same heads) for the prefill half of the metric.  Other workloads:
-``--workload prefill | mixed | cascade | tiny``.
+``--workload prefill | mixed | cascade | tiny | decode_e4m3 | kvwrite``
+(decode_e4m3: the decode batch over a pool of 8-bit e4m3 codes with per-head
+K/V scales; its algorithmic bytes count one byte per element).
 
 Prints ONE JSON line.  Algorithmic work counts each KV byte once per KV head
 (decode) and 4*H*d FLOPs per visible (query, key) pair (prefill); masked and
@@ -44,7 +46,9 @@ WORKLOADS = {
     "mixed": 4,
     "cascade": 5,
     "tiny": 1,
+    "decode_e4m3": 2,
 }
+KV_DTYPES = {"decode_e4m3": "fp8_e4m3"}
 DESCRIPTIONS = {
     1: "tiny mixed: 4 seqs, seq_lens 17/33/64/100, query_lens 1/1/16/100; 4 q / 2 kv heads, d=64, bs=16, fp32",
     2: "decode-only: 256 seqs, q=1, ctx U[512,8192]; 32 q / 8 kv heads, d=128, bs=16, bf16, random page placement",
@@ -109,7 +113,8 @@ def _batch_to_device(batch, common_prefix_len=None, kv_split_tokens=0):
     return pa.to_device(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc, batch.seq_lens,
                         num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
                         block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, causal=batch.causal,
-                        common_prefix_len=cp, kv_split_tokens=kv_split_tokens, device="cuda:0")
+                        common_prefix_len=cp, kv_split_tokens=kv_split_tokens, device="cuda:0",
+                        kv_dtype=batch.kv_dtype, k_scale=batch.k_scale, v_scale=batch.v_scale)
 
 
 def time_steps(db, steps: int, warmup: int) -> dict:
@@ -171,14 +176,17 @@ def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
     ql = np.diff(qsl).astype(np.int64)
     done_bytes = done_flops = 0
     seqs = 0
-    row_bytes = 2 * batch.num_kv_heads * batch.head_size * (2 if batch.dtype == "bf16" else 4)
+    elem = 1 if batch.kv_dtype == "fp8_e4m3" else (2 if batch.dtype == "bf16" else 4)
+    row_bytes = 2 * batch.num_kv_heads * batch.head_size * elem
     t_total = 0.0
     with threadpool_limits(limits=1):
         for b in order:
             rows = np.arange(qsl[b], qsl[b + 1])
             t0 = time.perf_counter()
             oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, qsl, batch.seq_lens, batch.scale,
-                                  rows, dtype=batch.dtype, causal=batch.causal)
+                                  rows, dtype=batch.dtype, causal=batch.causal, kv_dtype=batch.kv_dtype,
+                                  k_scale=1.0 if batch.k_scale is None else batch.k_scale,
+                                  v_scale=1.0 if batch.v_scale is None else batch.v_scale)
             t_total += time.perf_counter() - t0
             seqs += 1
             if ql[b] == 1:
@@ -199,12 +207,12 @@ def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
 
 # ---------------------------------------------------------------------------
 
-def measure(cfg: int, steps: int, warmup: int, seed=None) -> dict:
+def measure(cfg: int, steps: int, warmup: int, seed=None, kv_dtype: str = "same") -> dict:
     """Generate the workload, time it, and return the measurement record."""
     import attention_paged_kv_varlen_amd as pa
     from workloads import config_batch
-    batch = config_batch(cfg, seed=seed)
-    s = 2 if batch.dtype == "bf16" else 4
+    batch = config_batch(cfg, seed=seed, kv_dtype=kv_dtype)
+    s = 1 if kv_dtype == "fp8_e4m3" else (2 if batch.dtype == "bf16" else 4)
     counts = algorithmic_counts(batch.query_lens, batch.seq_lens, num_heads=batch.num_heads,
                                 num_kv_heads=batch.num_kv_heads, head_size=batch.head_size, elem_bytes=s,
                                 common_prefix_len=batch.common_prefix_len, causal=batch.causal)
@@ -229,7 +237,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
     run, and write them to profiles/traffic_counters.json."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_dispatch(path, counter):
         vals = {}
         for row in csv.DictReader(open(path)):
             if row["Counter_Name"] != counter:
@@ -239,30 +247,40 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
         out = {}
         for (name, _), v in vals.items():
             out.setdefault(name, []).append(v)
-        return {k: sum(v) / len(v) for k, v in out.items()}
+        return out
 
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
-    copy_f = [v for k, v in fetch.items() if "copy" in k.lower()]
-    copy_w = [v for k, v in write.items() if "copy" in k.lower()]
+    fd = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wd = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch = {k: sum(v) / len(v) for k, v in fd.items()}
+    write = {k: sum(v) / len(v) for k, v in wd.items()}
+    # the calibration copy is the largest copy dispatch (small host uploads use
+    # the same copy kernel)
+    copy_f = [x for k, v in fd.items() if "copy" in k.lower() for x in v]
+    copy_w = [x for k, v in wd.items() if "copy" in k.lower() for x in v]
     f_scale = copy_bytes / (max(copy_f) * 1024.0)
     w_scale = copy_bytes / (max(copy_w) * 1024.0)
     with open(KERNEL_SRC, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    res = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-                            "command": command}}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            res = json.load(f)
+    except (OSError, ValueError):
+        res = {}
+    calib = {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
+    res["_calibration"] = calib
     for name in fetch:
         fam = next((k for k in kernels if k in name), None)
         if fam is None or name not in write:
             continue
         family = {"decode_kernel": "decode", "prefill_wide_kernel": "prefill", "merge_kernel": "merge"}[fam]
-        tag = "bf16_d128" if "unsigned short, 128" in name or "prefill_wide" in name else None
+        tag = ("bf16_e4m3_d128" if "unsigned char, 128" in name else
+               "bf16_d128" if "unsigned short, 128" in name or "prefill_wide" in name else None)
         if tag is None:
             continue
         fb = fetch[name] * 1024.0 * f_scale
         wb = write[name] * 1024.0 * w_scale
         res[f"{family}_{tag}"] = {"kernel": name, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                                  "bytes_per_launch": fb + wb, "kernel_source_sha256": sha}
+                                  "bytes_per_launch": fb + wb, "kernel_source_sha256": sha, "calibration": calib}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     return res
@@ -348,10 +366,12 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-command", default="", help="command recorded with --summarize-pmc")
+    ap.add_argument("--pmc-kernels", default="decode_kernel,prefill_wide_kernel,merge_kernel",
+                    help="kernel families --summarize-pmc records (comma-separated)")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         res = summarize_pmc(*args.summarize_pmc, copy_bytes=args.copy_calibration_mib << 20,
-                            command=args.pmc_command)
+                            command=args.pmc_command, kernels=tuple(args.pmc_kernels.split(",")))
         print(json.dumps(res, indent=1))
         return 0
     if args.gpus != 1:
@@ -375,7 +395,8 @@ def main(argv=None) -> int:
         print(json.dumps(kvwrite_line(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return 0
     cfg = WORKLOADS[args.workload]
-    m = measure(cfg, args.steps, args.warmup)
+    kv_dtype = KV_DTYPES.get(args.workload, "same")
+    m = measure(cfg, args.steps, args.warmup, kv_dtype=kv_dtype)
     batch, counts, t = m["batch"], m["counts"], m["timing"]
     ms = t["ms_per_step"]
     dtype = batch.dtype
@@ -390,7 +411,9 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V, random page placement)",
-        "config": {"workload": DESCRIPTIONS[cfg], "num_seqs": batch.num_seqs, "num_tokens": batch.num_tokens,
+        "config": {"workload": DESCRIPTIONS[cfg] if kv_dtype == "same" else
+                   DESCRIPTIONS[cfg].replace("bf16,", "bf16 queries, e4m3 KV pool (per-head K/V scales),"),
+                   "num_seqs": batch.num_seqs, "num_tokens": batch.num_tokens,
                    "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
                    "head_size": batch.head_size, "block_size": batch.block_size,
                    "common_prefix_len": batch.common_prefix_len, "seed": cfg,
@@ -441,7 +464,10 @@ def main(argv=None) -> int:
     line["algorithmic"] = {k: counts[k] for k in ("decode_bytes", "prefill_flops", "decode_kv_tokens",
                                                   "prefill_tokens")}
 
-    if cfg == 2 and not args.no_secondary:
+    if kv_dtype != "same":
+        line["config"]["kv_dtype"] = kv_dtype
+        line["data"] = "synthetic (seeded N(0,1) Q; random e4m3 codes and per-head scales; random page placement)"
+    if args.workload == "decode" and not args.no_secondary:
         del m
         p = measure(3, max(10, args.steps // 4), max(2, args.warmup // 2))
         kp, k = _kernel(p["timing"], "prefill_")
