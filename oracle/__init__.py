@@ -48,6 +48,7 @@ from .attention import (  # noqa: F401
     to_f64,
     write_kv,
 )
+from .layout import kv_cache_stride_order, logical_pool  # noqa: F401
 from .fp8 import (  # noqa: F401
     dequantize_pool,
     e4m3_decode,

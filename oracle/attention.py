@@ -25,6 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 from .fp8 import e4m3_decode, scales_per_head
+from .layout import kv_cache_stride_order, logical_pool  # noqa: F401
 
 
 # ---------------------------------------------------------------------------
@@ -119,15 +120,17 @@ def metadata(query_start_loc, seq_lens, common_prefix_len: int = 0,
 # Gather
 # ---------------------------------------------------------------------------
 
-def gather(kv_cache: np.ndarray, block_table_row, seq_len: int):
+def gather(kv_cache: np.ndarray, block_table_row, seq_len: int, kv_layout: str = "NHD"):
     """Contiguous K and V of one sequence, ``[seq_len, Hkv, d]`` each, same dtype.
 
     «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
     the kernel is handed the block table and gathers over the physical blocks.
     Token ``t`` lives in block ``block_table_row[t // bs]`` at slot ``t % bs``;
     slot 0 of the pool's second dimension holds K and slot 1 holds V
-    («FlashAttention y FlashInfer», §Flujo de datos).
+    («FlashAttention y FlashInfer», §Flujo de datos).  ``kv_layout`` is the
+    pool's memory order (:func:`oracle.layout.kv_cache_stride_order`).
     """
+    kv_cache = logical_pool(kv_cache, kv_layout)
     bs = kv_cache.shape[2]
     t = np.arange(int(seq_len))
     blocks = np.asarray(block_table_row, dtype=np.int64)[t // bs]
@@ -162,19 +165,21 @@ def slot_mapping(query_start_loc, seq_lens, block_table, block_size: int):
     return out
 
 
-def write_kv(kv_cache: np.ndarray, key: np.ndarray, value: np.ndarray, slots):
+def write_kv(kv_cache: np.ndarray, key: np.ndarray, value: np.ndarray, slots, kv_layout: str = "NHD"):
     """A copy of the pool with token ``t``'s K row ``key[t]`` (``[Hkv, d]``) at slot
     ``slots[t]`` of the K half and its V row in the V half; a negative slot skips
-    the token.  Slot ``s`` is block ``s // bs``, offset ``s % bs``.
+    the token.  Slot ``s`` is block ``s // bs``, offset ``s % bs``.  The copy keeps
+    the pool's memory order ``kv_layout``.
     """
-    pool = np.array(kv_cache, copy=True)
+    out = np.array(kv_cache, copy=True)
+    pool = logical_pool(out, kv_layout)             # a view: writes land in `out`
     bs = pool.shape[2]
     for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if s < 0:
             continue
         pool[s // bs, 0, s % bs] = key[t]
         pool[s // bs, 1, s % bs] = value[t]
-    return pool
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -227,12 +232,14 @@ def _kv_values(K, V, dtype: str, kv_dtype, k_scale, v_scale):
 
 
 def attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale, rows,
-                   *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0):
+                   *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+                   kv_layout: str = "NHD"):
     """Output and log-sum-exp of the chosen token rows only (any order).
 
     Same definition as :func:`attention`; used where the whole batch is too large
     for the CPU.  Returns ``out [len(rows), H, d]`` and ``lse [len(rows), H]``.
     """
+    kv_cache = logical_pool(kv_cache, kv_layout)
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     L = np.asarray(seq_lens, dtype=np.int64)
     H, Hkv, g = _dims(q, kv_cache)
@@ -264,7 +271,8 @@ def attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale, r
 
 
 def attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
-              *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0):
+              *, dtype: str = "bf16", causal: bool = True, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+              kv_layout: str = "NHD"):
     """Exact attention for every token row of a mixed varlen batch.
 
     For row ``r = query_start_loc[b] + i``, head ``h`` and KV head ``h // g``, the
@@ -278,7 +286,8 @@ def attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
 
     With ``kv_dtype="fp8_e4m3"`` the pool holds e4m3 codes and the keys and
     values are ``decode(code) * k_scale`` and ``decode(code) * v_scale`` (one scale,
-    or one per KV head); queries keep ``dtype``.
+    or one per KV head); queries keep ``dtype``.  ``kv_layout`` is the pool's
+    memory order (NHD or HND).
 
     Returns ``out [T, H, d]`` and ``lse [T, H]`` in float64, rows in the
     caller's order.
@@ -286,7 +295,7 @@ def attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
     T = int(np.asarray(query_start_loc)[-1])
     return attention_rows(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
                           np.arange(T), dtype=dtype, causal=causal, kv_dtype=kv_dtype,
-                          k_scale=k_scale, v_scale=v_scale)
+                          k_scale=k_scale, v_scale=v_scale, kv_layout=kv_layout)
 
 
 def merge_states(o1, lse1, o2, lse2):
@@ -315,7 +324,7 @@ def merge_states(o1, lse1, o2, lse2):
 
 def cascade_attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale,
                       common_prefix_len: int, *, dtype: str = "bf16", causal: bool = True,
-                      kv_dtype=None, k_scale=1.0, v_scale=1.0):
+                      kv_dtype=None, k_scale=1.0, v_scale=1.0, kv_layout: str = "NHD"):
     """Cascade form: shared prefix once, each sequence's own suffix, merged by LSE.
 
     «El especialista del plato estrella», §Qué aporta FlashInfer: when the batch
@@ -326,6 +335,7 @@ def cascade_attention(q, kv_cache, block_table, query_start_loc, seq_lens, scale
     Returns the same ``out, lse`` as :func:`attention`.
     """
     P = int(common_prefix_len)
+    kv_cache = logical_pool(kv_cache, kv_layout)
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     L = np.asarray(seq_lens, dtype=np.int64)
     bs = kv_cache.shape[2]

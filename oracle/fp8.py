@@ -25,6 +25,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .layout import logical_pool
+
 E4M3_MAX = 448.0
 
 
@@ -89,26 +91,28 @@ def scales_per_head(scale, num_kv_heads: int) -> np.ndarray:
     return s
 
 
-def dequantize_pool(kv_cache, k_scale, v_scale) -> np.ndarray:
-    """float64 pool ``(num_blocks, 2, bs, Hkv, d)`` of an e4m3 pool: K entries are
+def dequantize_pool(kv_cache, k_scale, v_scale, kv_layout: str = "NHD") -> np.ndarray:
+    """float64 pool of an e4m3 pool, same shape and memory order: K entries are
     ``decode(code) * k_scale[kvh]`` and V entries ``decode(code) * v_scale[kvh]``."""
     pool = np.asarray(kv_cache, dtype=np.uint8)
-    Hkv = pool.shape[3]
+    out = e4m3_decode(pool)
+    lv = logical_pool(out, kv_layout)               # a view of `out`
+    Hkv = lv.shape[3]
     ks = scales_per_head(k_scale, Hkv)
     vs = scales_per_head(v_scale, Hkv)
-    out = e4m3_decode(pool)
-    out[:, 0] *= ks[None, None, :, None]
-    out[:, 1] *= vs[None, None, :, None]
+    lv[:, 0] *= ks[None, None, :, None]
+    lv[:, 1] *= vs[None, None, :, None]
     return out
 
 
-def write_kv_fp8(kv_cache, key, value, slots, k_scale, v_scale):
+def write_kv_fp8(kv_cache, key, value, slots, k_scale, v_scale, kv_layout: str = "NHD"):
     """A copy of an e4m3 pool with token ``t``'s K and V rows quantised with the
     K / V scale of each KV head and stored at slot ``slots[t]`` (block ``s // bs``,
     offset ``s % bs``); a negative slot skips the token.  ``key`` and ``value``
     are ``[T, Hkv, d]`` arrays of values (not bit patterns) that float32 holds
     exactly, e.g. the values of bf16 inputs."""
-    pool = np.array(kv_cache, dtype=np.uint8, copy=True)
+    out = np.array(kv_cache, dtype=np.uint8, copy=True)
+    pool = logical_pool(out, kv_layout)             # a view: writes land in `out`
     bs, Hkv = pool.shape[2], pool.shape[3]
     ks = scales_per_head(k_scale, Hkv)
     vs = scales_per_head(v_scale, Hkv)
@@ -118,4 +122,4 @@ def write_kv_fp8(kv_cache, key, value, slots, k_scale, v_scale):
         for h in range(Hkv):
             pool[s // bs, 0, s % bs, h] = quantize(key[t, h], ks[h])
             pool[s // bs, 1, s % bs, h] = quantize(value[t, h], vs[h])
-    return pool
+    return out

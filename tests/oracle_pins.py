@@ -595,6 +595,98 @@ def check_write_kv_fp8(O):
     assert (one[sl // 16, 0, sl % 16] == 0x3C).all() and (one[sl // 16, 1, sl % 16] == 0xBC).all()
 
 
+# ---------------------------------------------------------------------------
+# Pool memory order (NHD / HND) and large pages
+# ---------------------------------------------------------------------------
+
+def _flat_pool(logical, layout):
+    """Physical pool for a logical (blocks, 2, bs, Hkv, d) array, written element
+    by element at its flat offset: NHD ((blk*2 + kv)*bs + slot)*Hkv*d + h*d + e,
+    HND ((blk*2 + kv)*Hkv + h)*bs*d + slot*d + e."""
+    nb, _, bs, Hkv, d = logical.shape
+    flat = np.empty(logical.size, dtype=logical.dtype)
+    for blk in range(nb):
+        for kv in range(2):
+            for slot in range(bs):
+                for h in range(Hkv):
+                    if layout == "NHD":
+                        off = ((blk * 2 + kv) * bs + slot) * Hkv * d + h * d
+                    else:
+                        off = ((blk * 2 + kv) * Hkv + h) * bs * d + slot * d
+                    flat[off:off + d] = logical[blk, kv, slot, h]
+    shape = (nb, 2, bs, Hkv, d) if layout == "NHD" else (nb, 2, Hkv, bs, d)
+    return flat.reshape(shape)
+
+
+def check_layout_gather(O):
+    # «FlashAttention y FlashInfer», §Motivación de diseño: NHD keeps the
+    # logical order, HND puts the KV head before the slot.
+    assert tuple(O.kv_cache_stride_order("NHD")) == (0, 1, 2, 3, 4)
+    assert tuple(O.kv_cache_stride_order("HND")) == (0, 1, 3, 2, 4)
+    for bs, lens in ((16, [1, 15, 17, 40]), (128, [130, 5, 256])):
+        Ks, Vs = _random_logical(lens, 3, 4, seed=100 + bs)
+        pool, bt = pool_from_logical(Ks, Vs, bs, seed=101 + bs)
+        for layout in ("NHD", "HND"):
+            phys = _flat_pool(pool, layout)
+            for b, L in enumerate(lens):
+                K, V = O.gather(phys, bt[b], L, kv_layout=layout)
+                assert np.array_equal(K, Ks[b]) and np.array_equal(V, Vs[b])
+
+
+def check_layout_attention_and_large_pages(O):
+    # The memory order changes nothing in the result; pages of 128 .. 1024
+    # tokens (the large pages of «FlashAttention y FlashInfer», §Motivación de
+    # diseño) give the same attention as 16-token pages of the same values.
+    lens, qlens = [300, 1025, 64, 700], [1, 1, 64, 30]
+    Ks, Vs = _random_logical(lens, 2, 8, seed=110)
+    rng = np.random.default_rng(111)
+    q = rng.standard_normal((sum(qlens), 4, 8)).astype(np.float32)
+    ref = None
+    for bs in (16, 128, 1024):
+        pool, bt = pool_from_logical(Ks, Vs, bs, seed=112 + bs)
+        for layout in ("NHD", "HND"):
+            phys = _flat_pool(pool, layout)
+            got = O.attention(q, phys, bt, _qsl(qlens), np.array(lens), 0.3, dtype="fp32", kv_layout=layout)
+            if ref is None:
+                ref = got
+            assert np.abs(got[0] - ref[0]).max() < 1e-12 and np.abs(got[1] - ref[1]).max() < 1e-12
+    # cascade over an HND pool with 128-token pages
+    P = 256
+    cl = [P + 3, P + 100, P + 129]
+    Kc, Vc = _random_logical(cl, 2, 8, seed=113)
+    poolc, btc = pool_from_logical(Kc, Vc, 128, seed=114, shared_prefix_blocks=P // 128)
+    physc = _flat_pool(poolc, "HND")
+    qc = rng.standard_normal((3, 4, 8)).astype(np.float32)
+    full = O.attention(qc, physc, btc, _qsl([1, 1, 1]), np.array(cl), 0.3, dtype="fp32", kv_layout="HND")
+    casc = O.cascade_attention(qc, physc, btc, _qsl([1, 1, 1]), np.array(cl), 0.3, P, dtype="fp32",
+                               kv_layout="HND")
+    assert np.abs(full[0] - casc[0]).max() < 1e-12 and np.abs(full[1] - casc[1]).max() < 1e-12
+
+
+def check_layout_writes(O):
+    # Writes into an HND pool land where the flat HND offsets say: the HND
+    # result is the flat-offset image of the NHD result (bf16-like float and
+    # e4m3 writes alike).
+    lens, qlens = [17, 40], [1, 8]
+    Ks, Vs = _random_logical(lens, 2, 8, seed=120)
+    pool, bt = pool_from_logical(Ks, Vs, 16, seed=121)
+    slots = O.slot_mapping(_qsl(qlens), lens, bt, 16)
+    rng = np.random.default_rng(122)
+    T = sum(qlens)
+    nk = rng.standard_normal((T, 2, 8)).astype(np.float32)
+    nv = rng.standard_normal((T, 2, 8)).astype(np.float32)
+    nhd = O.write_kv(pool, nk, nv, slots)
+    hnd = O.write_kv(_flat_pool(pool, "HND"), nk, nv, slots, kv_layout="HND")
+    assert np.array_equal(hnd, _flat_pool(nhd, "HND"), equal_nan=True)
+    codes = np.where(np.isnan(pool), 0x7F, np.abs(pool * 10) % 120).astype(np.uint8)
+    ks, vs = np.array([0.5, 2.0], np.float32), np.array([0.25, 1.0], np.float32)
+    nhd8 = O.write_kv_fp8(codes, nk, nv, slots, ks, vs)
+    hnd8 = O.write_kv_fp8(_flat_pool(codes, "HND"), nk, nv, slots, ks, vs, kv_layout="HND")
+    assert np.array_equal(hnd8, _flat_pool(nhd8, "HND"))
+    deq = O.dequantize_pool(_flat_pool(codes, "HND"), ks, vs, kv_layout="HND")
+    assert np.array_equal(deq, _flat_pool(O.dequantize_pool(codes, ks, vs), "HND"), equal_nan=True)
+
+
 ALL_CHECKS = [
     check_kv_cache_shape,
     check_gather_roundtrip,
@@ -619,6 +711,9 @@ ALL_CHECKS = [
     check_quantize_divides_in_float32,
     check_fp8_attention_reduces_to_fp32,
     check_write_kv_fp8,
+    check_layout_gather,
+    check_layout_attention_and_large_pages,
+    check_layout_writes,
     check_write_kv_fills_pages,
     check_write_kv_chunks_follow_context,
 ]

@@ -14,7 +14,10 @@ from tests import oracle_pins
 ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 SRC = os.path.join(ORACLE_DIR, "attention.py")
 SRC_FP8 = os.path.join(ORACLE_DIR, "fp8.py")
+SRC_LAYOUT = os.path.join(ORACLE_DIR, "layout.py")
 FP8_IMPORT = "from .fp8 import e4m3_decode, scales_per_head\n"
+LAYOUT_IMPORT_ATT = "from .layout import kv_cache_stride_order, logical_pool  # noqa: F401\n"
+LAYOUT_IMPORT_FP8 = "from .layout import logical_pool\n"
 
 MUTANTS = {
     "causal_off_by_one": ("visible = t[None, :] <= (cb + i)[:, None]\n        else:\n            visible = np.ones((len(i), Lb)",
@@ -68,10 +71,12 @@ MUTANTS_FP8 = {
                             "y = np.asarray(x, dtype=np.float64) / float(scale)\n    return e4m3_encode(y)"),
     "quantize_multiplies": ("/ np.float32(scale)", "* np.float32(scale)"),
     "per_tensor_scale_ignored": ("return np.full(num_kv_heads, s[0])", "return np.full(num_kv_heads, 1.0)"),
-    "dequantize_scales_swapped": ("out[:, 0] *= ks[None, None, :, None]\n    out[:, 1] *= vs[None, None, :, None]",
-                                  "out[:, 0] *= vs[None, None, :, None]\n    out[:, 1] *= ks[None, None, :, None]"),
+    "dequantize_scales_swapped": ("lv[:, 0] *= ks[None, None, :, None]\n    lv[:, 1] *= vs[None, None, :, None]",
+                                  "lv[:, 0] *= vs[None, None, :, None]\n    lv[:, 1] *= ks[None, None, :, None]"),
     "write_fp8_v_with_k_scale": ("quantize(value[t, h], vs[h])", "quantize(value[t, h], ks[h])"),
     "write_fp8_no_skip": ("        if s < 0:\n            continue\n        for h", "        for h"),
+    "write_fp8_on_physical_array": ("    pool = logical_pool(out, kv_layout)             # a view: writes land in `out`\n    bs, Hkv",
+                                    "    pool = out\n    bs, Hkv"),
 }
 MUTANTS_ATT_FP8 = {
     "attention_kv_scales_swapped": ("e4m3_decode(K) * ks[None, :, None], e4m3_decode(V) * vs[None, :, None]",
@@ -81,19 +86,29 @@ MUTANTS_ATT_FP8 = {
 MUTANTS.update(MUTANTS_ATT_FP8)
 
 
-def _load(src: str, fp8_src: str | None = None):
+def _load(src: str, fp8_src: str | None = None, layout_src: str | None = None):
     """The attention module from ``src`` with the e4m3 helpers of ``fp8_src``
-    (the real module's source unless given) in its namespace; the combined
-    namespace also exposes the e4m3 functions the pins call."""
+    and the memory-order helpers of ``layout_src`` (the real modules' sources
+    unless given) in its namespace; the combined namespace also exposes the
+    functions of those modules that the pins call."""
     if fp8_src is None:
         with open(SRC_FP8) as f:
             fp8_src = f.read()
+    if layout_src is None:
+        with open(SRC_LAYOUT) as f:
+            layout_src = f.read()
+    ml = types.ModuleType("oracle_layout_mutant")
+    exec(compile(layout_src, "oracle_layout_mutant", "exec"), ml.__dict__)
+    shared = {k: v for k, v in ml.__dict__.items() if not k.startswith("__")}
     m8 = types.ModuleType("oracle_fp8_mutant")
-    exec(compile(fp8_src, "oracle_fp8_mutant", "exec"), m8.__dict__)
+    m8.__dict__.update(shared)
+    assert fp8_src.count(LAYOUT_IMPORT_FP8) == 1
+    exec(compile(fp8_src.replace(LAYOUT_IMPORT_FP8, ""), "oracle_fp8_mutant", "exec"), m8.__dict__)
     mod = types.ModuleType("oracle_mutant")
     mod.__dict__.update({k: v for k, v in m8.__dict__.items() if not k.startswith("__")})
-    assert src.count(FP8_IMPORT) == 1
-    exec(compile(src.replace(FP8_IMPORT, ""), "oracle_mutant", "exec"), mod.__dict__)
+    assert src.count(FP8_IMPORT) == 1 and src.count(LAYOUT_IMPORT_ATT) == 1
+    exec(compile(src.replace(FP8_IMPORT, "").replace(LAYOUT_IMPORT_ATT, ""), "oracle_mutant", "exec"),
+         mod.__dict__)
     return mod
 
 
@@ -112,6 +127,29 @@ def _caught(mod):
         except Exception:  # any failure (assertion or crash) counts as caught
             failed.append(check.__name__)
     return failed
+
+
+MUTANTS_LAYOUT = {
+    "hnd_is_nhd": ("        return (0, 1, 3, 2, 4)", "        return (0, 1, 2, 3, 4)"),
+    "hnd_head_last": ("        return (0, 1, 3, 2, 4)", "        return (0, 1, 2, 4, 3)"),
+}
+MUTANTS.update({
+    "gather_ignores_layout": ("    kv_cache = logical_pool(kv_cache, kv_layout)\n    bs = kv_cache.shape[2]\n    t = np.arange",
+                              "    bs = kv_cache.shape[2]\n    t = np.arange"),
+    "write_kv_on_physical_array": ("    pool = logical_pool(out, kv_layout)             # a view: writes land in `out`\n    bs = pool.shape[2]\n    for t, s in",
+                                   "    pool = out\n    bs = pool.shape[2]\n    for t, s in"),
+})
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_LAYOUT))
+def test_layout_mutant_is_caught(name):
+    old, new = MUTANTS_LAYOUT[name]
+    with open(SRC_LAYOUT) as f:
+        srcl = f.read()
+    assert srcl.count(old) >= 1, f"mutation site for {name} not found"
+    with open(SRC) as f:
+        mod = _load(f.read(), layout_src=srcl.replace(old, new, 1))
+    assert _caught(mod), f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS_FP8))
