@@ -25,6 +25,8 @@ from ._capi import (  # noqa: F401
     PA_ERR_UNSUPPORTED,
     PA_FP32,
     PA_KV_FP8_E4M3,
+    PA_KV_HND,
+    PA_KV_NHD,
     PA_KV_SAME,
     PA_OK,
     PagedAttnError,
@@ -35,6 +37,7 @@ from ._capi import (  # noqa: F401
     pa_forward_fp8,
     pa_gather_kv,
     pa_kv_cache_shape,
+    pa_kv_cache_stride_order,
     pa_last_error,
     pa_merge_states,
     pa_params,

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_OOM = range(5)
 PA_BF16, PA_FP32 = 0, 1
 PA_KV_SAME, PA_KV_FP8_E4M3 = 0, 1
+PA_KV_NHD, PA_KV_HND = 0, 1
 (PA_ARRAY_ORDER, PA_ARRAY_IS_DECODE, PA_ARRAY_PREFIX_BLOCKS, PA_ARRAY_ROW_PARTIALS, PA_ARRAY_DECODE_LISTS,
  PA_ARRAY_DECODE_SPANS) = range(6)
 
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
-    "pa_kv_cache_shape", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
+    "pa_kv_cache_shape", "pa_kv_cache_stride_order", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
     "pa_plan_workspace_bytes", "pa_forward", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
     "pa_write_kv_fp8", "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start",
     "pa_profile_stop",
@@ -36,7 +37,7 @@ class pa_params(ctypes.Structure):
         ("head_size", c_int32), ("block_size", c_int32), ("num_blocks", c_int32),
         ("max_blocks_per_seq", c_int32), ("dtype", c_int32), ("causal", c_int32),
         ("common_prefix_len", c_int32), ("kv_split_tokens", c_int32), ("scale", c_float),
-        ("kv_dtype", c_int32),
+        ("kv_dtype", c_int32), ("kv_layout", c_int32),
     ]
 
 
@@ -76,6 +77,7 @@ def lib():
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_paged_kv_varlen_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     L.pa_kv_cache_shape.argtypes = [c_int64, c_int32, c_int32, c_int32, POINTER(c_int64)]
+    L.pa_kv_cache_stride_order.argtypes = [c_int32, POINTER(c_int32)]
     L.pa_plan_create.argtypes = [POINTER(pa_params), POINTER(c_int32), POINTER(c_int32), POINTER(c_int32),
                                  c_int, POINTER(c_void_p)]
     L.pa_plan_get_info.argtypes = [c_void_p, POINTER(pa_plan_info)]
@@ -154,12 +156,14 @@ class Plan:
 
 
 def make_params(*, num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq,
-                dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0, kv_dtype="same") -> pa_params:
+                dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0, kv_dtype="same",
+                kv_layout="NHD") -> pa_params:
     dt = {"bf16": PA_BF16, "fp32": PA_FP32}.get(dtype, dtype)
     kvt = {"same": PA_KV_SAME, None: PA_KV_SAME, "fp8_e4m3": PA_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
+    lay = {"NHD": PA_KV_NHD, "HND": PA_KV_HND}.get(kv_layout, kv_layout)
     return pa_params(int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size), int(block_size),
                      int(num_blocks), int(max_blocks_per_seq), int(dt), int(bool(causal)),
-                     int(common_prefix_len), int(kv_split_tokens), float(scale), int(kvt))
+                     int(common_prefix_len), int(kv_split_tokens), float(scale), int(kvt), int(lay))
 
 
 # ---------------------------------------------------------------------------
@@ -169,6 +173,13 @@ def make_params(*, num_seqs, num_heads, num_kv_heads, head_size, block_size, num
 def pa_kv_cache_shape(num_blocks: int, block_size: int, num_kv_heads: int, head_size: int) -> tuple:
     out = (c_int64 * 5)()
     _check(lib().pa_kv_cache_shape(num_blocks, block_size, num_kv_heads, head_size, out))
+    return tuple(int(x) for x in out)
+
+
+def pa_kv_cache_stride_order(layout) -> tuple:
+    lay = {"NHD": PA_KV_NHD, "HND": PA_KV_HND}.get(layout, layout)
+    out = (c_int32 * 5)()
+    _check(lib().pa_kv_cache_stride_order(int(lay), out))
     return tuple(int(x) for x in out)
 
 

@@ -115,6 +115,15 @@ pa_status pa_kv_cache_shape(int64_t num_blocks, int32_t block_size, int32_t num_
   return PA_OK;
 }
 
+pa_status pa_kv_cache_stride_order(int32_t layout, int32_t order_out[5]) {
+  g_err.clear();
+  if (!order_out) return set_err(PA_ERR_INVALID_ARG, "order_out is NULL");
+  if (layout != PA_KV_NHD && layout != PA_KV_HND) return set_err(PA_ERR_INVALID_ARG, "unknown layout");
+  const int32_t nhd[5] = {0, 1, 2, 3, 4}, hnd[5] = {0, 1, 3, 2, 4};
+  for (int i = 0; i < 5; ++i) order_out[i] = layout == PA_KV_HND ? hnd[i] : nhd[i];
+  return PA_OK;
+}
+
 pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc, const int32_t* seq_lens,
                          const int32_t* block_table, int device, pa_plan** plan_out) {
   g_err.clear();
@@ -282,6 +291,7 @@ static pa_status forward_common(const pa_plan* plan, const void* q, const void* 
   g.max_blocks = p.max_blocks_per_seq;
   g.dtype = p.dtype;
   g.kv_dtype = p.kv_dtype;
+  pa::pool_strides(p.kv_layout, p.block_size, p.num_kv_heads, p.head_size, g.slot_stride, g.head_stride);
   g.scale_log2 = (float)((double)p.scale * 1.4426950408889634);
   g.ps = hp.ps;
 
@@ -364,13 +374,19 @@ pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int
   if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
   if (params->kv_dtype != PA_KV_SAME && params->kv_dtype != PA_KV_FP8_E4M3)
     return set_err(PA_ERR_INVALID_ARG, "kv_dtype must be PA_KV_SAME or PA_KV_FP8_E4M3");
+  if (params->kv_layout != PA_KV_NHD && params->kv_layout != PA_KV_HND)
+    return set_err(PA_ERR_INVALID_ARG, "kv_layout must be PA_KV_NHD or PA_KV_HND");
   const int elem = params->kv_dtype == PA_KV_FP8_E4M3 ? 1 : params->dtype == PA_BF16 ? 2 : 4;
-  if ((int64_t)params->num_kv_heads * params->head_size * elem % 16 != 0)
-    return set_err(PA_ERR_UNSUPPORTED, "a K row (num_kv_heads * head_size elements) must be a multiple of 16 bytes");
+  if ((int64_t)params->head_size * elem % 16 != 0)
+    return set_err(PA_ERR_UNSUPPORTED, "a head row (head_size elements) must be a multiple of 16 bytes");
+  if ((int64_t)params->block_size * params->head_size > INT32_MAX / 2)
+    return set_err(PA_ERR_INVALID_ARG, "block_size * head_size too large");
   if (seq_len == 0) return PA_OK;
   if (!kv_cache || !block_table_row || !k_out || !v_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  int ss = 0, hs = 0;
+  pa::pool_strides(params->kv_layout, params->block_size, params->num_kv_heads, params->head_size, ss, hs);
   const int e = pa::launch_gather(kv_cache, block_table_row, seq_len, params->block_size, params->num_kv_heads,
-                                  params->head_size, elem, k_out, v_out, stream);
+                                  params->head_size, elem, ss, hs, k_out, v_out, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }
@@ -387,17 +403,23 @@ pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_ma
   if (params->dtype != PA_BF16 && params->dtype != PA_FP32) return set_err(PA_ERR_UNSUPPORTED, "dtype not built");
   if (params->kv_dtype != PA_KV_SAME)
     return set_err(PA_ERR_INVALID_ARG, "an e4m3 pool is written by pa_write_kv_fp8 (with its scales)");
-  const int64_t row_bytes =
-      (int64_t)params->num_kv_heads * params->head_size * (params->dtype == PA_BF16 ? 2 : 4);
-  if (row_bytes % 16 != 0 || row_bytes > INT32_MAX / 2)
-    return set_err(PA_ERR_UNSUPPORTED, "a K row (num_kv_heads * head_size elements) must be a multiple of 16 bytes");
+  if (params->kv_layout != PA_KV_NHD && params->kv_layout != PA_KV_HND)
+    return set_err(PA_ERR_INVALID_ARG, "kv_layout must be PA_KV_NHD or PA_KV_HND");
+  const int elem = params->dtype == PA_BF16 ? 2 : 4;
+  const int64_t head_bytes = (int64_t)params->head_size * elem;
+  const int64_t row_bytes = (int64_t)params->num_kv_heads * head_bytes;
+  if (head_bytes % 16 != 0 || row_bytes > INT32_MAX / 2 || (int64_t)params->block_size * head_bytes > INT32_MAX / 2)
+    return set_err(PA_ERR_UNSUPPORTED, "a head row (head_size elements) must be a multiple of 16 bytes");
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !slot_mapping || !kv_cache) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
   if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(kv_cache)) %
           16 != 0)
     return set_err(PA_ERR_INVALID_ARG, "key, value and kv_cache must be 16-byte aligned");
-  const int e = pa::launch_write_kv(key, value, slot_mapping, num_tokens, (int)row_bytes, params->block_size,
-                                    (int64_t)params->num_blocks * params->block_size, kv_cache, stream);
+  int ss = 0, hs = 0;
+  pa::pool_strides(params->kv_layout, params->block_size, params->num_kv_heads, params->head_size, ss, hs);
+  const int e = pa::launch_write_kv(key, value, slot_mapping, num_tokens, params->num_kv_heads, (int)head_bytes,
+                                    params->block_size, (int64_t)params->num_blocks * params->block_size,
+                                    (int64_t)ss * elem, (int64_t)hs * elem, kv_cache, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }
@@ -415,6 +437,10 @@ pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slo
   if (params->kv_dtype != PA_KV_FP8_E4M3) return set_err(PA_ERR_INVALID_ARG, "params->kv_dtype is not PA_KV_FP8_E4M3");
   if (params->dtype != PA_BF16) return set_err(PA_ERR_UNSUPPORTED, "e4m3 writes take bf16 key/value");
   if (params->head_size % 16 != 0) return set_err(PA_ERR_UNSUPPORTED, "head_size must be a multiple of 16");
+  if (params->kv_layout != PA_KV_NHD && params->kv_layout != PA_KV_HND)
+    return set_err(PA_ERR_INVALID_ARG, "kv_layout must be PA_KV_NHD or PA_KV_HND");
+  if ((int64_t)params->block_size * params->head_size > INT32_MAX / 2)
+    return set_err(PA_ERR_INVALID_ARG, "block_size * head_size too large");
   if ((int64_t)params->num_kv_heads * params->head_size > INT32_MAX / 4)
     return set_err(PA_ERR_INVALID_ARG, "K row too large");
   if (num_scales != 1 && num_scales != params->num_kv_heads)
@@ -425,9 +451,11 @@ pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slo
   if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(kv_cache)) %
           16 != 0)
     return set_err(PA_ERR_INVALID_ARG, "key, value and kv_cache must be 16-byte aligned");
+  int ss = 0, hs = 0;
+  pa::pool_strides(params->kv_layout, params->block_size, params->num_kv_heads, params->head_size, ss, hs);
   const int e = pa::launch_write_kv_fp8(key, value, slot_mapping, num_tokens, params->num_kv_heads, params->head_size,
-                                        params->block_size, (int64_t)params->num_blocks * params->block_size, k_scale,
-                                        v_scale, num_scales, kv_cache, stream);
+                                        params->block_size, (int64_t)params->num_blocks * params->block_size, ss, hs,
+                                        k_scale, v_scale, num_scales, kv_cache, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }

@@ -59,6 +59,7 @@ inline bool use_wide_prefill(int dtype, int head_size, int kv_dtype) {
 // Everything the kernels need besides the caller's tensors.
 struct LaunchGeom {
   int H, Hkv, g, D, bs, max_blocks, dtype, kv_dtype;
+  int slot_stride, head_stride;  // pool elements between slots / KV heads (see pool_strides)
   float scale_log2;  // scale * log2(e)
   PrefillShape ps;
 };
@@ -107,12 +108,27 @@ int launch_forward(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o,
                         float* l, int n_tok, int n_heads, int head_size, int dtype, void* stream);
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,
-                  int elem_bytes, void* k_out, void* v_out, void* stream);
-int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int row_bytes, int bs,
-                    int64_t n_slots, void* kv, void* stream);
+                  int elem_bytes, int64_t slot_stride, int64_t head_stride, void* k_out, void* v_out,
+                  void* stream);
+int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int head_bytes, int bs,
+                    int64_t n_slots, int64_t slot_bstride, int64_t head_bstride, void* kv, void* stream);
 int launch_write_kv_fp8(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int D, int bs,
-                        int64_t n_slots, const float* k_scale, const float* v_scale, int n_scales, void* kv,
-                        void* stream);
+                        int64_t n_slots, int64_t slot_stride, int64_t head_stride, const float* k_scale,
+                        const float* v_scale, int n_scales, void* kv, void* stream);
+
+// Pool element strides of the memory order `layout` (pa_kv_layout): between
+// consecutive slots of one KV head, and between KV heads of one slot.  NHD
+// (blocks, 2, slot, head, d): Hkv * D and D; HND (blocks, 2, head, slot, d):
+// D and bs * D.  The K/V halves and blocks are bs * Hkv * D apart either way.
+inline void pool_strides(int layout, int bs, int Hkv, int D, int& slot_stride, int& head_stride) {
+  if (layout == PA_KV_HND) {
+    slot_stride = D;
+    head_stride = bs * D;
+  } else {
+    slot_stride = Hkv * D;
+    head_stride = D;
+  }
+}
 
 // Launch bookkeeping for pa_profile_* (api.cpp).
 void profile_before(const char* name, void* stream);

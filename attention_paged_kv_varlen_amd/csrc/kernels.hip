@@ -226,6 +226,8 @@ struct KArgs {
   int tiles_per_head;  // prefill only
   int tiles_per_wg;    // prefill only: 2 per wave
   float scale_log2;
+  int slot_stride;  // pool elements between consecutive slots of one KV head (NHD: Hkv * D, HND: D)
+  int head_stride;  // pool elements between KV heads of one slot (NHD: D, HND: bs * D)
   const float* k_scale;  // e4m3 pool: K / V scales, one (n_scales = 1) or one per KV head
   const float* v_scale;
   int n_scales;
@@ -349,10 +351,10 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
     }
 
     const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
-    const int64_t slot_stride = (int64_t)a.Hkv * D;
+    const int64_t slot_stride = a.slot_stride;
     const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
     const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-    const KV* kvh_base = kv + (int64_t)kvh * D;
+    const KV* kvh_base = kv + (int64_t)kvh * a.head_stride;
     const int kv_end = it.kv_end;
 
     f32x4 o[VE];
@@ -515,10 +517,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
   }
 
   const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
-  const int64_t slot_stride = (int64_t)a.Hkv * D;
+  const int64_t slot_stride = a.slot_stride;
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-  const KV* kvh_base = kv + (int64_t)kvh * D;
+  const KV* kvh_base = kv + (int64_t)kvh * a.head_stride;
   const int chunk = tid % CPR;
 
   u32x4 stK[NLD], stV[NLD];
@@ -765,10 +767,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // loader: wave w fills block rows 16w .. 16w+15 of K and of V (one 16-key
   // tile, hence one physical block, per wave)
   const int64_t blk_stride = (int64_t)2 * a.bs * a.Hkv * D;
-  const int64_t slot_stride = (int64_t)a.Hkv * D;
+  const int64_t slot_stride = a.slot_stride;
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-  const uint16_t* kvh_base = kv + (int64_t)kvh * D;
+  const uint16_t* kvh_base = kv + (int64_t)kvh * a.head_stride;
   // per-lane byte offset of its 16-byte chunk inside the wave's slab of RPW
   // rows (rows 4i + lane/16, XOR-swizzled chunk): constant across blocks
   uint32_t loff[RPW / 4];
@@ -1100,28 +1102,35 @@ __global__ void __launch_bounds__(256) merge_states_kernel(const T* oa, const fl
 }
 
 __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* kv, const int32_t* bt_row, int seq_len,
-                                                     int bs, int64_t row_bytes, unsigned char* k_out,
+                                                     int bs, int Hkv, int head_bytes, int64_t slot_bstride,
+                                                     int64_t head_bstride, unsigned char* k_out,
                                                      unsigned char* v_out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t cpt = row_bytes / 16;  // 16-byte chunks per token (all KV heads)
+  const int cph = head_bytes / 16;  // 16-byte chunks per head row
+  const int64_t cpt = (int64_t)Hkv * cph;
   if (i >= (int64_t)seq_len * cpt) return;
   const int t = (int)(i / cpt);
-  const int64_t c = i % cpt;
+  const int h = (int)(i % cpt) / cph;
+  const int c = (int)(i % cpt) % cph;
   const int64_t blk = bt_row[t / bs];
-  const unsigned char* src = kv + (blk * 2 * bs + t % bs) * row_bytes + 16 * c;
-  reinterpret_cast<u32x4*>(k_out + (int64_t)t * row_bytes)[c] = *reinterpret_cast<const u32x4*>(src);
-  reinterpret_cast<u32x4*>(v_out + (int64_t)t * row_bytes)[c] =
-      *reinterpret_cast<const u32x4*>(src + (int64_t)bs * row_bytes);
+  const int64_t half = (int64_t)bs * Hkv * head_bytes;
+  const unsigned char* src = kv + blk * 2 * half + h * head_bstride + (t % bs) * slot_bstride + 16 * c;
+  const int64_t dst = ((int64_t)t * Hkv + h) * head_bytes + 16 * c;
+  *reinterpret_cast<u32x4*>(k_out + dst) = *reinterpret_cast<const u32x4*>(src);
+  *reinterpret_cast<u32x4*>(v_out + dst) = *reinterpret_cast<const u32x4*>(src + half);
 }
 
 // ---------------------------------------------------------------------------
 // Cache write: thread i copies 16-byte chunk i % (2 C) of token i / (2 C)
-// (C chunks per K or V row; the first C of the K row, then the V row) to the
-// token's slot.  Consecutive threads move consecutive bytes of one row, so
-// reads and writes are coalesced.
+// (C chunks per K or V row of all KV heads; the first C of the K row, then the
+// V row) to the token's slot; a head's bytes go to that head's place in the
+// pool's memory order.  Consecutive threads move consecutive bytes of one row,
+// so reads are coalesced, and so are writes within a head row.
 __global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, const unsigned char* v,
-                                                       const int64_t* slots, int n_tok, int row_bytes, int bs,
-                                                       int64_t n_slots, unsigned char* kv) {
+                                                       const int64_t* slots, int n_tok, int Hkv, int head_bytes,
+                                                       int bs, int64_t n_slots, int64_t slot_bstride,
+                                                       int64_t head_bstride, unsigned char* kv) {
+  const int row_bytes = Hkv * head_bytes;
   const int chunks = row_bytes / 16;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)n_tok * 2 * chunks) return;
@@ -1133,7 +1142,8 @@ __global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, c
   if (s < 0 || s >= n_slots) return;
   const int64_t blk = s / bs, in = s % bs;
   const unsigned char* src = (half ? v : k) + (int64_t)t * row_bytes + off;
-  unsigned char* dst = kv + ((blk * 2 + half) * bs + in) * (int64_t)row_bytes + off;
+  unsigned char* dst = kv + (blk * 2 + half) * bs * (int64_t)row_bytes + (off / head_bytes) * head_bstride +
+                       in * slot_bstride + off % head_bytes;
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
@@ -1144,6 +1154,7 @@ __global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, c
 // quotient clamped to +-448 first so that large values saturate; NaN -> 0x7F.
 __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, const uint16_t* v, const int64_t* slots,
                                                            int n_tok, int Hkv, int D, int bs, int64_t n_slots,
+                                                           int64_t slot_stride, int64_t head_stride,
                                                            const float* ks, const float* vs, int n_scales,
                                                            unsigned char* kv) {
   const int row = Hkv * D;  // elements per K row = bytes per pool row
@@ -1185,7 +1196,7 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, co
     out[j] = pk;
   }
   const int64_t blk = s / bs, in = s % bs;
-  unsigned char* dst = kv + ((blk * 2 + half) * bs + in) * (int64_t)row + off;
+  unsigned char* dst = kv + (blk * 2 + half) * bs * (int64_t)row + (off / D) * head_stride + in * slot_stride + off % D;
   *reinterpret_cast<u32x4*>(dst) = out;
 }
 
@@ -1237,6 +1248,8 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   a.bs = g.bs;
   a.max_blocks = g.max_blocks;
   a.scale_log2 = g.scale_log2;
+  a.slot_stride = g.slot_stride;
+  a.head_stride = g.head_stride;
   a.k_scale = t.k_scale;
   a.v_scale = t.v_scale;
   a.n_scales = t.n_scales;
@@ -1345,25 +1358,25 @@ int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves) 
   return e == hipSuccess ? n : 0;
 }
 
-int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int row_bytes, int bs,
-                    int64_t n_slots, void* kv, void* stream) {
-  const int64_t n = (int64_t)n_tok * 2 * (row_bytes / 16);
+int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int head_bytes, int bs,
+                    int64_t n_slots, int64_t slot_bstride, int64_t head_bstride, void* kv, void* stream) {
+  const int64_t n = (int64_t)n_tok * 2 * (Hkv * head_bytes / 16);
   const int64_t nblk = (n + 255) / 256;
   if (nblk > INT32_MAX) return (int)hipErrorInvalidConfiguration;
   return launch("write_kv", write_kv_kernel, dim3((unsigned)nblk), dim3(256), stream,
-                static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), slots, n_tok, row_bytes, bs,
-                n_slots, static_cast<unsigned char*>(kv));
+                static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), slots, n_tok, Hkv,
+                head_bytes, bs, n_slots, slot_bstride, head_bstride, static_cast<unsigned char*>(kv));
 }
 
 int launch_write_kv_fp8(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int D, int bs,
-                        int64_t n_slots, const float* k_scale, const float* v_scale, int n_scales, void* kv,
-                        void* stream) {
+                        int64_t n_slots, int64_t slot_stride, int64_t head_stride, const float* k_scale,
+                        const float* v_scale, int n_scales, void* kv, void* stream) {
   const int64_t n = (int64_t)n_tok * 2 * (Hkv * D / 16);
   const int64_t nblk = (n + 255) / 256;
   if (nblk > INT32_MAX) return (int)hipErrorInvalidConfiguration;
   return launch("write_kv_e4m3", write_kv_fp8_kernel, dim3((unsigned)nblk), dim3(256), stream,
                 static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slots, n_tok, Hkv, D, bs, n_slots,
-                k_scale, v_scale, n_scales, static_cast<unsigned char*>(kv));
+                slot_stride, head_stride, k_scale, v_scale, n_scales, static_cast<unsigned char*>(kv));
 }
 
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb, void* o, float* l, int n_tok,
@@ -1379,13 +1392,13 @@ int launch_merge_states(const void* oa, const float* la, const void* ob, const f
 }
 
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D, int elem_bytes,
-                  void* k_out, void* v_out, void* stream) {
-  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes;
-  const int64_t n = (int64_t)seq_len * (row_bytes / 16);
+                  int64_t slot_stride, int64_t head_stride, void* k_out, void* v_out, void* stream) {
+  const int head_bytes = D * elem_bytes;
+  const int64_t n = (int64_t)seq_len * Hkv * (head_bytes / 16);
   if (n == 0) return 0;
   return launch("gather", gather_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), stream,
-                (const unsigned char*)kv, bt_row, seq_len, bs, row_bytes, (unsigned char*)k_out,
-                (unsigned char*)v_out);
+                (const unsigned char*)kv, bt_row, seq_len, bs, Hkv, head_bytes, slot_stride * elem_bytes,
+                head_stride * elem_bytes, (unsigned char*)k_out, (unsigned char*)v_out);
 }
 
 }  // namespace pa

@@ -78,6 +78,10 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     return fail(err, PA_ERR_INVALID_ARG, "kv_dtype %lld (PA_KV_SAME, PA_KV_FP8_E4M3)", p.kv_dtype);
   if (p.kv_dtype == PA_KV_FP8_E4M3 && p.dtype != PA_BF16)
     return fail(err, PA_ERR_UNSUPPORTED, "an e4m3 pool is built for bf16 queries only");
+  if (p.kv_layout != PA_KV_NHD && p.kv_layout != PA_KV_HND)
+    return fail(err, PA_ERR_INVALID_ARG, "kv_layout %lld (PA_KV_NHD, PA_KV_HND)", p.kv_layout);
+  if ((int64_t)p.block_size * p.head_size > INT32_MAX / 2 || (int64_t)p.num_kv_heads * p.head_size > INT32_MAX / 2)
+    return fail(err, PA_ERR_INVALID_ARG, "block_size * head_size or num_kv_heads * head_size too large");
   if (p.num_blocks < 1) return fail(err, PA_ERR_INVALID_ARG, "num_blocks %lld < 1", p.num_blocks);
   if (p.max_blocks_per_seq < 1)
     return fail(err, PA_ERR_INVALID_ARG, "max_blocks_per_seq %lld < 1", p.max_blocks_per_seq);

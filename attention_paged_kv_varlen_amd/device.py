@@ -46,7 +46,8 @@ class DeviceBatch:
 
 def to_device(q, kv_cache, block_table, query_start_loc, seq_lens, *, num_heads, num_kv_heads, head_size,
               block_size, dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0,
-              device="cuda", kv_cache_dev=None, kv_dtype="same", k_scale=None, v_scale=None) -> DeviceBatch:
+              device="cuda", kv_cache_dev=None, kv_dtype="same", k_scale=None, v_scale=None,
+              kv_layout="NHD") -> DeviceBatch:
     """Build the plan and the device tensors (q, pool, table, out, lse, workspace;
     the K/V scales of an e4m3 pool)."""
     import torch
@@ -56,7 +57,7 @@ def to_device(q, kv_cache, block_table, query_start_loc, seq_lens, *, num_heads,
         num_seqs=len(seq_lens), num_heads=num_heads, num_kv_heads=num_kv_heads, head_size=head_size,
         block_size=block_size, num_blocks=kv_cache.shape[0], max_blocks_per_seq=bt.shape[1], dtype=dtype,
         scale=scale, causal=causal, common_prefix_len=common_prefix_len, kv_split_tokens=kv_split_tokens,
-        kv_dtype=kv_dtype)
+        kv_dtype=kv_dtype, kv_layout=kv_layout)
     plan = _capi.pa_plan_create(params, query_start_loc, seq_lens, bt, device=dev.index or 0)
     tq = _to_torch(q, dtype, dev)
     tkv = kv_cache_dev if kv_cache_dev is not None else _to_torch(kv_cache, dtype, dev)

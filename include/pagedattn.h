@@ -73,6 +73,16 @@ typedef enum pa_dtype { PA_BF16 = 0, PA_FP32 = 1 } pa_dtype;
  */
 typedef enum pa_kv_dtype { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
 
+/*
+ * Memory order of the pool («FlashAttention y FlashInfer», §Motivación de
+ * diseño: two layouts NHD / HND chosen by get_kv_cache_stride_order).  The
+ * logical shape is always (num_blocks, 2, bs, Hkv, d) (pa_kv_cache_shape).
+ * PA_KV_NHD stores it in that order: the KV heads of one slot are adjacent.
+ * PA_KV_HND stores (num_blocks, 2, Hkv, bs, d): one KV head's slots of a block
+ * are adjacent (for one head, a block's bs rows of d elements are contiguous).
+ */
+typedef enum pa_kv_layout { PA_KV_NHD = 0, PA_KV_HND = 1 } pa_kv_layout;
+
 /* Sizes of one batch.  All fields are read by pa_plan_create only. */
 typedef struct pa_params {
   int32_t num_seqs;           /* B >= 0 */
@@ -91,6 +101,8 @@ typedef struct pa_params {
   float scale;                /* softmax scale applied to q . k (positive, finite) */
   int32_t kv_dtype;           /* pa_kv_dtype: 0 = the pool has element type dtype; PA_KV_FP8_E4M3
                                  needs dtype PA_BF16 (else PA_ERR_UNSUPPORTED) */
+  int32_t kv_layout;          /* pa_kv_layout: 0 = NHD, 1 = HND; block sizes up to 1024 and beyond
+                                 (any multiple of 16) work with either */
 } pa_params;
 
 /* Opaque, immutable schedule for one batch; reusable across layers and calls. */
@@ -148,6 +160,15 @@ typedef struct pa_kernel_time {
  */
 pa_status pa_kv_cache_shape(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                             int32_t head_size, int64_t shape_out[5]);
+
+/*
+ * Memory order of the pool's logical dimensions (blocks, K/V, slot, KV head,
+ * head size), outermost first, for a pa_kv_layout: NHD -> {0, 1, 2, 3, 4},
+ * HND -> {0, 1, 3, 2, 4} («FlashAttention y FlashInfer», §Motivación de
+ * diseño, get_kv_cache_stride_order).  order_out: host int32[5].
+ * Errors: INVALID_ARG (unknown layout, NULL order_out).
+ */
+pa_status pa_kv_cache_stride_order(int32_t layout, int32_t order_out[5]);
 
 /*
  * Build the schedule for one batch (the metadata builder).  «AttentionBackend:
@@ -266,13 +287,14 @@ pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, 
  *                16-byte aligned.
  *  slot_mapping  device int64[num_tokens]; a negative slot skips the token, and
  *                so does a slot at or past num_blocks * block_size.
- *  kv_cache      device pool (num_blocks, 2, bs, Hkv, d) of params->dtype, 16-byte
- *                aligned, written in place; slots not named keep their contents.
- * Uses params->num_kv_heads, head_size, block_size, num_blocks and dtype.  Two
- * tokens with the same slot race.  Asynchronous on `stream`, copies bit for bit.
- * Errors: INVALID_ARG (sizes, NULL or misaligned pointers, an e4m3 pool: see
- * pa_write_kv_fp8), UNSUPPORTED (dtype, a K row that is not a whole number of
- * 16-byte chunks), HIP.
+ *  kv_cache      device pool (num_blocks, 2, bs, Hkv, d) of params->dtype in the
+ *                memory order params->kv_layout, 16-byte aligned, written in
+ *                place; slots not named keep their contents.
+ * Uses params->num_kv_heads, head_size, block_size, num_blocks, dtype and
+ * kv_layout.  Two tokens with the same slot race.  Asynchronous on `stream`,
+ * copies bit for bit.  Errors: INVALID_ARG (sizes, NULL or misaligned
+ * pointers, unknown layout, an e4m3 pool: see pa_write_kv_fp8), UNSUPPORTED
+ * (dtype, a head row that is not a whole number of 16-byte chunks), HIP.
  */
 pa_status pa_write_kv(const void* key, const void* value, const int64_t* slot_mapping, int32_t num_tokens,
                       const pa_params* params, void* kv_cache, void* stream);
@@ -299,10 +321,10 @@ pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slo
  * «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
  * token t is slot t % bs of block block_table_row[t / bs].
  *  kv_cache        device pool of params->dtype (e4m3 codes when params->kv_dtype
- *                  is PA_KV_FP8_E4M3).
+ *                  is PA_KV_FP8_E4M3) in the memory order params->kv_layout.
  *  block_table_row device int32[ceil(seq_len / bs)].
  *  k_out, v_out    device [seq_len, Hkv, d] each, the pool's element type.
- * Uses params->block_size, num_kv_heads, head_size, dtype, kv_dtype.  The ids are not
+ * Uses params->block_size, num_kv_heads, head_size, dtype, kv_dtype, kv_layout.  The ids are not
  * checked on the device: they must be in [0, num_blocks).
  * Errors: INVALID_ARG (sizes, NULL pointers), UNSUPPORTED (dtype).
  */

@@ -32,7 +32,8 @@ def run_gpu(batch, *, common_prefix_len=None, kv_split_tokens=0, causal=None, q=
         num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
         block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale,
         causal=batch.causal if causal is None else causal, common_prefix_len=cp,
-        kv_split_tokens=kv_split_tokens, kv_dtype=batch.kv_dtype, k_scale=batch.k_scale, v_scale=batch.v_scale)
+        kv_split_tokens=kv_split_tokens, kv_dtype=batch.kv_dtype, k_scale=batch.k_scale, v_scale=batch.v_scale,
+        kv_layout=batch.kv_layout)
     db.forward()
     torch.cuda.synchronize()
     out = db.out.float().cpu().numpy().astype(np.float64)
@@ -47,7 +48,7 @@ def oracle_full(batch, causal=None, q=None, kv_cache=None, block_table=None):
                             batch.query_start_loc, batch.seq_lens, batch.scale, dtype=batch.dtype,
                             causal=batch.causal if causal is None else causal, kv_dtype=batch.kv_dtype,
                             k_scale=1.0 if batch.k_scale is None else batch.k_scale,
-                            v_scale=1.0 if batch.v_scale is None else batch.v_scale)
+                            v_scale=1.0 if batch.v_scale is None else batch.v_scale, kv_layout=batch.kv_layout)
 
 
 def assert_close(out, lse, ref_out, ref_lse, what=""):

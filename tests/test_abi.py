@@ -126,3 +126,24 @@ def test_e4m3_forward_needs_a_device_plan_and_scales():
     with pytest.raises(pa.PagedAttnError) as ei:
         pa.pa_forward_fp8(plan, 16, 16, 16, 16, 16, 16, num_scales=2, stream=0)
     assert ei.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_stride_order_and_layout_checks():
+    # «FlashAttention y FlashInfer», §Motivación de diseño: NHD / HND stride orders
+    assert pa.pa_kv_cache_stride_order("NHD") == (0, 1, 2, 3, 4)
+    assert pa.pa_kv_cache_stride_order("HND") == (0, 1, 3, 2, 4)
+    with pytest.raises(pa.PagedAttnError) as ei:
+        pa.pa_kv_cache_stride_order(5)
+    assert ei.value.status == pa.PA_ERR_INVALID_ARG
+    p = pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=2, head_size=128, block_size=1024, num_blocks=4,
+                       max_blocks_per_seq=4, dtype="bf16", scale=0.1, kv_layout="HND")
+    plan = pa.pa_plan_create(p, [0, 3], [3000], device=-1)   # 1024-token pages plan as any others
+    assert pa.pa_plan_get_info(plan)["num_prefills"] == 1
+    bad = pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4,
+                         max_blocks_per_seq=4, dtype="bf16", scale=0.1, kv_layout=3)
+    for call in (lambda: pa.pa_plan_create(bad, [0, 1], [5], device=-1),
+                 lambda: pa.pa_write_kv(16, 16, 16, 1, bad, kv_cache=16, stream=0),
+                 lambda: pa.pa_gather_kv(16, 16, 1, bad, 16, 16, stream=0)):
+        with pytest.raises(pa.PagedAttnError) as ei:
+            call()
+        assert ei.value.status == pa.PA_ERR_INVALID_ARG

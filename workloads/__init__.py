@@ -10,7 +10,9 @@ declares in «FlashAttention y FlashInfer», §Flujo de datos):
 
 * ``q``            ``[num_tokens, num_heads, head_size]``
 * ``kv_cache``     ``[num_blocks, 2, block_size, num_kv_heads, head_size]``; index 0
-                   of dim 1 holds K, index 1 holds V
+                   of dim 1 holds K, index 1 holds V (``kv_layout="HND"`` stores
+                   the same pool as ``[num_blocks, 2, num_kv_heads, block_size,
+                   head_size]``)
 * ``block_table``  int32 ``[num_seqs, max_blocks_per_seq]``
 * ``query_start_loc`` int32 ``[num_seqs + 1]``, prefix sums of the query lengths
 * ``seq_lens``     int32 ``[num_seqs]``, KV length of each sequence including its
@@ -78,6 +80,7 @@ class Batch:
     kv_dtype: str = "same"          # "same" or "fp8_e4m3"
     k_scale: np.ndarray | None = None  # e4m3 pool: float32 [num_kv_heads]
     v_scale: np.ndarray | None = None
+    kv_layout: str = "NHD"          # memory order of kv_cache: "NHD" or "HND"
 
     @property
     def num_seqs(self) -> int:
@@ -127,6 +130,7 @@ def make_batch(
     name: str = "custom",
     max_blocks_per_seq: int | None = None,
     kv_dtype: str = "same",
+    kv_layout: str = "NHD",
 ) -> Batch:
     """Draw a batch for the given per-sequence query lengths and KV lengths.
 
@@ -226,6 +230,10 @@ def make_batch(
 
     qsl = np.zeros(B + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(qlens)
+    if kv_layout == "HND":   # store the same logical pool with the KV head before the slot
+        pool = np.ascontiguousarray(pool.transpose(0, 1, 3, 2, 4))
+    elif kv_layout != "NHD":
+        raise ValueError(f"kv_layout {kv_layout!r}")
     k_scale = v_scale = None
     if f8:
         rs = np.random.Generator(np.random.PCG64(ss.spawn(1)[0]))
@@ -250,6 +258,7 @@ def make_batch(
         kv_dtype=kv_dtype,
         k_scale=k_scale,
         v_scale=v_scale,
+        kv_layout=kv_layout,
     )
 
 
@@ -300,7 +309,8 @@ def config_lengths(cfg: int, seed: int | None = None):
     raise ValueError(f"unknown configuration {cfg}")
 
 
-def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtype: str = "same") -> Batch:
+def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtype: str = "same",
+                 kv_layout: str = "NHD") -> Batch:
     """Draw the full-size batch of configuration ``cfg`` (1..5); ``kv_dtype``
     "fp8_e4m3" gives the same lengths and placement over an e4m3 pool."""
     seed = cfg if seed is None else seed
@@ -312,5 +322,5 @@ def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtyp
         kw["scale"] = 1.0 / 8.0
     return make_batch(
         qlens, lens, seed=seed, shared_prefix_blocks=sp, poison=poison,
-        name=CONFIG_NAMES[cfg], kv_dtype=kv_dtype, **shape, **kw,
+        name=CONFIG_NAMES[cfg], kv_dtype=kv_dtype, kv_layout=kv_layout, **shape, **kw,
     )
