@@ -207,11 +207,12 @@ def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
 
 # ---------------------------------------------------------------------------
 
-def measure(cfg: int, steps: int, warmup: int, seed=None, kv_dtype: str = "same") -> dict:
+def measure(cfg: int, steps: int, warmup: int, seed=None, kv_dtype: str = "same", kv_layout: str = "NHD",
+            block_size=None) -> dict:
     """Generate the workload, time it, and return the measurement record."""
     import attention_paged_kv_varlen_amd as pa
     from workloads import config_batch
-    batch = config_batch(cfg, seed=seed, kv_dtype=kv_dtype)
+    batch = config_batch(cfg, seed=seed, kv_dtype=kv_dtype, kv_layout=kv_layout, block_size=block_size)
     s = 1 if kv_dtype == "fp8_e4m3" else (2 if batch.dtype == "bf16" else 4)
     counts = algorithmic_counts(batch.query_lens, batch.seq_lens, num_heads=batch.num_heads,
                                 num_kv_heads=batch.num_kv_heads, head_size=batch.head_size, elem_bytes=s,
@@ -358,6 +359,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=sorted(WORKLOADS) + ["kvwrite"], default="decode")
+    ap.add_argument("--kv-layout", choices=["NHD", "HND"], default="NHD",
+                    help="memory order of the pool (HND: KV head before slot)")
+    ap.add_argument("--block-size", type=int, default=None, help="page size override (a multiple of 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -396,7 +400,8 @@ def main(argv=None) -> int:
         return 0
     cfg = WORKLOADS[args.workload]
     kv_dtype = KV_DTYPES.get(args.workload, "same")
-    m = measure(cfg, args.steps, args.warmup, kv_dtype=kv_dtype)
+    m = measure(cfg, args.steps, args.warmup, kv_dtype=kv_dtype, kv_layout=args.kv_layout,
+                block_size=args.block_size)
     batch, counts, t = m["batch"], m["counts"], m["timing"]
     ms = t["ms_per_step"]
     dtype = batch.dtype
@@ -464,6 +469,10 @@ def main(argv=None) -> int:
     line["algorithmic"] = {k: counts[k] for k in ("decode_bytes", "prefill_flops", "decode_kv_tokens",
                                                   "prefill_tokens")}
 
+    if args.kv_layout != "NHD" or args.block_size is not None:
+        line["config"]["kv_layout"] = args.kv_layout
+        line["config"]["block_size"] = batch.block_size
+        line["config"]["workload"] += f" [pool {args.kv_layout}, bs={batch.block_size}]"
     if kv_dtype != "same":
         line["config"]["kv_dtype"] = kv_dtype
         line["data"] = "synthetic (seeded N(0,1) Q; random e4m3 codes and per-head scales; random page placement)"

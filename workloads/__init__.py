@@ -310,12 +310,14 @@ def config_lengths(cfg: int, seed: int | None = None):
 
 
 def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtype: str = "same",
-                 kv_layout: str = "NHD") -> Batch:
+                 kv_layout: str = "NHD", block_size: int | None = None) -> Batch:
     """Draw the full-size batch of configuration ``cfg`` (1..5); ``kv_dtype``
     "fp8_e4m3" gives the same lengths and placement over an e4m3 pool."""
     seed = cfg if seed is None else seed
     qlens, lens, sp = config_lengths(cfg, seed)
-    shape = CONFIG_SHAPES[cfg]
+    shape = dict(CONFIG_SHAPES[cfg])
+    if block_size is not None:  # same lengths and values, other page size
+        shape["block_size"] = int(block_size)
     kw = {}
     if cfg == 1:
         kw["num_blocks"] = 64
