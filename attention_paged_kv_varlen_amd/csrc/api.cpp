@@ -185,12 +185,15 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
         return set_err(PA_ERR_HIP, "hipSetDevice failed");
       }
       std::vector<unsigned char> host(total, 0);
-      std::memcpy(host.data() + o_dec, hp.decode_items.data(), b_dec);
-      std::memcpy(host.data() + o_pre, hp.prefill_items.data(), b_pre);
-      std::memcpy(host.data() + o_pfx, hp.prefix_items.data(), b_pfx);
-      std::memcpy(host.data() + o_mrg, hp.merges.data(), b_mrg);
-      std::memcpy(host.data() + o_row, hp.row_pbase.data(), b_row);
-      std::memcpy(host.data() + o_lst, hp.decode_lists.data(), b_lst);
+      auto put = [&](size_t off, const void* src, size_t n) {  // an empty vector's data() may be null
+        if (n) std::memcpy(host.data() + off, src, n);
+      };
+      put(o_dec, hp.decode_items.data(), b_dec);
+      put(o_pre, hp.prefill_items.data(), b_pre);
+      put(o_pfx, hp.prefix_items.data(), b_pfx);
+      put(o_mrg, hp.merges.data(), b_mrg);
+      put(o_row, hp.row_pbase.data(), b_row);
+      put(o_lst, hp.decode_lists.data(), b_lst);
       hipError_t e = hipMalloc(&plan->dev_buf, total);
       if (e != hipSuccess) {
         delete plan;
