@@ -48,12 +48,11 @@ struct PrefillShape {
   int head_groups;     // g / heads_per_wg
 };
 PrefillShape prefill_shape(int group, int tiles, int max_heads);
-// The wide prefill kernel serves bf16 with head size 128 on a bf16 pool: 4
-// waves, 8 column tiles per workgroup, both tiles of a wave on one head.  An
-// e4m3 pool goes through the general prefill kernel, which widens the codes to
-// bf16 while it stages them in LDS.
+// The wide prefill kernel serves bf16 queries with head size 128 (bf16 or
+// e4m3 pool): 4 waves, 8 column tiles per workgroup, both tiles of a wave on
+// one head.
 inline bool use_wide_prefill(int dtype, int head_size, int kv_dtype) {
-  return dtype == PA_BF16 && head_size == 128 && kv_dtype == PA_KV_SAME;
+  return dtype == PA_BF16 && head_size == 128 && (kv_dtype == PA_KV_SAME || kv_dtype == PA_KV_FP8_E4M3);
 }
 
 // Everything the kernels need besides the caller's tensors.

@@ -684,9 +684,9 @@ __device__ __forceinline__ u32x2 tr_read_b64(const unsigned char* p) {
 
 // Write one column whose accumulator tile dt holds d = 16 dt + 4 qd + i (i = 0..3).
 __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int h, int slot, int qd,
-                                                    const f32x4 (&o)[8], float m_run, float l_run) {
+                                                    const f32x4 (&o)[8], float m_run, float l_run, float omul) {
   constexpr int D = 128;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = l_run > 0.f ? omul / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   const int pb = a.row_pbase[row];
   if (pb < 0) {
@@ -715,7 +715,16 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
 // rarely after) a side path takes the exact column max, rescales O and l and
 // recomputes them.  Program order lets half 0's softmax run under half 1's
 // S^T MFMAs and half 1's softmax under half 0's O^T MFMAs.
+//
+// F8: the pool holds e4m3 codes.  The next block's codes are then loaded into
+// registers at the start of a block (16 per lane and load, two K and two V
+// loads per lane) and widened to bf16 into the same swizzled LDS layout at its
+// end, after the block's own reads of the other stage; everything that reads
+// LDS is unchanged.  The K scale joins the softmax scale, the V scale
+// multiplies the output.
+template <bool F8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+  using KV = std::conditional_t<F8, uint8_t, uint16_t>;
   constexpr int NW = 4;
   constexpr int RPW = kWideKT / NW;  // block rows each wave loads: one 16-key tile
   constexpr int D = 128, VE = 8, KS = 4;
@@ -738,9 +747,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int hgrp = hgi % a.head_groups;
   const int r = lane & 15, qd = lane >> 4;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
+  const KV* kv = static_cast<const KV*>(a.kv);
   const int kv_lo = it.kv_begin, kv_hi = it.kv_end;
-  const float sl2 = a.scale_log2;
+  const float sl2 = F8 ? a.scale_log2 * kv_scale_of(a.k_scale, a.n_scales, kvh) : a.scale_log2;
+  const float omul = F8 ? kv_scale_of(a.v_scale, a.n_scales, kvh) : 1.f;
 
   // this wave's two column tiles share one head
   const int head = kvh * a.g + hgrp * a.heads_per_grp + (2 * wave) / a.tiles_per_head;
@@ -770,7 +780,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t slot_stride = a.slot_stride;
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
-  const uint16_t* kvh_base = kv + (int64_t)kvh * a.head_stride;
+  const KV* kvh_base = kv + (int64_t)kvh * a.head_stride;
   // per-lane byte offset of its 16-byte chunk inside the wave's slab of RPW
   // rows (rows 4i + lane/16, XOR-swizzled chunk): constant across blocks
   uint32_t loff[RPW / 4];
@@ -783,9 +793,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // clamped); looked up one block ahead so the lookup's latency is covered by
   // the wait before the next barrier
   auto page_of = [&](int kb) { return btrow[min(kb + RPW * wave, kv_hi - 1) / a.bs]; };
+  // e4m3: this wave's slab of the next block, 16 codes per lane and load (row
+  // 8 i + lane / 8 of the slab, codes 16 (lane % 8) .. +15): K in st8[0..1],
+  // V in st8[2..3]
+  u32x4 st8[4];
   auto issue = [&](int kb, int stage, int pid) {
     pid = __builtin_amdgcn_readfirstlane(pid);
     const int key0 = kb + RPW * wave;  // wave-uniform
+    if constexpr (F8) {
+      // rows past the end re-read the last valid key (masked later); the
+      // slab lies in one physical block
+      const int pst = min(key0, kv_hi - 1) / a.bs * a.bs;
+      const KV* page = kvh_base + (int64_t)pid * blk_stride;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int key = min(key0 + 8 * i + (lane >> 3), kv_hi - 1);
+        const KV* src = page + (int64_t)(key - pst) * slot_stride + 16 * (lane & 7);
+        st8[i] = *reinterpret_cast<const u32x4*>(src);
+        st8[2 + i] = *reinterpret_cast<const u32x4*>(src + v_half);
+      }
+      return;
+    }
     lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + RPW * wave * kWideRow;
     if (key0 + RPW - 1 < kv_hi) {
       // whole slab valid and inside one physical block: scalar base + lane offset
@@ -805,17 +833,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int ks = min(key0, kv_hi - 1);
       const int blk = ks / a.bs;
       const int pst = blk * a.bs;
-      const uint16_t* page = kvh_base + (int64_t)pid * blk_stride;
+      const KV* page = kvh_base + (int64_t)pid * blk_stride;
 #pragma unroll
       for (int i = 0; i < RPW / 4; ++i) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
         const int key = min(kb + row, kv_hi - 1);
-        const uint16_t* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row));
+        const KV* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row));
         __builtin_amdgcn_global_load_lds((const void*)src,
                                          (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
                                          (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
                                          16, 0, 0);
+      }
+    }
+  };
+  // e4m3: widen the staged codes into LDS stage `stage` (bf16, same swizzled
+  // layout as the direct-to-LDS loads); chunk 2 (lane % 8) and its successor of
+  // the row hold codes 0..7 and 8..15 of the lane's load
+  auto commit = [&](int stage) {
+    if constexpr (F8) {
+      unsigned char* base = stage ? lds1 : lds0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = RPW * wave + 8 * i + (lane >> 3);
+        const int sw = wide_swizzle(row);
+        const int c = 2 * (lane & 7);
+        unsigned char* rk = base + row * kWideRow;
+        *reinterpret_cast<u32x4*>(rk + 16 * (c ^ sw)) = e4m3x8_to_bf16(st8[i][0], st8[i][1]);
+        *reinterpret_cast<u32x4*>(rk + 16 * ((c + 1) ^ sw)) = e4m3x8_to_bf16(st8[i][2], st8[i][3]);
+        *reinterpret_cast<u32x4*>(rk + kWideBlk + 16 * (c ^ sw)) = e4m3x8_to_bf16(st8[2 + i][0], st8[2 + i][1]);
+        *reinterpret_cast<u32x4*>(rk + kWideBlk + 16 * ((c + 1) ^ sw)) = e4m3x8_to_bf16(st8[2 + i][2], st8[2 + i][3]);
       }
     }
   };
@@ -862,7 +909,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       issue(kb + kWideKT, STAGE ^ 1, pnext);
       pnext = page_of(kb + 2 * kWideKT);
     }
-    if (MASKED && kb > wave_max_lim) return;
+    if (MASKED && kb > wave_max_lim) {
+      if (F8 && jb + 1 < nblk) commit(STAGE ^ 1);
+      return;
+    }
 
     const unsigned char* Kb = STAGE ? lds1 : lds0;
     const unsigned char* Vb = Kb + kWideBlk;
@@ -957,9 +1007,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         O::mma(o[1][dt], vf, pf[1]);
       }
     });
+    // the other stage was last read in block jb - 1, before this block's barrier
+    if (F8 && jb + 1 < nblk) commit(STAGE ^ 1);
   };
   if (nblk > 0) {
     issue(kv_lo, 0, page_of(kv_lo));
+    if (F8) commit(0);
     pnext = page_of(kv_lo + kWideKT);
   }
   using I0 = std::integral_constant<int, 0>;
@@ -981,7 +1034,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int c = 0; c < 2; ++c) {
     const float l = xlane_sum(l_run[c]);
     const int pos = pos0[c] + r;
-    if (pos < it.nrows) write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l);
+    if (pos < it.nrows) write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l, omul);
   }
 }
 
@@ -1225,7 +1278,11 @@ int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) 
   const dim3 grid((unsigned)n);
   if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint16_t>::value && D == 128)
   {
-    return launch(name, prefill_wide_kernel, grid, dim3(256), stream, p);
+    return launch(name, prefill_wide_kernel<false>, grid, dim3(256), stream, p);
+  }
+  else if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint8_t>::value && D == 128)
+  {
+    return launch(name, prefill_wide_kernel<true>, grid, dim3(256), stream, p);
   }
   else
     return launch(name, prefill_kernel<T, KV, D>, grid, dim3(256), stream, p);

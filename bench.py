@@ -362,6 +362,8 @@ def main(argv=None) -> int:
     ap.add_argument("--kv-layout", choices=["NHD", "HND"], default="NHD",
                     help="memory order of the pool (HND: KV head before slot)")
     ap.add_argument("--block-size", type=int, default=None, help="page size override (a multiple of 16)")
+    ap.add_argument("--kv-dtype", choices=["same", "fp8_e4m3"], default=None,
+                    help="element type of the pool (default: the workload's; decode_e4m3 = decode + fp8_e4m3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -399,7 +401,7 @@ def main(argv=None) -> int:
         print(json.dumps(kvwrite_line(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
         return 0
     cfg = WORKLOADS[args.workload]
-    kv_dtype = KV_DTYPES.get(args.workload, "same")
+    kv_dtype = args.kv_dtype or KV_DTYPES.get(args.workload, "same")
     m = measure(cfg, args.steps, args.warmup, kv_dtype=kv_dtype, kv_layout=args.kv_layout,
                 block_size=args.block_size)
     batch, counts, t = m["batch"], m["counts"], m["timing"]
