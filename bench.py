@@ -141,6 +141,30 @@ def time_steps(db, steps: int, warmup: int) -> dict:
     }
 
 
+def time_graph(db, steps: int, warmup: int) -> float:
+    """ms per step when one forward is captured into a HIP graph
+    (torch.cuda.CUDAGraph) and replayed: the launch cost of the step's kernels
+    is paid once at capture."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        db.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        db.forward()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def _traffic(kernel_name: str, launches_per_step: int = 1):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     when it is missing or the kernel source changed since it was taken."""
@@ -364,6 +388,8 @@ def main(argv=None) -> int:
     ap.add_argument("--block-size", type=int, default=None, help="page size override (a multiple of 16)")
     ap.add_argument("--kv-dtype", choices=["same", "fp8_e4m3"], default=None,
                     help="element type of the pool (default: the workload's; decode_e4m3 = decode + fp8_e4m3)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured into a HIP graph and replayed (key 'graph')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -468,6 +494,10 @@ def main(argv=None) -> int:
         line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
         line["prefill_TFLOPs_step"] = round(counts["prefill_flops"] / (ms * 1e-3) / 1e12, 2)
     line["roofline"] = roof
+    if args.graph:
+        gms = time_graph(m["db"], args.steps, args.warmup)
+        line["graph"] = {"ms_per_step": round(gms, 5), "value": round(line["value"] * ms / gms, 2),
+                         "unit": line["unit"]}
     line["algorithmic"] = {k: counts[k] for k in ("decode_bytes", "prefill_flops", "decode_kv_tokens",
                                                   "prefill_tokens")}
 
