@@ -84,16 +84,20 @@ def _fp8_params(**kw):
 
 
 def test_e4m3_pool_plan_checks():
-    """An e4m3 pool is a plan property: bf16 queries only, a known kv_dtype, and
-    the general prefill tiling (the wide kernel reads bf16 pools only)."""
+    """An e4m3 pool is a plan property: bf16 queries only, a known kv_dtype; the
+    prefill tiling follows the head size as for bf16 pools (wide kernel at
+    d = 128, general kernel at d = 64)."""
     qsl, sl = [0, 1, 65], [40, 64]
     # group of 8: the wide kernel takes 4 heads x 32 positions per workgroup,
     # the general one 8 heads x 16 positions
-    plan = pa.pa_plan_create(_fp8_params(num_heads=16), qsl, sl, device=-1)
-    same = pa.pa_plan_create(_fp8_params(num_heads=16, kv_dtype="same"), qsl, sl, device=-1)
-    info, info_same = pa.pa_plan_get_info(plan), pa.pa_plan_get_info(same)
-    assert info["num_decodes"] == 1 and info["num_prefills"] == 1
-    assert (info["prefill_rows_per_item"], info_same["prefill_rows_per_item"]) == (16, 32)
+    rows = {}
+    for d in (128, 64):
+        for kvd in ("fp8_e4m3", "same"):
+            plan = pa.pa_plan_create(_fp8_params(num_heads=16, head_size=d, kv_dtype=kvd), qsl, sl, device=-1)
+            info = pa.pa_plan_get_info(plan)
+            assert info["num_decodes"] == 1 and info["num_prefills"] == 1
+            rows[d, kvd] = info["prefill_rows_per_item"]
+    assert rows == {(128, "fp8_e4m3"): 32, (128, "same"): 32, (64, "fp8_e4m3"): 16, (64, "same"): 16}
     for kw, status in ((dict(dtype="fp32"), pa.PA_ERR_UNSUPPORTED), (dict(kv_dtype=7), pa.PA_ERR_INVALID_ARG)):
         with pytest.raises(pa.PagedAttnError) as ei:
             pa.pa_plan_create(_fp8_params(**kw), qsl, sl, device=-1)
