@@ -231,7 +231,14 @@ struct KArgs {
   const float* k_scale;  // e4m3 pool: K / V scales, one (n_scales = 1) or one per KV head
   const float* v_scale;
   int n_scales;
+  int bs_log2;  // log2(bs) when bs is a power of two, else -1
 };
+
+// Page (block-table index) of key n >= 0: a shift when the page size is a
+// power of two, else an unsigned division.
+__device__ __forceinline__ int page_index(const KArgs& a, int n) {
+  return a.bs_log2 >= 0 ? (int)((unsigned)n >> a.bs_log2) : (int)((unsigned)n / (unsigned)a.bs);
+}
 
 // Scale of KV head kvh from a per-tensor (n = 1) or per-head scale array.
 __device__ __forceinline__ float kv_scale_of(const float* sc, int n, int kvh) { return sc[n > 1 ? kvh : 0]; }
@@ -365,7 +372,7 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
     // One physical block per 16-key tile.  Keys past kv_end are clamped to the
     // last valid key (so only pool rows of this sequence are read) and masked.
     // The block ids of the next step's two tiles are fetched during this step.
-    auto tile_block = [&](int t) { return min(t, kv_end - 1) / a.bs; };
+    auto tile_block = [&](int t) { return page_index(a, min(t, kv_end - 1)); };
     int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
     for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
       const KV* pb[2];
@@ -528,7 +535,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int key = min(kb + tid / CPR + j * RPI, kv_hi - 1);
-      const int blk = key / a.bs;
+      const int blk = page_index(a, key);
       const KV* base = kvh_base + (int64_t)btrow[blk] * blk_stride + (int64_t)(key - blk * a.bs) * slot_stride;
       stK[j] = reinterpret_cast<const u32x4*>(base)[chunk];
       stV[j] = reinterpret_cast<const u32x4*>(base + v_half)[chunk];
@@ -792,7 +799,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // physical block of this wave's slab of the block at key kb (its first key,
   // clamped); looked up one block ahead so the lookup's latency is covered by
   // the wait before the next barrier
-  auto page_of = [&](int kb) { return btrow[min(kb + RPW * wave, kv_hi - 1) / a.bs]; };
+  auto page_of = [&](int kb) { return btrow[page_index(a, min(kb + RPW * wave, kv_hi - 1))]; };
   // e4m3: this wave's slab of the next block, 16 codes per lane and load (row
   // 8 i + lane / 8 of the slab, codes 16 (lane % 8) .. +15): K in st8[0..1],
   // V in st8[2..3]
@@ -803,7 +810,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (F8) {
       // rows past the end re-read the last valid key (masked later); the
       // slab lies in one physical block
-      const int pst = min(key0, kv_hi - 1) / a.bs * a.bs;
+      const int pst = page_index(a, min(key0, kv_hi - 1)) * a.bs;
       const KV* page = kvh_base + (int64_t)pid * blk_stride;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -817,7 +824,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + RPW * wave * kWideRow;
     if (key0 + RPW - 1 < kv_hi) {
       // whole slab valid and inside one physical block: scalar base + lane offset
-      const int blk = key0 / a.bs;
+      const int blk = page_index(a, key0);
       const unsigned char* base = reinterpret_cast<const unsigned char*>(
           kvh_base + (int64_t)pid * blk_stride + (int64_t)(key0 - blk * a.bs) * slot_stride);
 #pragma unroll
@@ -831,7 +838,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     } else {
       // tail: rows past the end re-read the last valid key (masked later)
       const int ks = min(key0, kv_hi - 1);
-      const int blk = ks / a.bs;
+      const int blk = page_index(a, ks);
       const int pst = blk * a.bs;
       const KV* page = kvh_base + (int64_t)pid * blk_stride;
 #pragma unroll
@@ -1305,6 +1312,7 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   a.bs = g.bs;
   a.max_blocks = g.max_blocks;
   a.scale_log2 = g.scale_log2;
+  a.bs_log2 = (g.bs & (g.bs - 1)) == 0 ? __builtin_ctz((unsigned)g.bs) : -1;
   a.slot_stride = g.slot_stride;
   a.head_stride = g.head_stride;
   a.k_scale = t.k_scale;

@@ -165,16 +165,17 @@ def time_graph(db, steps: int, warmup: int) -> float:
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def _traffic(kernel_name: str, launches_per_step: int = 1):
+def _traffic(kernel_name: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when it is missing or the kernel source changed since it was taken."""
+    when it is missing, was taken on another workload, or the kernel source
+    changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     ent = data.get(kernel_name)
-    if not ent:
+    if not ent or ent.get("workload") != workload:
         return None
     with open(KERNEL_SRC, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
@@ -254,12 +255,13 @@ def _kernel(t, prefix):
     return None, None
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str, kernels=("decode_kernel",
-                  "prefill_wide_kernel", "merge_kernel")) -> dict:
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str, workload: str,
+                  kernels=("decode_kernel", "prefill_wide_kernel", "merge_kernel")) -> dict:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
-    dispatch) into HBM bytes per launch of each kernel, each counter scaled by
-    what it reads for the plain device copy of `copy_bytes` bytes in the same
-    run, and write them to profiles/traffic_counters.json."""
+    dispatch) of `bench.py --workload <workload>` into HBM bytes per launch of
+    each kernel, each counter scaled by what it reads for the plain device copy
+    of `copy_bytes` bytes in the same run, and write them to
+    profiles/traffic_counters.json."""
     import csv
 
     def per_dispatch(path, counter):
@@ -304,8 +306,9 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
             continue
         fb = fetch[name] * 1024.0 * f_scale
         wb = write[name] * 1024.0 * w_scale
-        res[f"{family}_{tag}"] = {"kernel": name, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
-                                  "bytes_per_launch": fb + wb, "kernel_source_sha256": sha, "calibration": calib}
+        res[f"{family}_{tag}"] = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fb,
+                                  "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
+                                  "kernel_source_sha256": sha, "calibration": calib}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     return res
@@ -400,10 +403,14 @@ def main(argv=None) -> int:
     ap.add_argument("--pmc-command", default="", help="command recorded with --summarize-pmc")
     ap.add_argument("--pmc-kernels", default="decode_kernel,prefill_wide_kernel,merge_kernel",
                     help="kernel families --summarize-pmc records (comma-separated)")
+    ap.add_argument("--pmc-workload", default="decode",
+                    help="the --workload of the profiled runs that --summarize-pmc reads (default workload "
+                         "options); the counters serve only lines of that workload")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
         res = summarize_pmc(*args.summarize_pmc, copy_bytes=args.copy_calibration_mib << 20,
-                            command=args.pmc_command, kernels=tuple(args.pmc_kernels.split(",")))
+                            command=args.pmc_command, workload=args.pmc_workload,
+                            kernels=tuple(args.pmc_kernels.split(",")))
         print(json.dumps(res, indent=1))
         return 0
     if args.gpus != 1:
@@ -433,6 +440,11 @@ def main(argv=None) -> int:
     batch, counts, t = m["batch"], m["counts"], m["timing"]
     ms = t["ms_per_step"]
     dtype = batch.dtype
+    # counters serve only a run of the workload they were taken on, with its
+    # default pool (element type, memory order, page size)
+    default_pool = (kv_dtype == KV_DTYPES.get(args.workload, "same") and args.kv_layout == "NHD"
+                    and args.block_size is None)
+    traffic_key = args.workload if default_pool else None
     line = {
         "metric": METRIC,
         "n_gpus": 1,
@@ -466,8 +478,7 @@ def main(argv=None) -> int:
                                "naive_bytes": counts["decode_bytes_naive"], "cascade_bytes": counts["decode_bytes"]}
         roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
-        tr = _traffic(kname, 1)
-        roof["traffic"] = tr
+        roof["traffic"] = _traffic(kname, traffic_key)
     elif counts["prefill_tokens"] and not counts["decode_seqs"]:
         bound = "mfma"
         value = counts["prefill_flops"] / (ms * 1e-3) / 1e12
@@ -476,7 +487,7 @@ def main(argv=None) -> int:
         ach = counts["prefill_flops"] / (k["avg_us"] * 1e-6) / 1e12
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": _traffic(kname, 1)}
+                "frac": round(ach / peak, 4), "traffic": _traffic(kname, traffic_key)}
     else:
         # mixed step: the roofline of the whole step is max(bytes/BW, flops/peak)
         peak = MFMA_PEAK_TFLOPS[dtype]
@@ -488,7 +499,7 @@ def main(argv=None) -> int:
         dec_ach = counts["decode_bytes"] / (d["avg_us"] * 1e-6) / 1e9 if d else 0.0
         pre_ach = counts["prefill_flops"] / (p["avg_us"] * 1e-6) / 1e12 if p else 0.0
         roof = {"bound": "hbm", "kernel": kd, "achieved": round(dec_ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dec_ach / HBM_PEAK_GBS, 4), "traffic": _traffic(kd, 1),
+                "frac": round(dec_ach / HBM_PEAK_GBS, 4), "traffic": _traffic(kd, traffic_key),
                 "prefill": {"kernel": kp, "achieved_TFLOPs": round(pre_ach, 2), "peak": peak,
                             "frac": round(pre_ach / peak, 4)}}
         line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
@@ -521,7 +532,7 @@ def main(argv=None) -> int:
             "roofline": {"bound": "mfma", "kernel": kp, "achieved": round(pf / (k["avg_us"] * 1e-6) / 1e12, 2),
                          "peak": MFMA_PEAK_TFLOPS["bf16"],
                          "frac": round(pf / (k["avg_us"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-                         "traffic": _traffic(kp, 1)},
+                         "traffic": _traffic(kp, "prefill")},
         }
         del p
     if not args.no_cpu_baseline:
