@@ -42,6 +42,13 @@ SMALL = {
                                       num_heads=6, num_kv_heads=2, head_size=128, block_size=16, seed=18),
     "noncausal_bf16_d128_g4": _mixed([1, 40, 7], [64, 100, 7], num_heads=8, num_kv_heads=2, head_size=128,
                                      block_size=16, seed=19, causal=False),
+    # page sizes that are not powers of two take the division path of the
+    # page lookups in the general prefill kernel too
+    "mixed_bf16_d64_g2_bs80": _mixed([1, 45, 1, 90], [300, 45, 81, 250],
+                                     num_heads=4, num_kv_heads=2, head_size=64, block_size=80, seed=20),
+    "mixed_fp32_d128_g2_bs48": _mixed([1, 33, 1], [100, 130, 49],
+                                      num_heads=4, num_kv_heads=2, head_size=128, block_size=48, dtype="fp32",
+                                      seed=21),
 }
 
 

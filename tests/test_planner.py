@@ -217,9 +217,47 @@ def test_balanced_decode_lists_partition_the_keys(seed):
     assert info["decode_tokens_read"] == int(lens.sum()) * 8
 
 
-def test_decode_lists_are_single_items_beside_prefills_or_with_a_split():
+def test_decode_lists_are_single_items_with_a_split_or_a_shared_prefix():
     lens = [100, 5000, 40, 700]
-    for qlens, split in (([1, 1, 16, 1], 0), ([1, 1, 1, 1], 64)):
-        plan, info = host_plan(qlens, lens, split=split)
+    bt = np.arange(4 * 313, dtype=np.int32).reshape(4, 313)
+    bt[:, :1] = bt[0, :1]
+    for qlens, kw in (([1, 1, 1, 1], dict(split=64)), ([1, 1, 16, 1], dict(prefix=16, block_table=bt, mbs=313))):
+        plan, info = host_plan(qlens, lens, **kw)
         lists, spans = _decode_schedule(plan, info)
         assert np.array_equal(lists, np.arange(len(spans) + 1)) and info["decode_list_tokens"] == 0
+
+
+def _covers_decodes_in_order(plan, lens, spans):
+    order = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER)
+    pos = 0
+    for b in order:
+        k = 0
+        while pos < len(spans) and spans[pos][0] == b:
+            assert spans[pos][1] == k and spans[pos][2] > k
+            k = spans[pos][2]
+            pos += 1
+        if k:
+            assert k == lens[b]
+    assert pos == len(spans)
+
+
+@pytest.mark.parametrize("heavy", ["decode", "prefill"])
+def test_decode_lists_beside_prefills_take_a_share_of_the_machine(heavy):
+    """Beside prefills the balanced lists take between a quarter and three
+    quarters of the resident wave groups (host plans: 256 CUs, one workgroup
+    of two waves per list at H=8, Hkv=2): close to three quarters when the
+    decodes dominate, fewer when the prefill does; the keys are still covered
+    once, in order."""
+    if heavy == "decode":
+        qlens, lens = [1] * 64 + [32], [8000] * 64 + [32]
+    else:
+        qlens, lens = [1] * 40 + [4096], [3000] * 40 + [4096]
+    plan, info = host_plan(qlens, lens)
+    lists, spans = _decode_schedule(plan, info)
+    n = info["num_decode_lists"]
+    assert info["decode_list_tokens"] > 0 and 64 <= n <= 192
+    if heavy == "decode":
+        assert n >= 180
+    else:
+        assert n <= 128
+    _covers_decodes_in_order(plan, np.asarray(lens), spans[:, :3])
