@@ -217,7 +217,12 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * std::max(num_cus, 1) * dec_nw / dec_units);
     if (np > 0) lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
-    list_tokens = (int)round_up(ceil_div(dec_tokens, n_lists), 32);
+    // A list is closed with up to 31 keys of room unused (cuts inside a
+    // sequence fall on multiples of 32), so each holds 32 keys more than the
+    // even share: every closed list then takes more than the share, and the
+    // keys never spill into lists beyond n_lists (which would run as a second,
+    // nearly empty round of workgroups).
+    list_tokens = (int)round_up(ceil_div(dec_tokens, n_lists), 32) + 32;
     split = list_tokens;
   } else if (split == 0) {
     const int64_t target_items = std::max<int64_t>(1, (int64_t)32 * std::max(num_cus, 1) / Hkv);

@@ -217,6 +217,28 @@ def test_balanced_decode_lists_partition_the_keys(seed):
     assert info["decode_tokens_read"] == int(lens.sum()) * 8
 
 
+def test_balanced_decode_lists_never_exceed_the_resident_groups():
+    """Each list may close with up to 31 keys of room unused (cuts inside a
+    sequence fall on 32-key boundaries); the planner sizes the lists so that
+    the keys still fit in one list per resident group of waves (host plans: 256
+    CUs, one 8-wave workgroup per CU at Hkv = 8), never spilling into a second
+    round.  The suffix lengths of the cascade batch (128 decodes, U[256, 2048])
+    once gave 258 lists."""
+    from workloads import config_lengths
+    _, L, sp = config_lengths(5)
+    suffix = [int(x) - 16 * sp for x in L]
+    cases = [suffix] + [list(np.random.default_rng(500 + s).integers(1, 4096, size=int(n)))
+                        for s, n in enumerate([37, 128, 255, 256, 257, 400, 1000])]
+    for lens in cases:
+        plan, info = host_plan([1] * len(lens), lens, H=32, Hkv=8)
+        lists, spans = _decode_schedule(plan, info)
+        need = -(-int(np.sum(lens)) // 256)
+        assert info["num_decode_lists"] <= min(256, need), (len(lens), info["num_decode_lists"])
+        W = info["decode_list_tokens"]
+        sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
+        assert sizes.sum() == int(np.sum(lens)) and np.all(sizes <= W) and np.all(sizes[:-1] > W - 32)
+
+
 def test_decode_lists_are_single_items_with_a_split_or_a_shared_prefix():
     lens = [100, 5000, 40, 700]
     bt = np.arange(4 * 313, dtype=np.int32).reshape(4, 313)
