@@ -174,7 +174,7 @@ def _traffic(kernel_name: str, workload: str):
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel_name)
+    ent = data.get(f"{kernel_name}@{workload}")
     if not ent or ent.get("workload") != workload:
         return None
     with open(KERNEL_SRC, "rb") as f:
@@ -306,7 +306,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
             continue
         fb = fetch[name] * 1024.0 * f_scale
         wb = write[name] * 1024.0 * w_scale
-        res[f"{family}_{tag}"] = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fb,
+        res[f"{family}_{tag}@{workload}"] = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fb,
                                   "write_bytes_per_launch": wb, "bytes_per_launch": fb + wb,
                                   "kernel_source_sha256": sha, "calibration": calib}
     with open(TRAFFIC_FILE, "w") as f:
@@ -521,7 +521,7 @@ def main(argv=None) -> int:
         line["data"] = "synthetic (seeded N(0,1) Q; random e4m3 codes and per-head scales; random page placement)"
     if args.workload == "decode" and not args.no_secondary:
         del m
-        p = measure(3, max(10, args.steps // 4), max(2, args.warmup // 2))
+        p = measure(3, args.steps, args.warmup)
         kp, k = _kernel(p["timing"], "prefill_")
         pf = p["counts"]["prefill_flops"]
         line["secondary"] = {

@@ -39,14 +39,14 @@ def test_summary_scales_by_the_largest_copy_and_binds_the_workload(tmp_path, tra
     _counter_csv(write, "WRITE_SIZE", [(COPY, 1, 1024 * 1024), (COPY, 2, 999),
                                        (DEC, 3, 20.0), (DEC, 4, 20.0), (MRG, 5, 4.0)])
     res = bench.summarize_pmc(str(fetch), str(write), copy_bytes=1024 * mib, command="cmd", workload="decode")
-    dec = res["decode_bf16_d128"]
+    dec = res["decode_bf16_d128@decode"]
     # per dispatch: 400 and 500 KiB fetched -> 450 KiB mean, halved by the calibration
     assert dec["fetch_bytes_per_launch"] == pytest.approx(450 * 1024 / 2)
     assert dec["write_bytes_per_launch"] == pytest.approx(20 * 1024)
     assert dec["bytes_per_launch"] == pytest.approx(450 * 512 + 20 * 1024)
-    assert dec["workload"] == "decode" and res["merge_bf16_d128"]["workload"] == "decode"
+    assert dec["workload"] == "decode" and res["merge_bf16_d128@decode"]["workload"] == "decode"
     assert res["_calibration"]["fetch_scale"] == pytest.approx(0.5)
-    assert json.loads(traffic_file.read_text())["decode_bf16_d128"]["kernel"] == DEC
+    assert json.loads(traffic_file.read_text())["decode_bf16_d128@decode"]["kernel"] == DEC
 
 
 def test_traffic_serves_only_its_workload_and_source(tmp_path, traffic_file, monkeypatch):
@@ -58,6 +58,10 @@ def test_traffic_serves_only_its_workload_and_source(tmp_path, traffic_file, mon
     assert full == pytest.approx(64 * 512 + 8 * 1024)
     # another workload's line (mixed step, cascade) or a non-default pool gets none
     assert bench._traffic("decode_bf16_d128", "mixed") is None
+    # counters of the same kernel on another workload sit beside, not over, these
+    bench.summarize_pmc(str(fetch), str(write), copy_bytes=1 << 19, command="", workload="cascade")
+    assert bench._traffic("decode_bf16_d128", "cascade") == pytest.approx(full / 2)
+    assert bench._traffic("decode_bf16_d128", "decode") == pytest.approx(full)
     assert bench._traffic("decode_bf16_d128", None) is None
     assert bench._traffic("prefill_bf16_d128", "prefill") is None
     # counters taken before the kernel source changed are not used
