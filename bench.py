@@ -114,7 +114,8 @@ def _batch_to_device(batch, common_prefix_len=None, kv_split_tokens=0):
                         num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
                         block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, causal=batch.causal,
                         common_prefix_len=cp, kv_split_tokens=kv_split_tokens, device="cuda:0",
-                        kv_dtype=batch.kv_dtype, k_scale=batch.k_scale, v_scale=batch.v_scale)
+                        kv_dtype=batch.kv_dtype, k_scale=batch.k_scale, v_scale=batch.v_scale,
+                        kv_layout=batch.kv_layout)
 
 
 def time_steps(db, steps: int, warmup: int) -> dict:
@@ -188,6 +189,46 @@ def _traffic(kernel_name: str, workload: str):
 # CPU baseline (the oracle, untuned, one thread)
 # ---------------------------------------------------------------------------
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name() -> str:
+    try:
+        b = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except (AttributeError, KeyError, TypeError):
+        return "unknown"
+
+
+def copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Bandwidth of a plain device-to-device copy of `nbytes` on this machine (bytes
+    read plus bytes written per second, best of `reps` event-timed copies): the
+    copy-kernel figure reported beside the spec peak."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return 2 * nbytes / best / 1e9
+
+
 def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
     """Time the oracle on a bounded sample of the same batch: whole sequences in
     a fixed random order until `budget_s` of CPU work; one BLAS thread."""
@@ -222,7 +263,8 @@ def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
             if t_total >= budget_s:
                 break
     res = {"cores": 1, "kind": "oracle", "seconds": round(t_total, 3),
-           "sample": f"{seqs} of {batch.num_seqs} sequences of the same batch (numpy float64, 1 thread)"}
+           "sample": f"{seqs} of {batch.num_seqs} sequences of the same batch (numpy float64, 1 thread)",
+           "cpu_model": _cpu_model(), "blas": _blas_name()}
     if counts["decode_seqs"] and done_bytes:
         res.update(value=done_bytes / t_total / 1e9, unit="GB/s")
     else:
@@ -246,6 +288,46 @@ def measure(cfg: int, steps: int, warmup: int, seed=None, kv_dtype: str = "same"
     info = pa.pa_plan_get_info(db.plan)
     t = time_steps(db, steps, warmup)
     return {"cfg": cfg, "batch": batch, "counts": counts, "timing": t, "plan": info, "db": db}
+
+
+def measure_sub_plans(m, steps: int, warmup: int) -> dict:
+    """The decode part and the prefill part of a mixed batch, each run as a plan
+    of its own over the same device pool: decode GB/s and prefill TFLOP/s
+    without the other part beside them."""
+    import attention_paged_kv_varlen_amd as pa
+    batch, db = m["batch"], m["db"]
+    qsl = batch.query_start_loc
+    ql = np.diff(qsl)
+    elem = 1 if batch.kv_dtype == "fp8_e4m3" else (2 if batch.dtype == "bf16" else 4)
+    res = {}
+    for tag, idx in (("decode_only", np.where(ql == 1)[0]), ("prefill_only", np.where(ql != 1)[0])):
+        if len(idx) == 0:
+            continue
+        rows = np.concatenate([np.arange(qsl[b], qsl[b + 1]) for b in idx])
+        sub_qsl = np.concatenate([[0], np.cumsum(ql[idx])]).astype(np.int32)
+        sub_L = np.ascontiguousarray(batch.seq_lens[idx])
+        sdb = pa.to_device(np.ascontiguousarray(batch.q[rows]), batch.kv_cache,
+                           np.ascontiguousarray(batch.block_table[idx]), sub_qsl, sub_L,
+                           num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads, head_size=batch.head_size,
+                           block_size=batch.block_size, dtype=batch.dtype, scale=batch.scale, causal=batch.causal,
+                           device="cuda:0", kv_cache_dev=db.kv_cache, kv_dtype=batch.kv_dtype,
+                           k_scale=batch.k_scale, v_scale=batch.v_scale, kv_layout=batch.kv_layout)
+        c = algorithmic_counts(ql[idx], sub_L, num_heads=batch.num_heads, num_kv_heads=batch.num_kv_heads,
+                               head_size=batch.head_size, elem_bytes=elem, causal=batch.causal)
+        t = time_steps(sdb, steps, warmup)
+        ms = t["ms_per_step"]
+        ent = {"ms_per_step": round(ms, 5), "kernels_us": {k: round(v["avg_us"], 3) for k, v in t["kernels"].items()}}
+        if tag == "decode_only":
+            _, k = _kernel(t, "decode_")
+            ent.update(value=round(c["decode_bytes"] / (ms * 1e-3) / 1e9, 2), unit="GB/s",
+                       kernel_GBps=round(c["decode_bytes"] / (k["avg_us"] * 1e-6) / 1e9, 2))
+        else:
+            _, k = _kernel(t, "prefill_")
+            ent.update(value=round(c["prefill_flops"] / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
+                       kernel_TFLOPs=round(c["prefill_flops"] / (k["avg_us"] * 1e-6) / 1e12, 2))
+        res[tag] = ent
+        del sdb
+    return res
 
 
 def _kernel(t, prefix):
@@ -504,7 +586,11 @@ def main(argv=None) -> int:
                             "frac": round(pre_ach / peak, 4)}}
         line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
         line["prefill_TFLOPs_step"] = round(counts["prefill_flops"] / (ms * 1e-3) / 1e12, 2)
+    if roof["bound"] == "hbm":
+        roof["copy_kernel_GBps"] = round(copy_gbs(), 1)
     line["roofline"] = roof
+    if counts["decode_seqs"] and counts["prefill_tokens"]:
+        line["sub_plans"] = measure_sub_plans(m, args.steps, args.warmup)
     if args.graph:
         gms = time_graph(m["db"], args.steps, args.warmup)
         line["graph"] = {"ms_per_step": round(gms, 5), "value": round(line["value"] * ms / gms, 2),
