@@ -1037,11 +1037,46 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (jb + 1 < nblk) block(I1{}, std::true_type{}, jb + 1);
   }
 
+  // Epilogue.  Tiles whose rows go straight to out (no partial record) pass
+  // through LDS, so that each row leaves as 16 whole 16-byte pieces (one
+  // store instruction covers four full 256-byte rows) instead of 32-byte
+  // pieces of sixteen rows.  The staging area is the stage the last block did
+  // not use: it was last read in block nblk - 2, which every wave finished
+  // before the last block's barrier, and no load fills it any more.  Each wave
+  // uses its own 8 KB (two tiles of 16 rows x 256 bytes, chunk c of row t at
+  // c ^ t), so no further barrier is needed.  (The e4m3 variant keeps the
+  // direct stores: the staging code makes its register allocation spill.)
+  unsigned char* ost = ((nblk & 1) ? lds1 : lds0) + wave * 8192;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const float l = xlane_sum(l_run[c]);
     const int pos = pos0[c] + r;
-    if (pos < it.nrows) write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l, omul);
+    const bool valid = pos < it.nrows;
+    const bool direct = !valid || a.row_pbase[it.row0 + pos] < 0;
+    if (!F8 && __all(direct)) {
+      const float inv = l > 0.f ? omul / l : 0.f;
+      unsigned char* tb = ost + c * 4096;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        // d = 16 dt + 4 qd .. +3: 16-byte chunk 2 dt + qd / 2, half qd % 2
+        const f32x4 v = o[c][dt] * inv;
+        *reinterpret_cast<u32x2*>(tb + r * 256 + 16 * ((2 * dt + (qd >> 1)) ^ r) + 8 * (qd & 1)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+      if (valid && qd == 0 && a.lse)
+        a.lse[(int64_t)(it.row0 + pos) * a.H + head] = l > 0.f ? (m_run[c] + log2f(l)) * kLn2 : -INFINITY;
+      const int j = lane & 15;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t = 4 * k + (lane >> 4);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(tb + t * 256 + 16 * (j ^ t));
+        if (pos0[c] + t < it.nrows)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) +
+                                    ((int64_t)(it.row0 + pos0[c] + t) * a.H + head) * D + 8 * j) = x;
+      }
+    } else if (valid) {
+      write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l, omul);
+    }
   }
 }
 
