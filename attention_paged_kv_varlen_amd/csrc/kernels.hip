@@ -923,10 +923,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const unsigned char* Kb = STAGE ? lds1 : lds0;
     const unsigned char* Vb = Kb + kWideBlk;
+    // a masked block whose second half lies wholly above the wave's last
+    // visible key skips that half (it would add exp2(-inf) = 0 everywhere)
+    const bool half1 = !MASKED || __builtin_amdgcn_readfirstlane(kb + 32 <= wave_max_lim ? 1 : 0);
     // s[h][c][j][i]: score of key kb + 32 h + 16 j + 4 qd + i for column r of tile c
     f32x4 s[2][2][2];
     static_for<2>([&](auto hh) {
       constexpr int h = decltype(hh)::value;
+      if (h == 1 && !half1) return;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
@@ -942,6 +946,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     });
     static_for<2>([&](auto hh) {
       constexpr int h = decltype(hh)::value;
+      if (h == 1 && !half1) return;
       float x[2][8], p[2][8];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
