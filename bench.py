@@ -476,7 +476,9 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured into a HIP graph and replayed (key 'graph')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill measurement in the decode line")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the extra measurements: the prefill in the decode line, the mixed line's "
+                         "sub-plans and the device-copy bandwidth")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
@@ -586,10 +588,12 @@ def main(argv=None) -> int:
                             "frac": round(pre_ach / peak, 4)}}
         line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
         line["prefill_TFLOPs_step"] = round(counts["prefill_flops"] / (ms * 1e-3) / 1e12, 2)
-    if roof["bound"] == "hbm":
+    # extra measurements (left out of profiled runs with --no-secondary, so that
+    # a kernel trace holds only the step's own launches)
+    if roof["bound"] == "hbm" and not args.no_secondary:
         roof["copy_kernel_GBps"] = round(copy_gbs(), 1)
     line["roofline"] = roof
-    if counts["decode_seqs"] and counts["prefill_tokens"]:
+    if counts["decode_seqs"] and counts["prefill_tokens"] and not args.no_secondary:
         line["sub_plans"] = measure_sub_plans(m, args.steps, args.warmup)
     if args.graph:
         gms = time_graph(m["db"], args.steps, args.warmup)
