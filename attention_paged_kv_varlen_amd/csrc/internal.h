@@ -153,7 +153,8 @@ inline int decode_waves_per_wg(int units) {
   while (units % nw != 0) --nw;
   return nw;
 }
-// Decode workgroups of `waves` waves that fit on one CU at once (kernels.hip;
+// Decode workgroups of `waves` waves that fit on one CU at once, for the
+// variant that balanced lists run (two steps in flight for bf16 queries; kernels.hip;
 // the device must be current), or 0 if the query fails.
 int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves);
 

@@ -303,6 +303,89 @@ __device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int
   }
 }
 
+// Raw K / V loads of the decode (one lane's share of a 16-key tile) and their
+// widening to the MFMA operand type.  bf16 / fp32 pools load the operand
+// directly; e4m3 pools load codes (K: D/4 contiguous codes, 16 per load; V:
+// VE codes of one key row) that are widened to bf16 in registers.
+template <typename KV, int D, int KS>
+struct RawKOf {
+  typename Ops<KV, D / 16>::Frag f[KS];
+};
+template <int D, int KS>
+struct RawKOf<uint8_t, D, KS> {
+  u32x4 w[KS / 2];
+};
+template <typename KV, int VE>
+struct RawVOf {
+  typename Ops<KV, VE>::VRaw v;
+};
+template <int VE>
+struct RawVOf<uint8_t, VE> {
+  uint32_t w[VE / 4];
+};
+
+template <typename KV, int D, int KS>
+__device__ __forceinline__ RawKOf<KV, D, KS> load_k_raw(const KV* kp) {
+  RawKOf<KV, D, KS> r;
+  if constexpr (std::is_same<KV, uint8_t>::value) {
+#pragma unroll
+    for (int j = 0; j < KS / 2; ++j) r.w[j] = *reinterpret_cast<const u32x4*>(kp + 16 * j);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) r.f[kk] = Ops<KV, D / 16>::load(kp + 32 * kk);
+  }
+  return r;
+}
+
+template <typename KV, int VE>
+__device__ __forceinline__ RawVOf<KV, VE> load_v_raw(const KV* vp) {
+  RawVOf<KV, VE> r;
+  if constexpr (std::is_same<KV, uint8_t>::value) {
+    if constexpr (VE == 8) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(vp);
+      r.w[0] = w[0];
+      r.w[1] = w[1];
+    } else {
+      r.w[0] = *reinterpret_cast<const uint32_t*>(vp);
+    }
+  } else {
+    r.v = Ops<KV, VE>::load_v(vp);
+  }
+  return r;
+}
+
+template <typename T, typename KV, int D, int KS>
+__device__ __forceinline__ void widen_k(const RawKOf<KV, D, KS>& r, typename Ops<T, D / 16>::Frag (&kf)[KS]) {
+  if constexpr (std::is_same<KV, uint8_t>::value) {
+#pragma unroll
+    for (int j = 0; j < KS / 2; ++j) {
+      kf[2 * j] = typename Ops<T, D / 16>::Frag{e4m3x8_to_bf16(r.w[j][0], r.w[j][1])};
+      kf[2 * j + 1] = typename Ops<T, D / 16>::Frag{e4m3x8_to_bf16(r.w[j][2], r.w[j][3])};
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) kf[kk] = r.f[kk];
+  }
+}
+
+template <typename T, typename KV, int VE>
+__device__ __forceinline__ typename Ops<T, VE>::VRaw widen_v(const RawVOf<KV, VE>& r) {
+  if constexpr (std::is_same<KV, uint8_t>::value) {
+    typename Ops<T, VE>::VRaw v;
+    if constexpr (VE == 8) {
+      const u32x4 b = e4m3x8_to_bf16(r.w[0], r.w[1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v.w[j] = b[j];
+    } else {
+      v.w[0] = e4m3x2_to_bf16x2<false>(r.w[0]);
+      v.w[1] = e4m3x2_to_bf16x2<true>(r.w[0]);
+    }
+    return v;
+  } else {
+    return r.v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode: one wave per work item (a KV range of one sequence for one KV head);
 // the columns are the query heads of that KV head (up to 16 per head group).
@@ -310,7 +393,7 @@ __device__ __forceinline__ void write_column(const KArgs& a, int row, int h, int
 // which are widened to bf16 in registers; the K scale joins the softmax scale
 // and the V scale multiplies the output.
 // ---------------------------------------------------------------------------
-template <typename T, typename KV, int D>
+template <typename T, typename KV, int D, bool DB>
 __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
   constexpr bool F8 = std::is_same<KV, uint8_t>::value;
   static_assert(!F8 || std::is_same<T, uint16_t>::value, "e4m3 pools take bf16 queries");
@@ -319,6 +402,8 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
   using O = Ops<T, VE>;
   using Frag = typename O::Frag;
   using VRaw = typename O::VRaw;
+  using RawK = RawKOf<KV, D, KS>;
+  using RawV = RawVOf<KV, VE>;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -371,62 +456,39 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 
     // One physical block per 16-key tile.  Keys past kv_end are clamped to the
     // last valid key (so only pool rows of this sequence are read) and masked.
-    // The block ids of the next step's two tiles are fetched during this step.
+    // A step is 32 keys.  With DB (bf16 queries; the launch leaves it off
+    // beside a shared-prefix pass, whose decode items are short) two steps are
+    // in flight: the raw K/V loads of step t + 32 are issued before the
+    // arithmetic of step t (the steps alternate between two register sets, so
+    // nothing is copied); the block ids of the step after that are fetched
+    // meanwhile.
     auto tile_block = [&](int t) { return page_index(a, min(t, kv_end - 1)); };
-    int pid[2] = {btrow[tile_block(it.kv_begin)], btrow[tile_block(it.kv_begin + 16)]};
-    for (int t0 = it.kv_begin; t0 < kv_end; t0 += 32) {
-      const KV* pb[2];
-      int pst[2];
+    struct Raw {
+      RawK k[2];
+      RawV v[8];
+    };
+    auto load_step = [&](int t0, const int (&pid)[2], Raw& w) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        pst[tt] = tile_block(t0 + 16 * tt) * a.bs;
-        pb[tt] = kvh_base + (int64_t)__builtin_amdgcn_readfirstlane(pid[tt]) * blk_stride;
-      }
-      Frag kf[2][KS];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+        const int pst = tile_block(t0 + 16 * tt) * a.bs;
+        const KV* pb = kvh_base + (int64_t)__builtin_amdgcn_readfirstlane(pid[tt]) * blk_stride;
         const int key = min(t0 + 16 * tt + r, kv_end - 1);
-        if constexpr (F8) {
-          // D/4 contiguous codes, 16 per load (two k-steps)
-          const KV* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + (D / 4) * qd;
+        const KV* kp = pb + (int64_t)(key - pst) * slot_stride + (F8 ? (D / 4) * qd : 8 * qd);
+        w.k[tt] = load_k_raw<KV, D, KS>(kp);
 #pragma unroll
-          for (int j = 0; j < KS / 2; ++j) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 16 * j);
-            kf[tt][2 * j] = Frag{e4m3x8_to_bf16(w[0], w[1])};
-            kf[tt][2 * j + 1] = Frag{e4m3x8_to_bf16(w[2], w[3])};
-          }
-        } else {
-          const KV* kp = pb[tt] + (int64_t)(key - pst[tt]) * slot_stride + 8 * qd;
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) kf[tt][kk] = O::load(kp + 32 * kk);
+        for (int e = 4 * tt; e < 4 * tt + 4; ++e) {
+          const int vkey = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
+          w.v[e] = load_v_raw<KV, VE>(pb + v_half + (int64_t)(vkey - pst) * slot_stride + VE * r);
         }
       }
+    };
+    auto compute_step = [&](int t0, const Raw& w) {
+      Frag kf[2][KS];
       VRaw vr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tt = e >> 2;
-        const int key = min(t0 + 16 * tt + 4 * qd + (e & 3), kv_end - 1);
-        const KV* vp = pb[tt] + v_half + (int64_t)(key - pst[tt]) * slot_stride + VE * r;
-        if constexpr (F8) {
-          if constexpr (VE == 8) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(vp);
-            const u32x4 b = e4m3x8_to_bf16(w[0], w[1]);
+      for (int tt = 0; tt < 2; ++tt) widen_k<T, KV, D, KS>(w.k[tt], kf[tt]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vr[e].w[j] = b[j];
-          } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
-            vr[e].w[0] = e4m3x2_to_bf16x2<false>(w);
-            vr[e].w[1] = e4m3x2_to_bf16x2<true>(w);
-          }
-        } else {
-          vr[e] = O::load_v(vp);
-        }
-      }
-      if (t0 + 32 < kv_end) {
-        pid[0] = btrow[tile_block(t0 + 32)];
-        pid[1] = btrow[tile_block(t0 + 48)];
-      }
-
+      for (int e = 0; e < 8; ++e) vr[e] = widen_v<T, KV, VE>(w.v[e]);
       f32x4 s[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -450,6 +512,44 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
         const Frag vf = O::template vtrans<dt>(vr);
         O::mma(o[dt], vf, pf);
       });
+    };
+    const int kb0 = it.kv_begin;
+    int pid[2] = {btrow[tile_block(kb0)], btrow[tile_block(kb0 + 16)]};
+    if constexpr (DB) {
+      static_assert(sizeof(T) == 2, "two steps in flight are built for bf16 queries");
+      Raw wa, wb;
+      int pidb[2] = {0, 0};
+      load_step(kb0, pid, wa);
+      if (kb0 + 32 < kv_end) {
+        pidb[0] = btrow[tile_block(kb0 + 32)];
+        pidb[1] = btrow[tile_block(kb0 + 48)];
+      }
+      for (int t0 = kb0; t0 < kv_end; t0 += 64) {
+        const bool has_b = t0 + 32 < kv_end;
+        if (has_b) load_step(t0 + 32, pidb, wb);
+        if (t0 + 64 < kv_end) {
+          pid[0] = btrow[tile_block(t0 + 64)];
+          pid[1] = btrow[tile_block(t0 + 80)];
+        }
+        compute_step(t0, wa);
+        if (!has_b) break;
+        if (t0 + 64 < kv_end) load_step(t0 + 64, pid, wa);
+        if (t0 + 96 < kv_end) {
+          pidb[0] = btrow[tile_block(t0 + 96)];
+          pidb[1] = btrow[tile_block(t0 + 112)];
+        }
+        compute_step(t0 + 32, wb);
+      }
+    } else {
+      for (int t0 = kb0; t0 < kv_end; t0 += 32) {
+        Raw w;
+        load_step(t0, pid, w);
+        if (t0 + 32 < kv_end) {
+          pid[0] = btrow[tile_block(t0 + 32)];
+          pid[1] = btrow[tile_block(t0 + 48)];
+        }
+        compute_step(t0, w);
+      }
     }
 
     l_run += __shfl_xor(l_run, 16);
@@ -1411,7 +1511,12 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     d.lists = s.decode_lists;
     const int64_t nwg = (int64_t)s.n_decode_lists * (nhg / nw);
     if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-    err = launch(name, decode_kernel<T, KV, D>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
+    if constexpr (sizeof(T) == 2) {
+      err = s.n_prefix > 0 ? launch(name, decode_kernel<T, KV, D, false>, dim3((unsigned)nwg), dim3(64 * nw), stream, d)
+                           : launch(name, decode_kernel<T, KV, D, true>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
+    } else {
+      err = launch(name, decode_kernel<T, KV, D, false>, dim3((unsigned)nwg), dim3(64 * nw), stream, d);
+    }
     if (err) return err;
   }
   if (fork) {
@@ -1449,17 +1554,17 @@ int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves) 
   const int threads = 64 * waves;
   const bool f8 = kv_dtype == PA_KV_FP8_E4M3;
   if (dtype == PA_BF16 && f8 && head_size == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 128>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 128, true>, threads, 0);
   else if (dtype == PA_BF16 && f8 && head_size == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 64>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint8_t, 64, true>, threads, 0);
   else if (dtype == PA_BF16 && head_size == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 128>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 128, true>, threads, 0);
   else if (dtype == PA_BF16 && head_size == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 64>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<uint16_t, uint16_t, 64, true>, threads, 0);
   else if (dtype == PA_FP32 && head_size == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 128>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 128, false>, threads, 0);
   else if (dtype == PA_FP32 && head_size == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 64>, threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 64, false>, threads, 0);
   return e == hipSuccess ? n : 0;
 }
 
