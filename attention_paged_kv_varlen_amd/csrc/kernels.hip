@@ -588,12 +588,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the KV-head group is the fastest-varying workgroup index (see launch_prefill)
+  // within an item the KV head is the fastest-varying workgroup index, then
+  // the head group (see launch_prefill)
   const int nhg = a.Hkv * a.head_groups;
   const int hgi = (int)(blockIdx.x % (unsigned)nhg);
   const WorkItem it = a.items[blockIdx.x / (unsigned)nhg];
-  const int kvh = hgi / a.head_groups;
-  const int hgrp = hgi % a.head_groups;
+  const int kvh = hgi % a.Hkv;
+  const int hgrp = hgi / a.Hkv;
   const int r = lane & 15, qd = lane >> 4;
 
   const T* q = static_cast<const T*>(a.q);
@@ -846,12 +847,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // the KV-head group is the fastest-varying workgroup index (see launch_prefill)
+  // within an item the KV head is the fastest-varying workgroup index, then
+  // the head group (see launch_prefill)
   const int nhg = a.Hkv * a.head_groups;
   const int hgi = (int)(blockIdx.x % (unsigned)nhg);
   const WorkItem it = a.items[blockIdx.x / (unsigned)nhg];
-  const int kvh = hgi / a.head_groups;
-  const int hgrp = hgi % a.head_groups;
+  const int kvh = hgi % a.Hkv;
+  const int hgrp = hgi / a.Hkv;
   const int r = lane & 15, qd = lane >> 4;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const KV* kv = static_cast<const KV*>(a.kv);
@@ -1415,9 +1417,10 @@ int launch(const char* name, K kernel, dim3 grid, dim3 block, void* stream, Args
 }
 
 // Prefill-type launches use a 1-D grid of n_items x (Hkv x head_groups)
-// workgroups with the head group varying fastest.  Workgroups go to the eight
-// XCDs round-robin by linear index, so with 8 | Hkv x head_groups every XCD
-// serves a fixed set of KV heads and the pages of one KV head stay in one L2.
+// workgroups; within an item the KV head varies fastest, then the head group.
+// Workgroups go to the eight XCDs round-robin by linear index, so with 8 | Hkv
+// every XCD serves a fixed set of KV heads with all their head groups, and the
+// pages of one KV head stay in one L2.
 template <typename T, typename KV, int D>
 int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) {
   const int64_t n = (int64_t)n_items * p.Hkv * p.head_groups;
