@@ -41,7 +41,7 @@ static_assert(sizeof(MergeRow) == 16, "MergeRow layout");
 // Tile j holds head (j / tiles_per_head) of the workgroup's head group and
 // positions 16 * (j % tiles_per_head) .. +15.
 struct PrefillShape {
-  int tiles;           // column tiles per workgroup (8)
+  int tiles;           // column tiles per workgroup (8, or 16 for the 8-wave wide prefill)
   int heads_per_wg;    // 1, 2, 4 or 8, divides g, at most max_heads
   int tiles_per_head;  // tiles / heads_per_wg
   int rows_per_item;   // 16 * tiles_per_head
@@ -49,10 +49,19 @@ struct PrefillShape {
 };
 PrefillShape prefill_shape(int group, int tiles, int max_heads);
 // The wide prefill kernel serves bf16 queries with head size 128 (bf16 or
-// e4m3 pool): 4 waves, 8 column tiles per workgroup, both tiles of a wave on
-// one head.
+// e4m3 pool): 4 waves, 8 column tiles per workgroup (8 waves and 16 tiles
+// beside decodes, see wide_prefill_tiles), both tiles of a wave on one head.
 inline bool use_wide_prefill(int dtype, int head_size, int kv_dtype) {
   return dtype == PA_BF16 && head_size == 128 && (kv_dtype == PA_KV_SAME || kv_dtype == PA_KV_FP8_E4M3);
+}
+// Column tiles per wide-prefill workgroup.  Beside decodes (and without a
+// shared prefix) a bf16 pool's prefill runs 8-wave workgroups, each filling
+// the register file of its CU: a 4-wave prefill workgroup leaves a CU half
+// empty yet too full for an 8-wave decode workgroup, so the decode would get
+// fewer CUs.  Otherwise 4-wave workgroups, two per CU, whose independent
+// barriers let one's softmax overlap the other's MFMAs.
+inline int wide_prefill_tiles(bool beside_decodes, int common_prefix_len, int kv_dtype) {
+  return beside_decodes && common_prefix_len == 0 && kv_dtype == PA_KV_SAME ? 16 : 8;
 }
 
 // Everything the kernels need besides the caller's tensors.

@@ -814,9 +814,11 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
   }
 }
 
-// Workgroup of 4 waves, two workgroups per CU (their barriers are independent,
-// so one workgroup's softmax overlaps the other's MFMAs); each wave owns two
-// column tiles of one head.  A 64-key LDS block is processed as two 32-key
+// Workgroup of NW = 4 waves, two workgroups per CU (their barriers are
+// independent, so one workgroup's softmax overlaps the other's MFMAs), or of
+// NW = 8 waves, one per CU, when the prefill runs beside decodes (a 4-wave
+// workgroup would leave its CU half empty yet unable to take an 8-wave decode
+// workgroup); each wave owns two column tiles of one head.  A 64-key LDS block is processed as two 32-key
 // halves.  Exponentials are taken speculatively against the running max m (no
 // cross-lane reduction): when no lane sees x * scale - m above the lazy
 // threshold the values stand; otherwise (the first half of every item, and
@@ -830,10 +832,10 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
 // end, after the block's own reads of the other stage; everything that reads
 // LDS is unchanged.  The K scale joins the softmax scale, the V scale
 // multiplies the output.
-template <bool F8>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+template <bool F8, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
   using KV = std::conditional_t<F8, uint8_t, uint16_t>;
-  constexpr int NW = 4;
+  static_assert(NW == 4 || (NW == 8 && !F8), "4 waves, or 8 waves over a bf16 pool");
   constexpr int RPW = kWideKT / NW;  // block rows each wave loads: one 16-key tile
   constexpr int D = 128, VE = 8, KS = 4;
   using O = Ops<uint16_t, VE>;
@@ -1151,9 +1153,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // not use: it was last read in block nblk - 2, which every wave finished
   // before the last block's barrier, and no load fills it any more.  Each wave
   // uses its own 8 KB (two tiles of 16 rows x 256 bytes, chunk c of row t at
-  // c ^ t), so no further barrier is needed.  (The e4m3 variant keeps the
+  // c ^ t; with 8 waves 4 KB, one tile after the other), so no further
+  // barrier is needed.  (The e4m3 variant keeps the
   // direct stores: the staging code makes its register allocation spill.)
-  unsigned char* ost = ((nblk & 1) ? lds1 : lds0) + wave * 8192;
+  unsigned char* ost = ((nblk & 1) ? lds1 : lds0) + wave * (NW == 4 ? 8192 : 4096);
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const float l = xlane_sum(l_run[c]);
@@ -1162,7 +1165,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool direct = !valid || a.row_pbase[it.row0 + pos] < 0;
     if (!F8 && __all(direct)) {
       const float inv = l > 0.f ? omul / l : 0.f;
-      unsigned char* tb = ost + c * 4096;
+      unsigned char* tb = ost + (NW == 4 ? c * 4096 : 0);  // 8 waves: one tile at a time
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         // d = 16 dt + 4 qd .. +3: 16-byte chunk 2 dt + qd / 2, half qd % 2
@@ -1428,11 +1431,12 @@ int launch_prefill(const char* name, int n_items, void* stream, const KArgs& p) 
   const dim3 grid((unsigned)n);
   if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint16_t>::value && D == 128)
   {
-    return launch(name, prefill_wide_kernel<false>, grid, dim3(256), stream, p);
+    if (p.tiles_per_wg == 16) return launch(name, prefill_wide_kernel<false, 8>, grid, dim3(512), stream, p);
+    return launch(name, prefill_wide_kernel<false, 4>, grid, dim3(256), stream, p);
   }
   else if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint8_t>::value && D == 128)
   {
-    return launch(name, prefill_wide_kernel<true>, grid, dim3(256), stream, p);
+    return launch(name, prefill_wide_kernel<true, 4>, grid, dim3(256), stream, p);
   }
   else
     return launch(name, prefill_kernel<T, KV, D>, grid, dim3(256), stream, p);

@@ -189,7 +189,12 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
 
   // ---- schedule
   // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
-  hp.ps = use_wide_prefill(p.dtype, p.head_size, p.kv_dtype) ? prefill_shape(g, 8, 4) : prefill_shape(g, 8, 8);
+  if (use_wide_prefill(p.dtype, p.head_size, p.kv_dtype)) {
+    const int tiles = wide_prefill_tiles(nd > 0, P, p.kv_dtype);
+    hp.ps = prefill_shape(g, tiles, tiles / 2);
+  } else {
+    hp.ps = prefill_shape(g, 8, 8);
+  }
   const int QB = hp.ps.rows_per_item;
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;

@@ -73,6 +73,31 @@ def test_split_items_cover_each_decode_exactly():
         assert list(parts) == [n if n > 1 else 0 for n in want]
 
 
+def test_wide_prefill_takes_eight_waves_beside_decodes():
+    """bf16 pool, head size 128, g = 4: a prefill alone runs 4-wave workgroups
+    of 8 column tiles (32 positions of 4 heads); beside decodes, 8-wave
+    workgroups of 16 tiles (64 positions), which fill a CU each; a shared
+    prefix keeps the 4-wave shape, and so do an e4m3 pool and fp32 queries."""
+    _, alone = host_plan([100], [100])
+    _, mixed = host_plan([1, 100], [300, 100])
+    assert alone["prefill_rows_per_item"] == 32 and mixed["prefill_rows_per_item"] == 64
+    bt = np.zeros((2, 20), dtype=np.int32)
+    bt[1, 1:] = np.arange(1, 20)
+    _, casc = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
+    assert casc["prefill_rows_per_item"] == 32
+    _, f32 = host_plan([1, 100], [300, 100], dtype="fp32")
+    assert f32["prefill_rows_per_item"] == 32
+    params = pa.make_params(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=40,
+                            max_blocks_per_seq=20, dtype="bf16", scale=0.1, kv_dtype="fp8_e4m3")
+    plan = pa.pa_plan_create(params, np.array([0, 1, 101], np.int32), np.array([300, 100], np.int32), device=-1)
+    assert pa.pa_plan_get_info(plan)["prefill_rows_per_item"] == 32
+    # g = 8: 8 heads x 32 positions beside decodes, 4 heads x 32 positions alone
+    _, m8 = host_plan([1, 100], [300, 100], H=16, Hkv=2)
+    _, a8 = host_plan([100], [100], H=16, Hkv=2)
+    assert m8["prefill_rows_per_item"] == 32 and m8["prefill_head_groups"] == 1
+    assert a8["prefill_rows_per_item"] == 32 and a8["prefill_head_groups"] == 2
+
+
 def test_prefill_reads_follow_the_causal_staircase():
     # one 100-token prompt, g = 4: the work item for positions [i0, i0 + Q) reads
     # keys 0 .. i0 + Q - 1 (capped at 100), where Q is the item's position count.
