@@ -892,9 +892,11 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
     pos0[c] = 16 * ((2 * wave + c) % a.tiles_per_head);
     const int pos = pos0[c] + r;
     const bool valid = pos < it.nrows;
+    // Q rows and output rows are touched once: non-temporal hints
     const uint16_t* qp = q + ((int64_t)(it.row0 + (valid ? pos : 0)) * a.H + head) * D + 8 * qd;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[c][kk] = valid ? O::load(qp + 32 * kk) : O::zero();
+    for (int kk = 0; kk < KS; ++kk)
+      qf[c][kk] = valid ? Frag{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + 32 * kk))} : O::zero();
     lim[c] = it.causal ? it.lim0 + pos : kv_hi - 1;
     tmin[c] = it.causal ? it.lim0 + pos0[c] : kv_hi - 1;
     if (pos0[c] < it.nrows)
@@ -1200,8 +1202,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
         const int t = 4 * k + (lane >> 4);
         const u32x4 x = *reinterpret_cast<const u32x4*>(tb + t * 256 + 16 * (j ^ t));
         if (pos0[c] + t < it.nrows)
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) +
-                                    ((int64_t)(it.row0 + pos0[c] + t) * a.H + head) * D + 8 * j) = x;
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) +
+                                                                  ((int64_t)(it.row0 + pos0[c] + t) * a.H + head) * D + 8 * j));
       }
     } else if (valid) {
       write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l, omul);
