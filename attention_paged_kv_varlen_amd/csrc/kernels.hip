@@ -1356,21 +1356,26 @@ __global__ void __launch_bounds__(256) write_kv_kernel(const unsigned char* k, c
                                                        const int64_t* slots, int n_tok, int Hkv, int head_bytes,
                                                        int bs, int64_t n_slots, int64_t slot_bstride,
                                                        int64_t head_bstride, unsigned char* kv) {
+  // one workgroup per token: its slot is read once (a scalar), and the
+  // workgroup's threads walk the 16-byte chunks of the token's K row, then
+  // of its V row; both are touched once, so the loads and stores carry the
+  // non-temporal hint
+  const int t = (int)blockIdx.x;
+  if (t >= n_tok) return;
   const int row_bytes = Hkv * head_bytes;
   const int chunks = row_bytes / 16;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)n_tok * 2 * chunks) return;
-  const int t = (int)(i / (2 * chunks));
-  const int c = (int)(i % (2 * chunks));
-  const int half = c / chunks;
-  const int off = (c % chunks) * 16;
   const int64_t s = slots[t];
   if (s < 0 || s >= n_slots) return;
   const int64_t blk = s / bs, in = s % bs;
-  const unsigned char* src = (half ? v : k) + (int64_t)t * row_bytes + off;
-  unsigned char* dst = kv + (blk * 2 + half) * bs * (int64_t)row_bytes + (off / head_bytes) * head_bstride +
-                       in * slot_bstride + off % head_bytes;
-  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  for (int c = (int)threadIdx.x; c < 2 * chunks; c += (int)blockDim.x) {
+    const int half = c >= chunks ? 1 : 0;
+    const int off = (c - half * chunks) * 16;
+    const unsigned char* src = (half ? v : k) + (int64_t)t * row_bytes + off;
+    unsigned char* dst = kv + (blk * 2 + half) * bs * (int64_t)row_bytes + (off / head_bytes) * head_bstride +
+                         in * slot_bstride + off % head_bytes;
+    __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)),
+                                reinterpret_cast<u32x4*>(dst));
+  }
 }
 
 // Quantising cache write into an e4m3 pool: one thread per 16 elements of a
@@ -1606,10 +1611,8 @@ int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves) 
 
 int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int head_bytes, int bs,
                     int64_t n_slots, int64_t slot_bstride, int64_t head_bstride, void* kv, void* stream) {
-  const int64_t n = (int64_t)n_tok * 2 * (Hkv * head_bytes / 16);
-  const int64_t nblk = (n + 255) / 256;
-  if (nblk > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-  return launch("write_kv", write_kv_kernel, dim3((unsigned)nblk), dim3(256), stream,
+  if (n_tok <= 0) return 0;
+  return launch("write_kv", write_kv_kernel, dim3((unsigned)n_tok), dim3(256), stream,
                 static_cast<const unsigned char*>(k), static_cast<const unsigned char*>(v), slots, n_tok, Hkv,
                 head_bytes, bs, n_slots, slot_bstride, head_bstride, static_cast<unsigned char*>(kv));
 }
