@@ -396,10 +396,11 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
     return res
 
 
-def kvwrite_line(steps: int, warmup: int, cpu: bool) -> dict:
+def kvwrite_line(steps: int, warmup: int, cpu: bool, kv_dtype: str = "same") -> dict:
     """The cache write on its own: every token of the causal varlen prefill batch
     (a fresh K and V row each) written to its slot.  HBM-bound: each row is read
-    once and written once."""
+    once and written once (into an e4m3 pool: bf16 rows read, one-byte codes
+    written, with per-head K/V scales)."""
     import torch
 
     import attention_paged_kv_varlen_amd as pa
@@ -420,24 +421,35 @@ def kvwrite_line(steps: int, warmup: int, cpu: bool) -> dict:
     tk = torch.from_numpy(k).view(torch.bfloat16).to(dev)
     tv = torch.from_numpy(v).view(torch.bfloat16).to(dev)
     ts = torch.from_numpy(slots).to(dev)
-    pool = torch.from_numpy(batch.kv_cache).view(torch.bfloat16).to(dev)
+    f8 = kv_dtype == "fp8_e4m3"
     params = pa.make_params(num_seqs=batch.num_seqs, num_heads=batch.num_heads, num_kv_heads=Hkv, head_size=d,
                             block_size=bs, num_blocks=batch.num_blocks, max_blocks_per_seq=batch.max_blocks_per_seq,
-                            dtype="bf16", scale=batch.scale)
+                            dtype="bf16", scale=batch.scale, kv_dtype=kv_dtype)
+    if f8:
+        pool = torch.zeros(batch.kv_cache.shape, dtype=torch.uint8, device=dev)
+        ksc = torch.from_numpy(rng.uniform(0.005, 0.007, size=Hkv).astype(np.float32)).to(dev)
+        vsc = torch.from_numpy(rng.uniform(0.005, 0.007, size=Hkv).astype(np.float32)).to(dev)
+        write = lambda st: pa.pa_write_kv_fp8(tk, tv, ts, T, params, ksc, vsc, pool, stream=st)  # noqa: E731
+        kname = "write_kv_e4m3"
+    else:
+        pool = torch.from_numpy(batch.kv_cache).view(torch.bfloat16).to(dev)
+        write = lambda st: pa.pa_write_kv(tk, tv, ts, T, params, pool, st)  # noqa: E731
+        kname = "write_kv"
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        pa.pa_write_kv(tk, tv, ts, T, params, pool, stream)
+        write(stream)
     torch.cuda.synchronize()
     pa.pa_profile_start(steps + 8)
     t0 = time.perf_counter()
     for _ in range(steps):
-        pa.pa_write_kv(tk, tv, ts, T, params, pool, stream)
+        write(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     kern = pa.pa_profile_stop()
     us = {x["name"]: 1e3 * x["total_ms"] / max(x["launches"], 1) for x in kern}
-    nbytes = 2 * T * 2 * Hkv * d * 2  # K and V rows, read once and written once
-    ach = nbytes / (us["write_kv"] * 1e-6) / 1e9
+    # K and V rows read once (bf16) and written once (bf16, or one-byte codes)
+    nbytes = T * 2 * Hkv * d * (2 + (1 if f8 else 2))
+    ach = nbytes / (us[kname] * 1e-6) / 1e9
     line = {
         "metric": "KV-cache write GB/s (% HBM peak)", "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
@@ -445,19 +457,28 @@ def kvwrite_line(steps: int, warmup: int, cpu: bool) -> dict:
         "config": {"workload": f"cache write of the {T} tokens of the causal varlen prefill batch "
                                f"({Hkv} kv heads, d={d}, bs={bs}, random page placement)", "num_tokens": T},
         "kernels_us": {n: round(x, 3) for n, x in us.items()},
-        "roofline": {"bound": "hbm", "kernel": "write_kv", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
         "algorithmic": {"bytes": nbytes},
     }
+    if f8:
+        line["config"]["workload"] = line["config"]["workload"].replace("cache write", "cache write into an e4m3 pool")
+        line["config"]["kv_dtype"] = kv_dtype
     if cpu:
         import oracle
         n = min(T, 4096)
-        host_pool = batch.kv_cache
         t1 = time.perf_counter()
-        oracle.write_kv(host_pool, k[:n], v[:n], slots[:n])
+        if f8:
+            from oracle import fp8 as ofp8
+            def vals(bits):  # bf16 bit patterns -> their float32 values
+                return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+            ofp8.write_kv_fp8(np.zeros(batch.kv_cache.shape, dtype=np.uint8), vals(k[:n]), vals(v[:n]), slots[:n],
+                              ksc.cpu().numpy(), vsc.cpu().numpy())
+        else:
+            oracle.write_kv(batch.kv_cache, k[:n], v[:n], slots[:n])
         dt = time.perf_counter() - t1
-        line["cpu_baseline"] = {"value": 2 * n * 2 * Hkv * d * 2 / dt / 1e9, "unit": "GB/s", "cores": 1,
-                                "kind": "oracle", "seconds": round(dt, 3),
+        line["cpu_baseline"] = {"value": n * 2 * Hkv * d * (2 + (1 if f8 else 2)) / dt / 1e9, "unit": "GB/s",
+                                "cores": 1, "kind": "oracle", "seconds": round(dt, 3),
                                 "sample": f"{n} of {T} tokens (numpy, one pool copy included)"}
     return line
 
@@ -515,7 +536,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
     if args.workload == "kvwrite":
-        print(json.dumps(kvwrite_line(args.steps, args.warmup, not args.no_cpu_baseline)), flush=True)
+        print(json.dumps(kvwrite_line(args.steps, args.warmup, not args.no_cpu_baseline,
+                                      kv_dtype=args.kv_dtype or "same")), flush=True)
         return 0
     cfg = WORKLOADS[args.workload]
     kv_dtype = args.kv_dtype or KV_DTYPES.get(args.workload, "same")
