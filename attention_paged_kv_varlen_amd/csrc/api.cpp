@@ -21,8 +21,10 @@ struct pa_plan {
   pa::DeviceSchedule ds{};
   size_t ws_bytes = 0;
   // side stream and fork/join events, created with the plan when it holds both
-  // decode work and prefill or shared-prefix work, so that the MFMA-bound
-  // launches overlap the HBM-bound decode
+  // decode work and prefill work, so that the MFMA-bound launches overlap the
+  // HBM-bound decode (a shared-prefix pass without prefills runs before the
+  // decode on the caller's stream: beside it the decode lost more than the
+  // overlap gained)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
@@ -219,7 +221,7 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
       ds.n_merge = (int)hp.merges.size();
       ds.row_pbase = reinterpret_cast<const int32_t*>(base + o_row);
       ds.num_partials = hp.num_partials;
-      if (!hp.decode_items.empty() && (!hp.prefill_items.empty() || !hp.prefix_items.empty())) {
+      if (!hp.decode_items.empty() && !hp.prefill_items.empty()) {
         e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);

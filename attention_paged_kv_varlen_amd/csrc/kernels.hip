@@ -1495,9 +1495,11 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   int err = 0;
 
   // cascade prefix pass (all rows against the shared prefix) and prefills
-  // first, on the side stream when there is one (the MFMA-bound workgroups
-  // are then resident before the decode's fill the machine), decodes on the
-  // caller's stream, then the LSE merge of rows with several parts
+  // first, on the side stream when there is one (plans with decodes and
+  // prefills: the MFMA-bound workgroups are then resident before the
+  // decode's fill the machine; otherwise one after the other on the caller's
+  // stream), decodes on the caller's stream, then the LSE merge of rows with
+  // several parts
   void* stream = st.main;
   const bool fork = st.aux && s.n_decode > 0 && (s.n_prefill > 0 || s.n_prefix > 0);
   void* mstream = fork ? st.aux : stream;

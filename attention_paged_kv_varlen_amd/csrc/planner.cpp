@@ -199,22 +199,21 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
 
-  // Decode schedule.  With the automatic split and no shared prefix the
-  // decodes get balanced work lists: the decode keys, sequence after
+  // Decode schedule.  With the automatic split the decodes get balanced work
+  // lists: the decode keys (past the shared prefix, if any), sequence after
   // sequence, are cut into equal lists, one per group of waves resident at
   // once, so all of them finish together (a list may end one sequence and
   // start the next; each piece is an item with its own partial record).
   // Beside prefills the lists take only a share of the resident groups (see
-  // decode_share) and the prefill runs on the rest of the machine meanwhile.
-  // Otherwise (explicit split, or a shared prefix) each decode is cut into
-  // equal parts of at most `split` keys, one item per list, longest first,
-  // sized so that the work spreads over several waves per CU (items x Hkv ~
-  // 32 per CU) without tiny items.
+  // decode_share) and the prefill runs on the rest of the machine meanwhile;
+  // a shared-prefix pass without prefills runs before the decode instead.
+  // With an explicit split each decode is cut into equal parts of at most
+  // `split` keys, one item per list, longest first.
   int64_t dec_tokens = 0;
   for (int i = 0; i < nd; ++i) dec_tokens += seq_lens[hp.order[i]] - P;
   const int dec_units = Hkv * ((g + 15) / 16);
   const int dec_nw = decode_waves_per_wg(dec_units);
-  const bool balanced = p.kv_split_tokens == 0 && P == 0 && nd > 0 && decode_wgs_per_cu > 0;
+  const bool balanced = p.kv_split_tokens == 0 && nd > 0 && decode_wgs_per_cu > 0;
   int split = p.kv_split_tokens;
   int list_tokens = 0;
   if (balanced) {

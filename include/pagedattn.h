@@ -96,9 +96,9 @@ typedef struct pa_params {
   int32_t causal;             /* 1: key t visible to query i iff t <= c_b + i; 0: all L_b keys */
   int32_t common_prefix_len;  /* P: 0 = no cascade; else shared prefix tokens (see below) */
   int32_t kv_split_tokens;    /* 0 = automatic; else decode KV chunk per work item, multiple of 32
-                                 (automatic without a shared prefix: balanced work lists, see
-                                 pa_plan_info.num_decode_lists; beside prefills they take a share
-                                 of the resident waves and the prefill the rest) */
+                                 (automatic: balanced work lists over the keys past the shared
+                                 prefix, see pa_plan_info.num_decode_lists; beside prefills they
+                                 take a share of the resident waves and the prefill the rest) */
   float scale;                /* softmax scale applied to q . k (positive, finite) */
   int32_t kv_dtype;           /* pa_kv_dtype: 0 = the pool has element type dtype; PA_KV_FP8_E4M3
                                  needs dtype PA_BF16 (else PA_ERR_UNSUPPORTED) */

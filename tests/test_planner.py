@@ -264,14 +264,38 @@ def test_balanced_decode_lists_never_exceed_the_resident_groups():
         assert sizes.sum() == int(np.sum(lens)) and np.all(sizes <= W) and np.all(sizes[:-1] > W - 32)
 
 
-def test_decode_lists_are_single_items_with_a_split_or_a_shared_prefix():
+def test_decode_lists_are_single_items_with_an_explicit_split():
+    lens = [100, 5000, 40, 700]
+    plan, info = host_plan([1, 1, 1, 1], lens, split=64)
+    lists, spans = _decode_schedule(plan, info)
+    assert np.array_equal(lists, np.arange(len(spans) + 1)) and info["decode_list_tokens"] == 0
+
+
+def test_balanced_decode_lists_start_past_a_shared_prefix():
+    """With a shared prefix the balanced lists cut only the keys past it; each
+    decode row merges its prefix chunks with its suffix pieces."""
+    P = 32
     lens = [100, 5000, 40, 700]
     bt = np.arange(4 * 313, dtype=np.int32).reshape(4, 313)
-    bt[:, :1] = bt[0, :1]
-    for qlens, kw in (([1, 1, 1, 1], dict(split=64)), ([1, 1, 16, 1], dict(prefix=16, block_table=bt, mbs=313))):
-        plan, info = host_plan(qlens, lens, **kw)
-        lists, spans = _decode_schedule(plan, info)
-        assert np.array_equal(lists, np.arange(len(spans) + 1)) and info["decode_list_tokens"] == 0
+    bt[:, :P // 16] = bt[0, :P // 16]
+    plan, info = host_plan([1, 1, 1, 1], lens, prefix=P, block_table=bt, mbs=313, H=32, Hkv=8)
+    lists, spans = _decode_schedule(plan, info)
+    assert info["decode_list_tokens"] > 0 and info["num_decode_lists"] <= 256
+    assert np.all(spans[:, 1] >= P) and np.all(spans[:, 1] % 32 == 0)
+    assert info["decode_tokens_read"] == sum(L - P for L in lens) * 8
+    order = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER)
+    pos = 0
+    for b in order:  # the spans walk each sequence's suffix in order
+        k = P
+        while k < lens[b]:
+            seq, k0, k1 = spans[pos]
+            assert seq == b and k0 == k and k1 > k0
+            k = k1
+            pos += 1
+    assert pos == len(spans)
+    parts = np.bincount(spans[:, 0], minlength=4)
+    n_pc = info["num_prefix_items"] // max(1, -(-4 // info["prefill_rows_per_item"]))
+    assert np.array_equal(pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS), parts + n_pc)
 
 
 def _covers_decodes_in_order(plan, lens, spans):
