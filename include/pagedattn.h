@@ -230,10 +230,11 @@ size_t pa_plan_workspace_bytes(const pa_plan* plan);
  *  stream      hipStream_t (NULL = default stream).
  * Row order of out/lse is the caller's token order; the decode-first order only
  * affects the schedule.  The call is asynchronous and stream-ordered on
- * `stream`: when the plan holds both decode work and prefill or shared-prefix
- * work, the latter runs on a side stream owned by the plan, which first waits
- * for `stream` and which `stream` waits for before the final merge (event
- * record/wait only, so the call can be captured into a graph).  Concurrent calls
+ * `stream`: when the plan holds both decode work and prefill work, the prefill
+ * (and a shared-prefix pass, if any) runs on a side stream owned by the plan,
+ * which first waits for `stream` and which `stream` waits for before the final
+ * merge (event record/wait only, so the call can be captured into a graph);
+ * otherwise every launch is on `stream`.  Concurrent calls
  * on one plan need separate workspaces, and their side-stream work serialises.
  * Errors: INVALID_ARG (host-only plan, NULL pointers, small workspace, a plan
  * whose pool holds e4m3 codes: those run through pa_forward_fp8), HIP (launch
