@@ -7,7 +7,7 @@ script.  Entry points keep their C names::
     params = make_params(num_seqs=..., num_heads=..., ...)
     plan = pa_plan_create(params, query_start_loc, seq_lens, block_table, device=0)
     ws = torch.empty(pa_plan_workspace_bytes(plan), dtype=torch.uint8, device="cuda")
-    pa_forward(plan, q, kv_cache, block_table_dev, out, lse, ws)
+    pa_forward(plan, q, kv_cache, block_table_dev, query_start_loc_dev, seq_lens_dev, out, lse, ws)
 """
 from ._capi import (  # noqa: F401
     EXPORTED,
@@ -41,6 +41,7 @@ from ._capi import (  # noqa: F401
     pa_last_error,
     pa_merge_states,
     pa_params,
+    pa_plan_check_metadata,
     pa_plan_create,
     pa_plan_destroy,
     pa_plan_get_array,

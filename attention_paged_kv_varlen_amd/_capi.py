@@ -25,7 +25,7 @@ PA_KV_NHD, PA_KV_HND = 0, 1
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
     "pa_kv_cache_shape", "pa_kv_cache_stride_order", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
-    "pa_plan_workspace_bytes", "pa_forward", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
+    "pa_plan_workspace_bytes", "pa_plan_check_metadata", "pa_forward", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
     "pa_write_kv_fp8", "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start",
     "pa_profile_stop",
 )
@@ -37,7 +37,7 @@ class pa_params(ctypes.Structure):
         ("head_size", c_int32), ("block_size", c_int32), ("num_blocks", c_int32),
         ("max_blocks_per_seq", c_int32), ("dtype", c_int32), ("causal", c_int32),
         ("common_prefix_len", c_int32), ("kv_split_tokens", c_int32), ("scale", c_float),
-        ("kv_dtype", c_int32), ("kv_layout", c_int32),
+        ("kv_dtype", c_int32), ("kv_layout", c_int32), ("check_metadata", c_int32),
     ]
 
 
@@ -56,7 +56,8 @@ class pa_plan_info(ctypes.Structure):
 
 
 class pa_kernel_time(ctypes.Structure):
-    _fields_ = [("name", c_char * 48), ("launches", c_int32), ("total_ms", c_double)]
+    _fields_ = [("name", c_char * 48), ("launches", c_int32), ("total_ms", c_double), ("min_ms", c_double),
+                ("median_ms", c_double), ("max_ms", c_double)]
 
 
 class PagedAttnError(RuntimeError):
@@ -84,14 +85,15 @@ def lib():
     L.pa_plan_get_array.argtypes = [c_void_p, c_int32, POINTER(c_int32), c_int64, POINTER(c_int64)]
     L.pa_plan_workspace_bytes.argtypes = [c_void_p]
     L.pa_plan_workspace_bytes.restype = c_size_t
-    L.pa_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
-                             c_void_p]
+    L.pa_plan_check_metadata.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.pa_forward.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             c_void_p, c_size_t, c_void_p]
     L.pa_merge_states.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                   c_int32, c_int32, c_void_p]
     L.pa_gather_kv.argtypes = [c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p, c_void_p]
     L.pa_write_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p]
-    L.pa_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
-                                 c_void_p, c_void_p, c_size_t, c_void_p]
+    L.pa_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     L.pa_write_kv_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p,
                                   c_int32, c_void_p, c_void_p]
     L.pa_plan_destroy.argtypes = [c_void_p]
@@ -157,13 +159,14 @@ class Plan:
 
 def make_params(*, num_seqs, num_heads, num_kv_heads, head_size, block_size, num_blocks, max_blocks_per_seq,
                 dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0, kv_dtype="same",
-                kv_layout="NHD") -> pa_params:
+                kv_layout="NHD", check_metadata=False) -> pa_params:
     dt = {"bf16": PA_BF16, "fp32": PA_FP32}.get(dtype, dtype)
     kvt = {"same": PA_KV_SAME, None: PA_KV_SAME, "fp8_e4m3": PA_KV_FP8_E4M3}.get(kv_dtype, kv_dtype)
     lay = {"NHD": PA_KV_NHD, "HND": PA_KV_HND}.get(kv_layout, kv_layout)
     return pa_params(int(num_seqs), int(num_heads), int(num_kv_heads), int(head_size), int(block_size),
                      int(num_blocks), int(max_blocks_per_seq), int(dt), int(bool(causal)),
-                     int(common_prefix_len), int(kv_split_tokens), float(scale), int(kvt), int(lay))
+                     int(common_prefix_len), int(kv_split_tokens), float(scale), int(kvt), int(lay),
+                     int(bool(check_metadata)))
 
 
 # ---------------------------------------------------------------------------
@@ -220,23 +223,29 @@ def pa_plan_workspace_bytes(plan: Plan) -> int:
     return int(lib().pa_plan_workspace_bytes(plan.handle))
 
 
-def pa_forward(plan: Plan, q, kv_cache, block_table, out, lse=None, workspace=None, workspace_bytes=None,
-               stream=None) -> None:
+def pa_plan_check_metadata(plan: Plan, block_table, query_start_loc=None, seq_lens=None, stream=None) -> None:
+    _check(lib().pa_plan_check_metadata(plan.handle, _ptr(block_table), _ptr(query_start_loc), _ptr(seq_lens),
+                                        _stream(stream)))
+
+
+def pa_forward(plan: Plan, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse=None, workspace=None,
+               workspace_bytes=None, stream=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_forward(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(out), _ptr(lse),
-                            _ptr(workspace), workspace_bytes, _stream(stream)))
+    _check(lib().pa_forward(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+                            _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                            _stream(stream)))
 
 
-def pa_forward_fp8(plan: Plan, q, kv_cache, block_table, k_scale, v_scale, out, lse=None, workspace=None,
-                   workspace_bytes=None, num_scales=None, stream=None) -> None:
+def pa_forward_fp8(plan: Plan, q, kv_cache, block_table, query_start_loc, seq_lens, k_scale, v_scale, out, lse=None,
+                   workspace=None, workspace_bytes=None, num_scales=None, stream=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if num_scales is None:
         num_scales = int(k_scale.numel())
-    _check(lib().pa_forward_fp8(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(k_scale),
-                                _ptr(v_scale), int(num_scales), _ptr(out), _ptr(lse), _ptr(workspace),
-                                workspace_bytes, _stream(stream)))
+    _check(lib().pa_forward_fp8(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+                                _ptr(seq_lens), _ptr(k_scale), _ptr(v_scale), int(num_scales), _ptr(out), _ptr(lse),
+                                _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def pa_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out=None, *, num_tokens=None, num_heads=None,
@@ -290,5 +299,6 @@ def pa_profile_stop(capacity: int = 64) -> list:
     buf = (pa_kernel_time * capacity)()
     n = c_int32()
     _check(lib().pa_profile_stop(buf, capacity, ctypes.byref(n)))
-    return [{"name": buf[i].name.decode(), "launches": buf[i].launches, "total_ms": buf[i].total_ms}
+    return [{"name": buf[i].name.decode(), "launches": buf[i].launches, "total_ms": buf[i].total_ms,
+             "min_ms": buf[i].min_ms, "median_ms": buf[i].median_ms, "max_ms": buf[i].max_ms}
             for i in range(n.value)]

@@ -2,7 +2,8 @@
 
 Usage: ``python -m attention_paged_kv_varlen_amd.build`` (or ``build()``).  Every
 call recompiles.  The packed-FP32 target feature is switched off for the device
-code (ordinary float code only).
+code (ordinary float code only); the host-only sources (planner, C ABI) are
+compiled as plain C++ without it.
 """
 from __future__ import annotations
 
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 SOURCES = ["kernels.hip", "planner.cpp", "api.cpp"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -38,8 +40,11 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             path = os.path.join(CSRC, src)
             obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-                   "-Wall", "-Wno-unused-function", *DEVICE_FLAGS,
+            if src.endswith(".hip"):
+                lang = ["-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS]
+            else:  # host code only: no device pass, so no device-only flags
+                lang = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
+            cmd = [cc, *lang, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
                    "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)

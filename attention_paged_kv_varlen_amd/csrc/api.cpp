@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -27,6 +28,18 @@ struct pa_plan {
   // overlap gained)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // Held by a forward from its event record on the caller's stream to the
+  // caller's wait on the join event, so that two host threads sharing the plan
+  // cannot interleave their records of the two events (one side-stream pass
+  // would then wait on the other caller's stream).
+  std::mutex fork_mu;
+  // Device copies of the metadata the plan was built from, for
+  // pa_plan_check_metadata: query_start_loc [B+1], seq_lens [B], the host block
+  // table [B * max_blocks_per_seq] when one was given, and a 4-byte result.
+  const int32_t* dev_qsl = nullptr;
+  const int32_t* dev_seq_lens = nullptr;
+  const int32_t* dev_bt = nullptr;
+  int32_t* dev_check = nullptr;
 };
 
 namespace {
@@ -81,6 +94,10 @@ void prof_release() {
 }  // namespace
 
 namespace pa {
+
+pa_status set_last_error(pa_status s, const std::string& msg) { return set_err(s, msg); }
+
+int plan_device(const pa_plan* plan) { return plan ? plan->device : -1; }
 
 void profile_before(const char* name, void* stream) {
   if (!g_prof.active || (int)g_prof.recs.size() >= g_prof.max) return;
@@ -171,64 +188,74 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
                        : 0;
 
   if (device >= 0) {
-    const size_t b_dec = hp.decode_items.size() * sizeof(pa::WorkItem);
-    const size_t b_pre = hp.prefill_items.size() * sizeof(pa::WorkItem);
-    const size_t b_pfx = hp.prefix_items.size() * sizeof(pa::WorkItem);
-    const size_t b_mrg = hp.merges.size() * sizeof(pa::MergeRow);
-    const size_t b_row = hp.row_pbase.size() * sizeof(int32_t);
-    const size_t b_lst = hp.decode_lists.size() * sizeof(int32_t);
-    const size_t o_dec = 0, o_pre = o_dec + align256(b_dec), o_pfx = o_pre + align256(b_pre),
-                 o_mrg = o_pfx + align256(b_pfx), o_row = o_mrg + align256(b_mrg), o_lst = o_row + align256(b_row),
-                 total = o_lst + align256(b_lst);
-    if (total > 0) {
-      DeviceGuard guard(device);
-      if (!guard.ok) {
-        delete plan;
-        return set_err(PA_ERR_HIP, "hipSetDevice failed");
-      }
-      std::vector<unsigned char> host(total, 0);
-      auto put = [&](size_t off, const void* src, size_t n) {  // an empty vector's data() may be null
-        if (n) std::memcpy(host.data() + off, src, n);
-      };
-      put(o_dec, hp.decode_items.data(), b_dec);
-      put(o_pre, hp.prefill_items.data(), b_pre);
-      put(o_pfx, hp.prefix_items.data(), b_pfx);
-      put(o_mrg, hp.merges.data(), b_mrg);
-      put(o_row, hp.row_pbase.data(), b_row);
-      put(o_lst, hp.decode_lists.data(), b_lst);
-      hipError_t e = hipMalloc(&plan->dev_buf, total);
+    // one device buffer: the schedule, then the metadata copies; every
+    // section starts on a 256-byte boundary
+    struct Section {
+      const void* src;
+      size_t bytes;
+      size_t off;
+    };
+    std::vector<Section> sec = {
+        {hp.decode_items.data(), hp.decode_items.size() * sizeof(pa::WorkItem), 0},
+        {hp.prefill_items.data(), hp.prefill_items.size() * sizeof(pa::WorkItem), 0},
+        {hp.prefix_items.data(), hp.prefix_items.size() * sizeof(pa::WorkItem), 0},
+        {hp.merges.data(), hp.merges.size() * sizeof(pa::MergeRow), 0},
+        {hp.row_pbase.data(), hp.row_pbase.size() * sizeof(int32_t), 0},
+        {hp.decode_lists.data(), hp.decode_lists.size() * sizeof(int32_t), 0},
+        {hp.qsl.data(), hp.qsl.size() * sizeof(int32_t), 0},
+        {hp.seq_lens.data(), hp.seq_lens.size() * sizeof(int32_t), 0},
+        {hp.block_table.data(), hp.block_table.size() * sizeof(int32_t), 0},
+        {nullptr, sizeof(int32_t), 0},  // metadata check result
+    };
+    size_t total = 0;
+    for (Section& x : sec) {
+      x.off = total;
+      total += align256(x.bytes);
+    }
+    DeviceGuard guard(device);
+    if (!guard.ok) {
+      delete plan;
+      return set_err(PA_ERR_HIP, "hipSetDevice failed");
+    }
+    std::vector<unsigned char> host(total, 0);
+    for (const Section& x : sec)  // an empty vector's data() may be null
+      if (x.bytes && x.src) std::memcpy(host.data() + x.off, x.src, x.bytes);
+    hipError_t e = hipMalloc(&plan->dev_buf, total);
+    if (e != hipSuccess) {
+      plan->dev_buf = nullptr;
+      delete plan;
+      return set_err(PA_ERR_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
+    }
+    e = hipMemcpy(plan->dev_buf, host.data(), total, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      pa_plan_destroy(plan);
+      return hip_err(e, "hipMemcpy");
+    }
+    unsigned char* base = static_cast<unsigned char*>(plan->dev_buf);
+    pa::DeviceSchedule& ds = plan->ds;
+    ds.decode = reinterpret_cast<const pa::WorkItem*>(base + sec[0].off);
+    ds.n_decode = (int)hp.decode_items.size();
+    ds.prefill = reinterpret_cast<const pa::WorkItem*>(base + sec[1].off);
+    ds.n_prefill = (int)hp.prefill_items.size();
+    ds.prefix = reinterpret_cast<const pa::WorkItem*>(base + sec[2].off);
+    ds.n_prefix = (int)hp.prefix_items.size();
+    ds.merge = reinterpret_cast<const pa::MergeRow*>(base + sec[3].off);
+    ds.n_merge = (int)hp.merges.size();
+    ds.row_pbase = reinterpret_cast<const int32_t*>(base + sec[4].off);
+    ds.decode_lists = reinterpret_cast<const int32_t*>(base + sec[5].off);
+    ds.n_decode_lists = hp.decode_lists.empty() ? 0 : (int)hp.decode_lists.size() - 1;
+    ds.num_partials = hp.num_partials;
+    plan->dev_qsl = reinterpret_cast<const int32_t*>(base + sec[6].off);
+    plan->dev_seq_lens = reinterpret_cast<const int32_t*>(base + sec[7].off);
+    plan->dev_bt = hp.block_table.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + sec[8].off);
+    plan->dev_check = reinterpret_cast<int32_t*>(base + sec[9].off);
+    if (!hp.decode_items.empty() && !hp.prefill_items.empty()) {
+      e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);
       if (e != hipSuccess) {
-        delete plan;
-        return set_err(PA_ERR_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
-      }
-      e = hipMemcpy(plan->dev_buf, host.data(), total, hipMemcpyHostToDevice);
-      if (e != hipSuccess) {
-        (void)hipFree(plan->dev_buf);
-        delete plan;
-        return hip_err(e, "hipMemcpy");
-      }
-      unsigned char* base = static_cast<unsigned char*>(plan->dev_buf);
-      pa::DeviceSchedule& ds = plan->ds;
-      ds.decode = reinterpret_cast<const pa::WorkItem*>(base + o_dec);
-      ds.n_decode = (int)hp.decode_items.size();
-      ds.decode_lists = reinterpret_cast<const int32_t*>(base + o_lst);
-      ds.n_decode_lists = hp.decode_lists.empty() ? 0 : (int)hp.decode_lists.size() - 1;
-      ds.prefill = reinterpret_cast<const pa::WorkItem*>(base + o_pre);
-      ds.n_prefill = (int)hp.prefill_items.size();
-      ds.prefix = reinterpret_cast<const pa::WorkItem*>(base + o_pfx);
-      ds.n_prefix = (int)hp.prefix_items.size();
-      ds.merge = reinterpret_cast<const pa::MergeRow*>(base + o_mrg);
-      ds.n_merge = (int)hp.merges.size();
-      ds.row_pbase = reinterpret_cast<const int32_t*>(base + o_row);
-      ds.num_partials = hp.num_partials;
-      if (!hp.decode_items.empty() && !hp.prefill_items.empty()) {
-        e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);
-        if (e != hipSuccess) {
-          pa_plan_destroy(plan);
-          return hip_err(e, "stream/event creation");
-        }
+        pa_plan_destroy(plan);
+        return hip_err(e, "stream/event creation");
       }
     }
   }
@@ -276,15 +303,53 @@ pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, in
 
 size_t pa_plan_workspace_bytes(const pa_plan* plan) { return plan ? plan->ws_bytes : 0; }
 
+}  // extern "C"
+
+namespace {
+
+bool misaligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
+
+// Compare the caller's device metadata with the plan's copies (one small
+// kernel, then a wait for its 4-byte result on `stream`).  NULL arrays are not
+// compared.  PA_OK, INVALID_ARG on a mismatch, or HIP.
+pa_status check_metadata(const pa_plan* plan, const int32_t* block_table, const int32_t* qsl,
+                         const int32_t* seq_lens, void* stream) {
+  const pa::HostPlan& hp = plan->hp;
+  const pa_params& p = hp.p;
+  if (misaligned(block_table, 4) || misaligned(qsl, 4) || misaligned(seq_lens, 4))
+    return set_err(PA_ERR_INVALID_ARG, "metadata arrays must be 4-byte aligned");
+  int e = pa::launch_check_metadata(block_table, qsl, seq_lens, plan->dev_bt, plan->dev_qsl, plan->dev_seq_lens,
+                                    p.num_seqs, p.max_blocks_per_seq, p.block_size, p.num_blocks, plan->dev_check,
+                                    stream);
+  if (e != 0) return hip_err((hipError_t)e, "metadata check launch");
+  int32_t bad = -1;
+  hipError_t h = hipMemcpyAsync(&bad, plan->dev_check, sizeof(bad), hipMemcpyDeviceToHost,
+                                static_cast<hipStream_t>(stream));
+  if (h == hipSuccess) h = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (h != hipSuccess) return hip_err(h, "metadata check");
+  if (bad != 0)
+    return set_err(PA_ERR_INVALID_ARG,
+                   "device metadata differs from the plan's (query_start_loc, seq_lens or block_table): " +
+                       std::to_string(bad) + " threads saw a mismatch");
+  return PA_OK;
+}
+
 // The forward of pa_forward and pa_forward_fp8 after their own checks.
-static pa_status forward_common(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                                const float* k_scale, const float* v_scale, int n_scales) {
+pa_status forward_common(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                         const int32_t* qsl, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, const float* k_scale, const float* v_scale,
+                         int n_scales) {
   const pa::HostPlan& hp = plan->hp;
   if (hp.T == 0) return PA_OK;
   if (!q || !kv_cache || !block_table || !out) return set_err(PA_ERR_INVALID_ARG, "q/kv_cache/block_table/out is NULL");
   if (workspace_bytes < plan->ws_bytes) return set_err(PA_ERR_INVALID_ARG, "workspace too small");
   if (plan->ws_bytes > 0 && !workspace) return set_err(PA_ERR_INVALID_ARG, "workspace is NULL");
+  // the kernels move q, out, the pool and the workspace in 16-byte pieces
+  if (misaligned(q, 16) || misaligned(out, 16) || misaligned(kv_cache, 16) ||
+      (plan->ws_bytes > 0 && misaligned(workspace, 16)))
+    return set_err(PA_ERR_INVALID_ARG, "q, out, kv_cache and workspace must be 16-byte aligned");
+  if (misaligned(block_table, 4) || misaligned(lse, 4))
+    return set_err(PA_ERR_INVALID_ARG, "block_table and lse must be 4-byte aligned");
 
   const pa_params& p = hp.p;
   pa::LaunchGeom g{};
@@ -316,26 +381,52 @@ static pa_status forward_common(const pa_plan* plan, const void* q, const void* 
   }
   DeviceGuard guard(plan->device);
   if (!guard.ok) return set_err(PA_ERR_HIP, "hipSetDevice failed");
+  if (p.check_metadata) {
+    const pa_status cs = check_metadata(plan, block_table, qsl, seq_lens, stream);
+    if (cs != PA_OK) return cs;
+  }
   const pa::Streams st{stream, plan->aux, plan->ev_fork, plan->ev_join};
-  const int e = pa::launch_forward(g, plan->ds, t, st);
+  int e;
+  if (plan->aux) {
+    std::lock_guard<std::mutex> lock(const_cast<pa_plan*>(plan)->fork_mu);
+    e = pa::launch_forward(g, plan->ds, t, st);
+  } else {
+    e = pa::launch_forward(g, plan->ds, t, st);
+  }
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
   return PA_OK;
 }
 
-pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table, void* out,
-                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+pa_status pa_plan_check_metadata(const pa_plan* plan, const int32_t* block_table, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
+  DeviceGuard guard(plan->device);
+  if (!guard.ok) return set_err(PA_ERR_HIP, "hipSetDevice failed");
+  return check_metadata(plan, block_table, query_start_loc, seq_lens, stream);
+}
+
+pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
+                     const int32_t* query_start_loc, const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
   if (plan->hp.p.kv_dtype != PA_KV_SAME)
     return set_err(PA_ERR_INVALID_ARG, "the plan's pool holds e4m3 codes: use pa_forward_fp8 with its scales");
-  return forward_common(plan, q, kv_cache, block_table, out, lse, workspace, workspace_bytes, stream, nullptr,
-                        nullptr, 0);
+  return forward_common(plan, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, 0);
 }
 
 pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cache, const int32_t* block_table,
-                         const float* k_scale, const float* v_scale, int32_t num_scales, void* out, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         const int32_t* query_start_loc, const int32_t* seq_lens, const float* k_scale,
+                         const float* v_scale, int32_t num_scales, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!plan) return set_err(PA_ERR_INVALID_ARG, "plan is NULL");
   if (plan->device < 0) return set_err(PA_ERR_INVALID_ARG, "host-only plan cannot run");
@@ -346,10 +437,10 @@ pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cach
     return set_err(PA_ERR_INVALID_ARG, "num_scales must be 1 or num_kv_heads");
   if (plan->hp.T == 0) return PA_OK;
   if (!k_scale || !v_scale) return set_err(PA_ERR_INVALID_ARG, "k_scale / v_scale is NULL");
-  if (reinterpret_cast<uintptr_t>(kv_cache) % 16 != 0)
-    return set_err(PA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
-  return forward_common(plan, q, kv_cache, block_table, out, lse, workspace, workspace_bytes, stream, k_scale,
-                        v_scale, num_scales);
+  if (misaligned(k_scale, 4) || misaligned(v_scale, 4))
+    return set_err(PA_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+  return forward_common(plan, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse, workspace,
+                        workspace_bytes, stream, k_scale, v_scale, num_scales);
 }
 
 pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o_out,
@@ -512,7 +603,7 @@ pa_status pa_profile_start(int32_t max_launches) {
 pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count) {
   g_err.clear();
   if (!g_prof.active) return set_err(PA_ERR_INVALID_ARG, "no profiling session on this thread");
-  std::map<std::string, std::pair<int, double>> agg;
+  std::map<std::string, std::vector<double>> agg;
   std::vector<std::string> names;
   pa_status st = PA_OK;
   for (const ProfRec& r : g_prof.recs) {
@@ -526,10 +617,9 @@ pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count)
     auto it = agg.find(r.name);
     if (it == agg.end()) {
       names.push_back(r.name);
-      agg[r.name] = {1, (double)ms};
+      agg[r.name] = {(double)ms};
     } else {
-      it->second.first += 1;
-      it->second.second += ms;
+      it->second.push_back((double)ms);
     }
   }
   prof_release();
@@ -538,10 +628,16 @@ pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count)
   if ((int32_t)names.size() > capacity || (!out && !names.empty()))
     return set_err(PA_ERR_INVALID_ARG, "capacity too small");
   for (size_t i = 0; i < names.size(); ++i) {
+    std::vector<double>& v = agg[names[i]];
+    std::sort(v.begin(), v.end());
+    const size_t n = v.size();
     std::memset(&out[i], 0, sizeof(pa_kernel_time));
     std::snprintf(out[i].name, sizeof(out[i].name), "%s", names[i].c_str());
-    out[i].launches = agg[names[i]].first;
-    out[i].total_ms = agg[names[i]].second;
+    out[i].launches = (int32_t)n;
+    for (double x : v) out[i].total_ms += x;
+    out[i].min_ms = v.front();
+    out[i].max_ms = v.back();
+    out[i].median_ms = n % 2 ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
   }
   return PA_OK;
 }

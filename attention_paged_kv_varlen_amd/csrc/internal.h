@@ -118,6 +118,12 @@ int launch_merge_states(const void* oa, const float* la, const void* ob, const f
 int launch_gather(const void* kv, const int32_t* bt_row, int seq_len, int bs, int Hkv, int D,
                   int elem_bytes, int64_t slot_stride, int64_t head_stride, void* k_out, void* v_out,
                   void* stream);
+// One workgroup comparing the caller's device metadata with the plan's copies
+// (NULL caller arrays and a NULL p_bt are skipped or replaced by the pool range
+// check); writes the mismatch count to *bad.
+int launch_check_metadata(const int32_t* bt, const int32_t* qsl, const int32_t* sl, const int32_t* p_bt,
+                          const int32_t* p_qsl, const int32_t* p_sl, int B, int mb, int bs, int num_blocks,
+                          int32_t* bad, void* stream);
 int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int head_bytes, int bs,
                     int64_t n_slots, int64_t slot_bstride, int64_t head_bstride, void* kv, void* stream);
 int launch_write_kv_fp8(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int D, int bs,
@@ -138,6 +144,11 @@ inline void pool_strides(int layout, int bs, int Hkv, int D, int& slot_stride, i
   }
 }
 
+// The calling thread's error message for pa_last_error (api.cpp); returns `s`.
+pa_status set_last_error(pa_status s, const std::string& msg);
+// The device a plan runs on (< 0: host-only plan).
+int plan_device(const pa_plan* plan);
+
 // Launch bookkeeping for pa_profile_* (api.cpp).
 void profile_before(const char* name, void* stream);
 void profile_after(void* stream);
@@ -147,6 +158,8 @@ struct HostPlan {
   pa_params p{};
   int32_t T = 0;
   std::vector<int32_t> order, is_decode, prefix_blocks, row_partials, row_pbase;
+  // the metadata the plan was built from (block_table empty when none was given)
+  std::vector<int32_t> qsl, seq_lens, block_table;
   std::vector<WorkItem> decode_items, prefill_items, prefix_items;
   std::vector<int32_t> decode_lists;  // [lists + 1]
   std::vector<MergeRow> merges;

@@ -1346,6 +1346,34 @@ __global__ void __launch_bounds__(256) gather_kernel(const unsigned char* kv, co
   *reinterpret_cast<u32x4*>(v_out + dst) = *reinterpret_cast<const u32x4*>(src + half);
 }
 
+// Comparison of the caller's device metadata with the plan's copies: every
+// entry of query_start_loc [B + 1] and seq_lens [B], and the used entries
+// (the first ceil(L_b / bs) of row b, L_b from the plan) of the block table,
+// against the plan's host table when it kept one, else against the pool size
+// ([0, num_blocks)).  NULL caller arrays are skipped.  One workgroup: *bad
+// receives the number of threads that saw a difference (0 = consistent).
+__global__ void __launch_bounds__(1024) check_metadata_kernel(const int32_t* bt, const int32_t* qsl,
+                                                              const int32_t* sl, const int32_t* p_bt,
+                                                              const int32_t* p_qsl, const int32_t* p_sl, int B,
+                                                              int mb, int bs, int num_blocks, int32_t* bad) {
+  bool diff = false;
+  for (int i = (int)threadIdx.x; i <= B; i += (int)blockDim.x) {
+    if (qsl && qsl[i] != p_qsl[i]) diff = true;
+    if (sl && i < B && sl[i] != p_sl[i]) diff = true;
+  }
+  if (bt) {
+    const int64_t n = (int64_t)B * mb;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const int b = (int)(i / mb), j = (int)(i % mb);
+      if (j >= (p_sl[b] + bs - 1) / bs) continue;
+      const int32_t id = bt[i];
+      if (p_bt ? id != p_bt[i] : (id < 0 || id >= num_blocks)) diff = true;
+    }
+  }
+  const int n_bad = __syncthreads_count(diff ? 1 : 0);
+  if (threadIdx.x == 0) *bad = n_bad;
+}
+
 // ---------------------------------------------------------------------------
 // Cache write: thread i copies 16-byte chunk i % (2 C) of token i / (2 C)
 // (C chunks per K or V row of all KV heads; the first C of the K row, then the
@@ -1609,6 +1637,13 @@ int decode_workgroups_per_cu(int dtype, int kv_dtype, int head_size, int waves) 
   else if (dtype == PA_FP32 && head_size == 64)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<float, float, 64, false, true>, threads, 0);
   return e == hipSuccess ? n : 0;
+}
+
+int launch_check_metadata(const int32_t* bt, const int32_t* qsl, const int32_t* sl, const int32_t* p_bt,
+                          const int32_t* p_qsl, const int32_t* p_sl, int B, int mb, int bs, int num_blocks,
+                          int32_t* bad, void* stream) {
+  return launch("check_metadata", check_metadata_kernel, dim3(1), dim3(1024), stream, bt, qsl, sl, p_bt, p_qsl, p_sl,
+                B, mb, bs, num_blocks, bad);
 }
 
 int launch_write_kv(const void* k, const void* v, const int64_t* slots, int n_tok, int Hkv, int head_bytes, int bs,

@@ -112,6 +112,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (p.max_blocks_per_seq < 1)
     return fail(err, PA_ERR_INVALID_ARG, "max_blocks_per_seq %lld < 1", p.max_blocks_per_seq);
   if (p.causal != 0 && p.causal != 1) return fail(err, PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p.check_metadata != 0 && p.check_metadata != 1)
+    return fail(err, PA_ERR_INVALID_ARG, "check_metadata must be 0 or 1");
   if (!std::isfinite(p.scale) || !(p.scale > 0.f))
     return fail(err, PA_ERR_INVALID_ARG, "scale must be positive and finite");
   if (p.kv_split_tokens < 0 || p.kv_split_tokens % 32 != 0)
@@ -165,6 +167,9 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   hp.p = p;
   const int H = p.num_heads, Hkv = p.num_kv_heads, g = H / Hkv;
   hp.T = B > 0 ? qsl[B] : 0;
+  hp.qsl.assign(qsl, qsl + B + 1);
+  hp.seq_lens.assign(seq_lens, seq_lens + B);
+  if (block_table) hp.block_table.assign(block_table, block_table + (int64_t)B * mb);
   hp.order.reserve(B);
   hp.is_decode.resize(B);
   int nd = 0, ndt = 0, np = 0, npt = 0;

@@ -29,6 +29,8 @@ class DeviceBatch:
     q: object
     kv_cache: object
     block_table: object
+    query_start_loc: object
+    seq_lens: object
     out: object
     lse: object
     workspace: object
@@ -37,19 +39,20 @@ class DeviceBatch:
 
     def forward(self, stream=None) -> None:
         if self.k_scale is not None:
-            _capi.pa_forward_fp8(self.plan, self.q, self.kv_cache, self.block_table, self.k_scale, self.v_scale,
-                                 self.out, self.lse, self.workspace, stream=stream)
+            _capi.pa_forward_fp8(self.plan, self.q, self.kv_cache, self.block_table, self.query_start_loc,
+                                 self.seq_lens, self.k_scale, self.v_scale, self.out, self.lse, self.workspace,
+                                 stream=stream)
         else:
-            _capi.pa_forward(self.plan, self.q, self.kv_cache, self.block_table, self.out, self.lse,
-                             self.workspace, stream=stream)
+            _capi.pa_forward(self.plan, self.q, self.kv_cache, self.block_table, self.query_start_loc,
+                             self.seq_lens, self.out, self.lse, self.workspace, stream=stream)
 
 
 def to_device(q, kv_cache, block_table, query_start_loc, seq_lens, *, num_heads, num_kv_heads, head_size,
               block_size, dtype, scale, causal=True, common_prefix_len=0, kv_split_tokens=0,
               device="cuda", kv_cache_dev=None, kv_dtype="same", k_scale=None, v_scale=None,
-              kv_layout="NHD") -> DeviceBatch:
-    """Build the plan and the device tensors (q, pool, table, out, lse, workspace;
-    the K/V scales of an e4m3 pool)."""
+              kv_layout="NHD", check_metadata=False) -> DeviceBatch:
+    """Build the plan and the device tensors (q, pool, table, query_start_loc,
+    seq_lens, out, lse, workspace; the K/V scales of an e4m3 pool)."""
     import torch
     dev = torch.device(device)
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
@@ -57,11 +60,13 @@ def to_device(q, kv_cache, block_table, query_start_loc, seq_lens, *, num_heads,
         num_seqs=len(seq_lens), num_heads=num_heads, num_kv_heads=num_kv_heads, head_size=head_size,
         block_size=block_size, num_blocks=kv_cache.shape[0], max_blocks_per_seq=bt.shape[1], dtype=dtype,
         scale=scale, causal=causal, common_prefix_len=common_prefix_len, kv_split_tokens=kv_split_tokens,
-        kv_dtype=kv_dtype, kv_layout=kv_layout)
+        kv_dtype=kv_dtype, kv_layout=kv_layout, check_metadata=check_metadata)
     plan = _capi.pa_plan_create(params, query_start_loc, seq_lens, bt, device=dev.index or 0)
     tq = _to_torch(q, dtype, dev)
     tkv = kv_cache_dev if kv_cache_dev is not None else _to_torch(kv_cache, dtype, dev)
     tbt = torch.from_numpy(bt).to(dev)
+    tqsl = torch.from_numpy(np.ascontiguousarray(query_start_loc, dtype=np.int32)).to(dev)
+    tsl = torch.from_numpy(np.ascontiguousarray(seq_lens, dtype=np.int32)).to(dev)
     out = torch.empty_like(tq)
     lse = torch.empty(tq.shape[0], num_heads, dtype=torch.float32, device=dev)
     nws = _capi.pa_plan_workspace_bytes(plan)
@@ -70,4 +75,4 @@ def to_device(q, kv_cache, block_table, query_start_loc, seq_lens, *, num_heads,
     if kv_dtype == "fp8_e4m3":
         ks = torch.from_numpy(np.ascontiguousarray(k_scale, dtype=np.float32).reshape(-1)).to(dev)
         vs = torch.from_numpy(np.ascontiguousarray(v_scale, dtype=np.float32).reshape(-1)).to(dev)
-    return DeviceBatch(params, plan, tq, tkv, tbt, out, lse, ws, ks, vs)
+    return DeviceBatch(params, plan, tq, tkv, tbt, tqsl, tsl, out, lse, ws, ks, vs)

@@ -119,8 +119,11 @@ def _batch_to_device(batch, common_prefix_len=None, kv_split_tokens=0):
 
 
 def time_steps(db, steps: int, warmup: int) -> dict:
-    """Warm up, then time `steps` forwards (wall clock between synchronisations)
-    while the library records HIP events around each of its launches."""
+    """Warm up, then time `steps` forwards: wall clock between synchronisations
+    (ms_per_step), HIP events on the caller's stream around each forward (the
+    step's device time; the side stream joins it before the forward ends), and
+    HIP events the library records around each of its launches (per kernel:
+    average, median, shortest and longest launch)."""
     import torch
 
     import attention_paged_kv_varlen_amd as pa
@@ -128,18 +131,30 @@ def time_steps(db, steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         db.forward(stream)
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     pa.pa_profile_start(steps * 8 + 8)
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for e0, e1 in ev:
+        e0.record(stream)
         db.forward(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = pa.pa_profile_stop()
+    step = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     return {
         "ms_per_step": (t1 - t0) * 1e3 / steps,
-        "kernels": {k["name"]: {"launches": k["launches"], "avg_us": 1e3 * k["total_ms"] / max(k["launches"], 1)}
+        "step_event_ms": {"median": float(np.median(step)), "min": step[0], "max": step[-1]},
+        "kernels": {k["name"]: {"launches": k["launches"], "avg_us": 1e3 * k["total_ms"] / max(k["launches"], 1),
+                                "median_us": 1e3 * k["median_ms"], "min_us": 1e3 * k["min_ms"],
+                                "max_us": 1e3 * k["max_ms"]}
                     for k in kern},
     }
+
+
+def launch_stats(k) -> dict:
+    """Per-launch event times of one kernel family (us)."""
+    return {x: round(k[f"{x}_us"], 3) for x in ("avg", "median", "min", "max")}
 
 
 def time_graph(db, steps: int, warmup: int) -> float:
@@ -229,46 +244,64 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / best / 1e9
 
 
-def cpu_baseline(batch, counts, budget_s: float = 12.0) -> dict:
-    """Time the oracle on a bounded sample of the same batch: whole sequences in
-    a fixed random order until `budget_s` of CPU work; one BLAS thread."""
+def cpu_threads() -> int:
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(batch, counts, budget_s: float = 8.0, repeats: int = 3) -> dict:
+    """Time the oracle on a bounded sample of the same batch, with BLAS threads
+    set to the host cores this process may use: whole sequences in a fixed
+    random order until `budget_s` of oracle time (the sample), then the same
+    sample again `repeats - 1` times; the best of the repeats counts."""
     from threadpoolctl import threadpool_limits
 
     import oracle
+    threads = cpu_threads()
     rng = np.random.default_rng(0)
     order = rng.permutation(batch.num_seqs)
     qsl = batch.query_start_loc
     L = batch.seq_lens.astype(np.int64)
     ql = np.diff(qsl).astype(np.int64)
-    done_bytes = done_flops = 0
-    seqs = 0
     elem = 1 if batch.kv_dtype == "fp8_e4m3" else (2 if batch.dtype == "bf16" else 4)
     row_bytes = 2 * batch.num_kv_heads * batch.head_size * elem
-    t_total = 0.0
-    with threadpool_limits(limits=1):
+
+    def run(b):
+        oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, qsl, batch.seq_lens, batch.scale,
+                              np.arange(qsl[b], qsl[b + 1]), dtype=batch.dtype, causal=batch.causal,
+                              kv_dtype=batch.kv_dtype, k_scale=1.0 if batch.k_scale is None else batch.k_scale,
+                              v_scale=1.0 if batch.v_scale is None else batch.v_scale)
+
+    sample, times = [], []
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
         for b in order:
-            rows = np.arange(qsl[b], qsl[b + 1])
-            t0 = time.perf_counter()
-            oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, qsl, batch.seq_lens, batch.scale,
-                                  rows, dtype=batch.dtype, causal=batch.causal, kv_dtype=batch.kv_dtype,
-                                  k_scale=1.0 if batch.k_scale is None else batch.k_scale,
-                                  v_scale=1.0 if batch.v_scale is None else batch.v_scale)
-            t_total += time.perf_counter() - t0
-            seqs += 1
-            if ql[b] == 1:
-                done_bytes += int(L[b]) * row_bytes
-            else:
-                c = int(L[b] - ql[b])
-                done_flops += 4 * batch.num_heads * batch.head_size * int(ql[b] * c + ql[b] * (ql[b] + 1) // 2)
-            if t_total >= budget_s:
+            run(b)
+            sample.append(int(b))
+            if time.perf_counter() - t0 >= budget_s:
                 break
-    res = {"cores": 1, "kind": "oracle", "seconds": round(t_total, 3),
-           "sample": f"{seqs} of {batch.num_seqs} sequences of the same batch (numpy float64, 1 thread)",
+        times.append(time.perf_counter() - t0)
+        for _ in range(repeats - 1):
+            t0 = time.perf_counter()
+            for b in sample:
+                run(b)
+            times.append(time.perf_counter() - t0)
+    best = min(times)
+    done_bytes = sum(int(L[b]) * row_bytes for b in sample if ql[b] == 1)
+    done_flops = sum(4 * batch.num_heads * batch.head_size * int(ql[b] * (L[b] - ql[b]) + ql[b] * (ql[b] + 1) // 2)
+                     for b in sample if ql[b] != 1)
+    res = {"cores": threads, "kind": "oracle", "seconds": round(best, 3),
+           "seconds_each_repeat": [round(x, 3) for x in times],
+           "sample": f"{len(sample)} of {batch.num_seqs} sequences of the same batch (numpy float64, "
+                     f"BLAS threads = {threads} host cores; best of {len(times)})",
            "cpu_model": _cpu_model(), "blas": _blas_name()}
     if counts["decode_seqs"] and done_bytes:
-        res.update(value=done_bytes / t_total / 1e9, unit="GB/s")
+        res.update(value=done_bytes / best / 1e9, unit="GB/s")
     else:
-        res.update(value=done_flops / t_total / 1e12, unit="TFLOP/s")
+        res.update(value=done_flops / best / 1e12, unit="TFLOP/s")
     return res
 
 
@@ -500,7 +533,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the extra measurements: the prefill in the decode line, the mixed line's "
                          "sub-plans and the device-copy bandwidth")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle work in the cpu_baseline sample (timed 3 times)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -569,7 +603,9 @@ def main(argv=None) -> int:
                    "head_size": batch.head_size, "block_size": batch.block_size,
                    "common_prefix_len": batch.common_prefix_len, "seed": cfg,
                    "kv_split_tokens": m["plan"]["kv_split_tokens"]},
+        "step_event_ms": {k: round(v, 5) for k, v in t["step_event_ms"].items()},
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in t["kernels"].items()},
+        "kernel_launch_us": {k: launch_stats(v) for k, v in t["kernels"].items()},
     }
     bound = "hbm"
     if counts["decode_seqs"] and not counts["prefill_tokens"]:
@@ -583,7 +619,7 @@ def main(argv=None) -> int:
             line["cascade"] = {"effective_GBps_vs_naive_bytes": round(counts["decode_bytes_naive"] / (ms * 1e-3) / 1e9, 1),
                                "naive_bytes": counts["decode_bytes_naive"], "cascade_bytes": counts["decode_bytes"]}
         roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "launch_us": launch_stats(k)}
         roof["traffic"] = _traffic(kname, traffic_key)
     elif counts["prefill_tokens"] and not counts["decode_seqs"]:
         bound = "mfma"
@@ -593,7 +629,7 @@ def main(argv=None) -> int:
         ach = counts["prefill_flops"] / (k["avg_us"] * 1e-6) / 1e12
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": _traffic(kname, traffic_key)}
+                "frac": round(ach / peak, 4), "launch_us": launch_stats(k), "traffic": _traffic(kname, traffic_key)}
     else:
         # mixed step: the roofline of the whole step is max(bytes/BW, flops/peak)
         peak = MFMA_PEAK_TFLOPS[dtype]
@@ -605,9 +641,10 @@ def main(argv=None) -> int:
         dec_ach = counts["decode_bytes"] / (d["avg_us"] * 1e-6) / 1e9 if d else 0.0
         pre_ach = counts["prefill_flops"] / (p["avg_us"] * 1e-6) / 1e12 if p else 0.0
         roof = {"bound": "hbm", "kernel": kd, "achieved": round(dec_ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dec_ach / HBM_PEAK_GBS, 4), "traffic": _traffic(kd, traffic_key),
+                "frac": round(dec_ach / HBM_PEAK_GBS, 4), "launch_us": launch_stats(d) if d else None,
+                "traffic": _traffic(kd, traffic_key),
                 "prefill": {"kernel": kp, "achieved_TFLOPs": round(pre_ach, 2), "peak": peak,
-                            "frac": round(pre_ach / peak, 4)}}
+                            "frac": round(pre_ach / peak, 4), "launch_us": launch_stats(p) if p else None}}
         line["decode_GBps_step"] = round(counts["decode_bytes"] / (ms * 1e-3) / 1e9, 2)
         line["prefill_TFLOPs_step"] = round(counts["prefill_flops"] / (ms * 1e-3) / 1e12, 2)
     # extra measurements (left out of profiled runs with --no-secondary, so that
@@ -639,11 +676,14 @@ def main(argv=None) -> int:
         line["secondary"] = {
             "workload": DESCRIPTIONS[3],
             "ms_per_step": round(p["timing"]["ms_per_step"], 5),
+            "step_event_ms": {x: round(v, 5) for x, v in p["timing"]["step_event_ms"].items()},
             "value": round(pf / (p["timing"]["ms_per_step"] * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s",
             "roofline": {"bound": "mfma", "kernel": kp, "achieved": round(pf / (k["avg_us"] * 1e-6) / 1e12, 2),
                          "peak": MFMA_PEAK_TFLOPS["bf16"],
                          "frac": round(pf / (k["avg_us"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                         "launch_us": launch_stats(k),
+                         "frac_at_median_launch": round(pf / (k["median_us"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                          "traffic": _traffic(kp, "prefill")},
         }
         del p

@@ -104,6 +104,9 @@ typedef struct pa_params {
                                  needs dtype PA_BF16 (else PA_ERR_UNSUPPORTED) */
   int32_t kv_layout;          /* pa_kv_layout: 0 = NHD, 1 = HND; block sizes up to 1024 and beyond
                                  (any multiple of 16) work with either */
+  int32_t check_metadata;     /* 1: every forward first runs pa_plan_check_metadata on its device
+                                 arrays (a debugging mode: it waits for the stream and cannot be
+                                 captured into a graph); 0: the device arrays are trusted */
 } pa_params;
 
 /* Opaque, immutable schedule for one batch; reusable across layers and calls. */
@@ -151,6 +154,9 @@ typedef struct pa_kernel_time {
   char name[48];     /* kernel family, e.g. "decode_bf16_d128" */
   int32_t launches;  /* launches recorded */
   double total_ms;   /* summed device time between HIP events around each launch */
+  double min_ms;     /* shortest launch */
+  double median_ms;  /* median launch (mean of the two middle ones for an even count) */
+  double max_ms;     /* longest launch */
 } pa_kernel_time;
 
 /*
@@ -214,19 +220,43 @@ pa_status pa_plan_get_array(const pa_plan* plan, int32_t which, int32_t* dst, in
 size_t pa_plan_workspace_bytes(const pa_plan* plan);
 
 /*
+ * Compare device metadata with the host arrays the plan was built from
+ * («AttentionBackend: capa de abstracción», §Flujo de datos: the forward takes
+ * the metadata the builder produced; here the builder's copy drives the
+ * schedule, so the caller's device arrays must describe the same batch).
+ *  block_table     device int32[B * max_blocks_per_seq] or NULL (not compared).
+ *                  The used ids (the first ceil(L_b / bs) of row b) must equal the
+ *                  host table given to pa_plan_create; a plan made without one
+ *                  checks that they lie in [0, num_blocks).
+ *  query_start_loc device int32[B + 1] or NULL; must equal the plan's, entry for entry.
+ *  seq_lens        device int32[B] or NULL; likewise.
+ * Runs one small kernel on `stream` and waits for it (not capturable).
+ * Errors: INVALID_ARG (host-only plan, misaligned arrays, any difference: the
+ * message gives the count), HIP.
+ */
+pa_status pa_plan_check_metadata(const pa_plan* plan, const int32_t* block_table,
+                                 const int32_t* query_start_loc, const int32_t* seq_lens, void* stream);
+
+/*
  * Run attention for the planned batch.  «AttentionBackend: capa de abstracción»,
  * §Archivos clave: forward(layer, query, key, value, kv_cache, attn_metadata,
  * output); the new tokens' K/V are already in the pool (the cache write is a
  * separate step, «FlashAttention y FlashInfer», §Responsabilidades).
  *
- *  q           device [T, H, d], element type of the plan.
- *  kv_cache    device [num_blocks, 2, bs, Hkv, d], same element type.
+ *  q           device [T, H, d], element type of the plan, 16-byte aligned.
+ *  kv_cache    device [num_blocks, 2, bs, Hkv, d], same element type, 16-byte aligned.
  *  block_table device int32[B * max_blocks_per_seq]; the used ids must equal the
  *              host table given to (or implied by) the plan.
- *  out         device [T, H, d], same element type; fully written.
+ *  query_start_loc, seq_lens  device int32[B + 1] and int32[B], or NULL: the
+ *              batch's metadata (the attn_metadata of the pages' forward).  The
+ *              schedule comes from the plan's own copy, so the kernels do not
+ *              read them; with params.check_metadata = 1 they, and block_table,
+ *              are compared with the plan's first (pa_plan_check_metadata).
+ *  out         device [T, H, d], same element type, 16-byte aligned; fully written.
  *  lse         device float32[T, H] natural-log LSE, or NULL to skip it.
- *  workspace   device scratch of at least pa_plan_workspace_bytes(plan) bytes
- *              (NULL allowed when that is 0); contents need no initialisation.
+ *  workspace   device scratch of at least pa_plan_workspace_bytes(plan) bytes,
+ *              16-byte aligned (NULL allowed when that is 0); contents need no
+ *              initialisation.
  *  stream      hipStream_t (NULL = default stream).
  * Row order of out/lse is the caller's token order; the decode-first order only
  * affects the schedule.  The call is asynchronous and stream-ordered on
@@ -234,14 +264,18 @@ size_t pa_plan_workspace_bytes(const pa_plan* plan);
  * (and a shared-prefix pass, if any) runs on a side stream owned by the plan,
  * which first waits for `stream` and which `stream` waits for before the final
  * merge (event record/wait only, so the call can be captured into a graph);
- * otherwise every launch is on `stream`.  Concurrent calls
- * on one plan need separate workspaces, and their side-stream work serialises.
- * Errors: INVALID_ARG (host-only plan, NULL pointers, small workspace, a plan
- * whose pool holds e4m3 codes: those run through pa_forward_fp8), HIP (launch
- * failure).
+ * otherwise every launch is on `stream`.  Host threads may share a plan: each
+ * call needs its own workspace, calls on such a plan enqueue one at a time (a
+ * lock held while they record the fork/join events), and their side-stream work
+ * runs in the order they were made.
+ * Errors: INVALID_ARG (host-only plan, NULL or misaligned pointers, small
+ * workspace, metadata differing from the plan's when checked, a plan whose pool
+ * holds e4m3 codes: those run through pa_forward_fp8), HIP (launch failure).
+ * On error nothing is launched (a metadata check may have run).
  */
 pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
-                     const int32_t* block_table, void* out, float* lse, void* workspace,
+                     const int32_t* block_table, const int32_t* query_start_loc,
+                     const int32_t* seq_lens, void* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
 /*
@@ -256,11 +290,12 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
  *              they may change between calls without a new plan.  Positive and
  *              finite (not checked on the device).
  * Everything else as pa_forward.  Errors: INVALID_ARG (as pa_forward, a plan
- * without an e4m3 pool, NULL scales, num_scales not 1 or Hkv, misaligned pool),
- * HIP.
+ * without an e4m3 pool, NULL or misaligned scales, num_scales not 1 or Hkv,
+ * misaligned pool), HIP.
  */
 pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cache,
-                         const int32_t* block_table, const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, const int32_t* query_start_loc,
+                         const int32_t* seq_lens, const float* k_scale, const float* v_scale,
                          int32_t num_scales, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream);
 
@@ -347,8 +382,8 @@ const char* pa_last_error(void);
  * pa_profile_start(max_launches), every launch made by this thread records a
  * HIP event before and after it, on the launch's stream, up to max_launches.
  * pa_profile_stop waits for the recorded events, sums device time per kernel
- * family into out (host, `capacity` entries; *count receives how many) and
- * ends the session.  Errors: INVALID_ARG (no session / bad sizes), HIP.
+ * family into out (host, `capacity` entries; *count receives how many) with
+ * the shortest, median and longest launch, and ends the session.  Errors: INVALID_ARG (no session / bad sizes), HIP.
  */
 pa_status pa_profile_start(int32_t max_launches);
 pa_status pa_profile_stop(pa_kernel_time* out, int32_t capacity, int32_t* count);

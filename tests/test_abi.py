@@ -128,7 +128,7 @@ def test_e4m3_write_validates_before_any_launch():
 def test_e4m3_forward_needs_a_device_plan_and_scales():
     plan = pa.pa_plan_create(_fp8_params(), [0, 1, 65], [40, 64], device=-1)
     with pytest.raises(pa.PagedAttnError) as ei:
-        pa.pa_forward_fp8(plan, 16, 16, 16, 16, 16, 16, num_scales=2, stream=0)
+        pa.pa_forward_fp8(plan, 16, 16, 16, None, None, 16, 16, 16, num_scales=2, stream=0)
     assert ei.value.status == pa.PA_ERR_INVALID_ARG
 
 

@@ -20,7 +20,7 @@ def test_empty_batch_launches_nothing():
     plan = pa.pa_plan_create(params, [0], [], np.zeros((0, 1), np.int32), device=0)
     assert pa.pa_plan_get_info(plan)["num_tokens"] == 0
     assert pa.pa_plan_workspace_bytes(plan) == 0
-    pa.pa_forward(plan, 0, 0, 0, 0)          # no rows: nothing is launched or read
+    pa.pa_forward(plan, 0, 0, 0, None, None, 0)  # no rows: nothing is launched or read
     torch.cuda.synchronize()
 
 

@@ -1,15 +1,16 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
 
-Small batches are compared on every element; the full-size workloads on
-sampled rows the oracle computes one by one, plus properties that hold at any
-size (finite outputs, cascade = non-cascade).  Gathers are bit-exact.
+Small batches are compared on every element; the full-size workloads on every
+row (decode-only, chunked-prefill mixed, cascade) or a dense spread of rows of
+every prompt (causal varlen prefill), plus properties that hold at any size
+(finite outputs, cascade = non-cascade).  Gathers are bit-exact.
 """
 import numpy as np
 import pytest
 
 import attention_paged_kv_varlen_amd as pa
 import oracle
-from tests.gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, oracle_full, run_gpu, sample_rows
+from tests.gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, oracle_full, run_gpu
 from workloads import config_batch, f32_to_bf16_bits, make_batch
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +103,41 @@ def test_cascade_small_matches_oracle_and_non_cascade():
     po, pl, _ = run_gpu(batch, common_prefix_len=0)
     assert_close(po, pl, ref_o, ref_l, "non-cascade vs oracle")
     assert_close(co, cl, po, pl, "cascade vs non-cascade")
+
+
+# A shared prefix with decodes alone: the prefix pass, then balanced decode
+# lists over the suffixes (starting at P), then the merge.  Pieces of a list may
+# start off a 32-key boundary of the sequence (P = 16 x odd), pages may hold
+# 128 keys in HND order, and the pool may hold e4m3 codes.
+CASCADE_DECODES = {
+    "bf16_bs16_P128": dict(P=128, block_size=16),
+    "bf16_bs16_P16x21": dict(P=16 * 21, block_size=16),
+    "fp32_bs16_P64": dict(P=64, block_size=16, dtype="fp32"),
+    "bf16_hnd_bs128_P256": dict(P=256, block_size=128, kv_layout="HND"),
+    "e4m3_bs16_P144": dict(P=144, block_size=16, kv_dtype="fp8_e4m3"),
+    "bf16_g8_bs64_P192": dict(P=192, block_size=64, num_heads=16),
+}
+
+
+@pytest.mark.parametrize("name", list(CASCADE_DECODES))
+def test_cascade_decodes_only_match_oracle(name):
+    kw = dict(CASCADE_DECODES[name])
+    P = kw.pop("P")
+    kw.setdefault("num_heads", 8)
+    rng = np.random.default_rng(23)
+    extra = rng.integers(1, 900, size=14).tolist() + [1, 31, 33, 1000]
+    lens = [P + e for e in extra]
+    batch = make_batch([1] * len(lens), lens, num_kv_heads=2, head_size=128, seed=24,
+                       shared_prefix_blocks=P // kw["block_size"], **kw)
+    announce(f"cascade decodes only {name} B={batch.num_seqs} P={P}")
+    co, cl, db = run_gpu(batch)
+    info = pa.pa_plan_get_info(db.plan)
+    assert info["num_prefill_items"] == 0 and info["num_prefix_items"] > 0
+    assert 0 < info["num_decode_lists"] < info["num_decode_items"] and info["decode_list_tokens"] > 0
+    ref_o, ref_l = oracle_full(batch)
+    assert_close(co, cl, ref_o, ref_l, f"{name} cascade vs oracle")
+    po, pl, _ = run_gpu(batch, common_prefix_len=0)
+    assert_close(po, pl, ref_o, ref_l, f"{name} non-cascade vs oracle")
 
 
 @pytest.mark.parametrize("split", [32, 96, 512, 0])
@@ -257,8 +293,8 @@ def test_forward_rejects_small_workspace_and_keeps_outputs():
     assert need > 0
     db.out.fill_(3.0)
     with pytest.raises(pa.PagedAttnError) as ei:
-        pa.pa_forward(db.plan, db.q, db.kv_cache, db.block_table, db.out, db.lse, db.workspace,
-                      workspace_bytes=need - 1)
+        pa.pa_forward(db.plan, db.q, db.kv_cache, db.block_table, db.query_start_loc, db.seq_lens, db.out, db.lse,
+                      db.workspace, workspace_bytes=need - 1)
     assert ei.value.status == pa.PA_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert bool(torch.all(db.out.float() == 3.0))
@@ -287,15 +323,45 @@ def test_profile_records_kernel_times():
 # Full-size workloads
 # ---------------------------------------------------------------------------
 
+def full_config_rows(batch, cfg):
+    """Rows of a full-size workload compared with the oracle: every row of the
+    decode-only, chunked-prefill mixed and cascade workloads (the oracle takes
+    seconds for them), and for the causal varlen prefill (1.7 TFLOP of dense
+    float64 work in all) the first and last 8 rows of every prompt plus 48
+    spread between them (so every prompt's first, middle and last tiles and
+    its ragged tail are covered)."""
+    qsl = batch.query_start_loc
+    if cfg != 3:
+        return np.arange(int(qsl[-1]), dtype=np.int64)
+    rows = []
+    for b in range(batch.num_seqs):
+        r0, r1 = int(qsl[b]), int(qsl[b + 1])
+        rows += list(range(r0, min(r0 + 8, r1))) + list(range(max(r0, r1 - 8), r1))
+        rows += np.linspace(r0, r1 - 1, 48).astype(np.int64).tolist()
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+def _row_kinds(batch, rows):
+    ql = np.diff(batch.query_start_loc)
+    seq = np.searchsorted(batch.query_start_loc, rows, side="right") - 1
+    dec = ql[seq] == 1
+    return int(dec.sum()), int((~dec).sum()), len(np.unique(seq[~dec]))
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_config_sampled_rows(cfg):
+def test_full_config_against_oracle(cfg):
     announce(f"full config {cfg}: generating")
     batch = config_batch(cfg)
     announce(f"full config {cfg}: B={batch.num_seqs} T={batch.num_tokens} pool={batch.kv_cache.nbytes / 1e9:.2f} GB")
     out, lse, _ = run_gpu(batch)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
-    rows = sample_rows(batch, seed=cfg)
+    rows = full_config_rows(batch, cfg)
+    n_dec, n_pre, n_pre_seqs = _row_kinds(batch, rows)
+    announce(f"full config {cfg}: comparing {len(rows)} of {batch.num_tokens} rows with the oracle "
+             f"({n_dec} decode rows, {n_pre} prefill rows of {n_pre_seqs} sequences)")
+    if cfg == 4:  # all four chunks, every row
+        assert n_pre == 4 * 512 and n_pre_seqs == 4
     ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
                                          batch.seq_lens, batch.scale, rows, dtype=batch.dtype)
     assert_close(out[rows], lse[rows], ref_o, ref_l, f"config {cfg} ({len(rows)} rows)")
@@ -307,12 +373,16 @@ def test_full_config5_cascade():
     batch = config_batch(5)
     announce(f"full config 5: B={batch.num_seqs} P={batch.common_prefix_len}")
     co, cl, db = run_gpu(batch)
+    info = pa.pa_plan_get_info(db.plan)
+    assert info["common_prefix_len"] == batch.common_prefix_len and info["num_prefix_items"] > 0
     po, pl, _ = run_gpu(batch, common_prefix_len=0)
     assert_close(co, cl, po, pl, "config 5 cascade vs non-cascade (all rows)")
-    rows = sample_rows(batch, seed=5)
+    rows = full_config_rows(batch, 5)
+    announce(f"full config 5: comparing all {len(rows)} rows (cascade and non-cascade) with the oracle")
     ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
                                          batch.seq_lens, batch.scale, rows, dtype=batch.dtype)
     assert_close(co[rows], cl[rows], ref_o, ref_l, f"config 5 cascade ({len(rows)} rows)")
+    assert_close(po[rows], pl[rows], ref_o, ref_l, f"config 5 non-cascade ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])

@@ -190,7 +190,7 @@ def test_query_start_loc_must_start_at_zero():
 
 def test_host_only_plan_cannot_run():
     plan, _ = host_plan([1], [10])
-    assert _status(lambda: pa.pa_forward(plan, 1, 1, 1, 1, None, None, 0, stream=0)) == pa.PA_ERR_INVALID_ARG
+    assert _status(lambda: pa.pa_forward(plan, 16, 16, 16, None, None, 16, None, None, 0, stream=0)) == pa.PA_ERR_INVALID_ARG
 
 
 def test_workspace_size_accounts_for_partials():
