@@ -35,6 +35,7 @@ from ._capi import (  # noqa: F401
     make_params,
     pa_forward,
     pa_forward_fp8,
+    pa_forward_noalloc,
     pa_gather_kv,
     pa_kv_cache_shape,
     pa_kv_cache_stride_order,

@@ -25,7 +25,7 @@ PA_KV_NHD, PA_KV_HND = 0, 1
 # Every symbol include/pagedattn.h declares.
 EXPORTED = (
     "pa_kv_cache_shape", "pa_kv_cache_stride_order", "pa_plan_create", "pa_plan_get_info", "pa_plan_get_array",
-    "pa_plan_workspace_bytes", "pa_plan_check_metadata", "pa_forward", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
+    "pa_plan_workspace_bytes", "pa_plan_check_metadata", "pa_forward", "pa_forward_noalloc", "pa_forward_fp8", "pa_merge_states", "pa_gather_kv", "pa_write_kv",
     "pa_write_kv_fp8", "pa_plan_destroy", "pa_status_string", "pa_last_error", "pa_profile_start",
     "pa_profile_stop",
 )
@@ -92,6 +92,8 @@ def lib():
                                   c_int32, c_int32, c_void_p]
     L.pa_gather_kv.argtypes = [c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p, c_void_p]
     L.pa_write_kv.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p]
+    L.pa_forward_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p]
     L.pa_forward_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     L.pa_write_kv_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, POINTER(pa_params), c_void_p, c_void_p,
@@ -235,6 +237,12 @@ def pa_forward(plan: Plan, q, kv_cache, block_table, query_start_loc, seq_lens, 
     _check(lib().pa_forward(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
                             _ptr(seq_lens), _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
                             _stream(stream)))
+
+
+def pa_forward_noalloc(plan: Plan, q, kv_cache, block_table, query_start_loc, seq_lens, out, lse=None,
+                       stream=None) -> None:
+    _check(lib().pa_forward_noalloc(plan.handle, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(query_start_loc),
+                                    _ptr(seq_lens), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def pa_forward_fp8(plan: Plan, q, kv_cache, block_table, query_start_loc, seq_lens, k_scale, v_scale, out, lse=None,

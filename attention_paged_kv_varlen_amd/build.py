@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["kernels.hip", "planner.cpp", "api.cpp"]
+SOURCES = ["kernels.hip", "noalloc.hip", "planner.cpp", "api.cpp"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -279,6 +279,25 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * pa_forward for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, with the partial-result workspace in a static device array of
+ * 64 MiB that the library holds on each device it runs on (until the process
+ * ends) instead of caller memory.  The call itself allocates nothing; its first
+ * call for a device looks the array's address up.
+ *  Arguments as pa_forward, without workspace.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one GPU (other streams, other threads) race on it and must be
+ * serialised by the caller.  Nothing in the array needs clearing: every
+ * partial record a forward reads is written earlier in the same forward.
+ * Errors: as pa_forward; INVALID_ARG when pa_plan_workspace_bytes(plan)
+ * exceeds 64 MiB (use pa_forward with a workspace); HIP.
+ */
+pa_status pa_forward_noalloc(const pa_plan* plan, const void* q, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* query_start_loc,
+                             const int32_t* seq_lens, void* out, float* lse, void* stream);
+
+/*
  * pa_forward over a pool of e4m3 codes (plan made with kv_dtype =
  * PA_KV_FP8_E4M3): the keys and values are decode(code) * k_scale and
  * decode(code) * v_scale («FlashAttention y FlashInfer», §Motivación de diseño
