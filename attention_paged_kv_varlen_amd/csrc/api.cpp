@@ -22,10 +22,10 @@ struct pa_plan {
   pa::DeviceSchedule ds{};
   size_t ws_bytes = 0;
   // side stream and fork/join events, created with the plan when it holds both
-  // decode work and prefill work, so that the MFMA-bound launches overlap the
-  // HBM-bound decode (a shared-prefix pass without prefills runs before the
-  // decode on the caller's stream: beside it the decode lost more than the
-  // overlap gained)
+  // decode work and prefill work, or a shared-prefix pass that runs beside the
+  // decode on CUs of its own, so that the MFMA-bound launches overlap the
+  // HBM-bound decode (otherwise a shared-prefix pass runs before the decode on
+  // the caller's stream)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // Held by a forward from its event record on the caller's stream to the
@@ -245,11 +245,12 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
     ds.decode_lists = reinterpret_cast<const int32_t*>(base + sec[5].off);
     ds.n_decode_lists = hp.decode_lists.empty() ? 0 : (int)hp.decode_lists.size() - 1;
     ds.num_partials = hp.num_partials;
+    ds.prefix_beside = hp.prefix_beside;
     plan->dev_qsl = reinterpret_cast<const int32_t*>(base + sec[6].off);
     plan->dev_seq_lens = reinterpret_cast<const int32_t*>(base + sec[7].off);
     plan->dev_bt = hp.block_table.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + sec[8].off);
     plan->dev_check = reinterpret_cast<int32_t*>(base + sec[9].off);
-    if (!hp.decode_items.empty() && !hp.prefill_items.empty()) {
+    if (!hp.decode_items.empty() && (!hp.prefill_items.empty() || hp.prefix_beside)) {
       e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);

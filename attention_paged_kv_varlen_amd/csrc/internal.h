@@ -85,6 +85,7 @@ struct DeviceSchedule {
   int n_merge;
   const int32_t* row_pbase;
   int num_partials;
+  bool prefix_beside;  // see HostPlan::prefix_beside
 };
 
 struct Tensors {
@@ -166,6 +167,9 @@ struct HostPlan {
   pa_plan_info info{};
   PrefillShape ps{};
   int num_partials = 0;
+  // the shared-prefix pass runs beside the decode on CUs of its own (8-wave
+  // prefix workgroups, decode lists sized for the other CUs)
+  bool prefix_beside = false;
 };
 
 // Decode launch shape: the Hkv x ceil(g / 16) units of an item are run by

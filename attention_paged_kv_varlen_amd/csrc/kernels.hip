@@ -473,14 +473,13 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
 
     // One physical block per 16-key tile.  Keys past kv_end are clamped to the
     // last valid key (so only pool rows of this sequence are read) and masked.
-    // A step is 32 keys.  With DB (bf16 queries; the launch leaves it off
-    // beside a shared-prefix pass, whose decode items are short) two steps are
-    // in flight: the raw K/V loads of step t + 32 are issued before the
-    // arithmetic of step t (the steps alternate between two register sets, so
-    // nothing is copied); the block ids of the step after that are fetched
-    // meanwhile.  With NT (no prefill beside the decode) the K/V loads carry
-    // the non-temporal hint: the pool is streamed once, and a decode alone
-    // then reads HBM about 9 % faster; beside a prefill it is slower.
+    // A step is 32 keys.  With DB (bf16 queries) two steps are in flight:
+    // the raw K/V loads of step t + 32 are issued before the arithmetic of
+    // step t (the steps alternate between two register sets, so nothing is
+    // copied); the block ids of the step after that are fetched meanwhile.
+    // With NT (no MFMA work beside the decode) the K/V loads carry the
+    // non-temporal hint: the pool is streamed once, and a decode alone then
+    // reads HBM about 9 % faster; beside a prefill it is slower.
     auto tile_block = [&](int t) { return page_index(a, min(t, kv_end - 1)); };
     struct Raw {
       RawK k[2];
@@ -1574,16 +1573,13 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
     d.lists = s.decode_lists;
     const int64_t nwg = (int64_t)s.n_decode_lists * (nhg / nw);
     if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-    // two steps in flight unless beside a shared-prefix pass; non-temporal
-    // K/V loads unless a prefill runs beside the decode
+    // two steps in flight (bf16 queries); non-temporal K/V loads unless
+    // MFMA work (prefills, the shared-prefix pass) runs beside the decode
     const dim3 dg((unsigned)nwg), db(64 * nw);
+    const bool beside = s.n_prefill > 0 || s.prefix_beside;
     if constexpr (sizeof(T) == 2) {
-      if (s.n_prefix > 0)
-        err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, false, false>, dg, db, stream, d)
-                              : launch(name, decode_kernel<T, KV, D, false, true>, dg, db, stream, d);
-      else
-        err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, true, false>, dg, db, stream, d)
-                              : launch(name, decode_kernel<T, KV, D, true, true>, dg, db, stream, d);
+      err = beside ? launch(name, decode_kernel<T, KV, D, true, false>, dg, db, stream, d)
+                   : launch(name, decode_kernel<T, KV, D, true, true>, dg, db, stream, d);
     } else {
       err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, false, false>, dg, db, stream, d)
                             : launch(name, decode_kernel<T, KV, D, false, true>, dg, db, stream, d);

@@ -39,7 +39,7 @@ PrefillShape prefill_shape(int group, int tiles, int max_heads) {
 
 namespace {
 
-constexpr int kPrefixChunk = 1024;  // shared-prefix keys per cascade work item
+constexpr int kPrefixChunk = 1024;  // shared-prefix keys per cascade work item (prefix before the decode)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -69,6 +69,17 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
   if (t_dec + t_pre <= 0.0) return 0.75;
   return std::min(0.75, std::max(0.25, t_dec / (t_dec + t_pre)));
 }
+
+// Rates of this library's kernels on one MI355X CU (measured on a shared-prefix
+// batch): the 8-wave wide prefill executes about 3.6 TFLOP/s of MFMA work per
+// CU on long non-causal units, and a decode workgroup draws about 25 GB/s
+// from HBM (the decode as a whole at most about 6.5 TB/s).  A unit's fixed
+// cost (its Q rows in, the first K/V block's latency, its output out) is
+// worth about 192 keys.
+constexpr double kPrefixFlopsPerCu = 3.6e12;
+constexpr double kDecodeBytesPerCu = 25.0e9;
+constexpr double kDecodeBytesAll = 6.5e12;
+constexpr int kUnitOverheadKeys = 192;
 
 pa_status fail(std::string& err, pa_status st, const char* fmt, long long a = 0, long long b = 0,
                long long c = 0) {
@@ -193,6 +204,11 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (P > 0) hp.prefix_blocks.assign(block_table, block_table + P / bs);
 
   // ---- schedule
+  int64_t dec_tokens = 0;
+  for (int i = 0; i < nd; ++i) dec_tokens += seq_lens[hp.order[i]] - P;
+  const int dec_units = Hkv * ((g + 15) / 16);
+  const int dec_nw = decode_waves_per_wg(dec_units);
+  const bool balanced = p.kv_split_tokens == 0 && nd > 0 && decode_wgs_per_cu > 0;
   // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
   if (use_wide_prefill(p.dtype, p.head_size, p.kv_dtype)) {
     const int tiles = wide_prefill_tiles(nd > 0, P, p.kv_dtype);
@@ -200,9 +216,41 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   } else {
     hp.ps = prefill_shape(g, 8, 8);
   }
+  int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
+
+  // Shared prefix beside the decode.  With decodes only (bf16 pool, head size
+  // 128, automatic split) the prefix pass runs at the same time as the decode,
+  // on CUs of its own: one 8-wave workgroup per prefix unit (chunk, column
+  // group, KV head), each filling a CU's registers, while the decode lists are
+  // sized for the remaining CUs.  The chunk count sets how many CUs the prefix
+  // takes; it is chosen so that the two finish together (the rates above).
+  if (P > 0 && np == 0 && balanced && use_wide_prefill(p.dtype, p.head_size, p.kv_dtype) &&
+      p.kv_dtype == PA_KV_SAME) {
+    const PrefillShape s16 = prefill_shape(g, 16, 8);
+    const int per_chunk = (int)ceil_div(hp.T, s16.rows_per_item) * Hkv * s16.head_groups;
+    const double dec_bytes = (double)dec_tokens * 2.0 * Hkv * p.head_size * 2.0;
+    double best_t = 0.0;
+    int best_c = 0;
+    for (int c = 1; c <= ceil_div(P, 64) && (int64_t)c * per_chunk <= num_cus - 8; ++c) {
+      const int len = (int)round_up(ceil_div(P, c), 64);
+      const int units = (int)ceil_div(P, len) * per_chunk;
+      const double t_pfx = 16.0 * s16.tiles * (len + kUnitOverheadKeys) * 4.0 * p.head_size / kPrefixFlopsPerCu;
+      const double t_dec = dec_bytes / std::min(kDecodeBytesAll, (num_cus - units) * kDecodeBytesPerCu);
+      const double t = std::max(t_pfx, t_dec);
+      if (best_c == 0 || t < best_t) {
+        best_t = t;
+        best_c = c;
+      }
+    }
+    if (best_c > 0) {
+      hp.ps = s16;
+      n_pc = best_c;
+      hp.prefix_beside = true;
+    }
+  }
   const int QB = hp.ps.rows_per_item;
-  const int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
   const int pc_len = P > 0 ? (int)round_up(ceil_div(P, n_pc), 64) : 0;
+  if (P > 0) n_pc = (int)ceil_div(P, pc_len);  // no empty chunk
 
   // Decode schedule.  With the automatic split the decodes get balanced work
   // lists: the decode keys (past the shared prefix, if any), sequence after
@@ -211,19 +259,17 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   // start the next; each piece is an item with its own partial record).
   // Beside prefills the lists take only a share of the resident groups (see
   // decode_share) and the prefill runs on the rest of the machine meanwhile;
-  // a shared-prefix pass without prefills runs before the decode instead.
+  // beside a shared-prefix pass (above) they cover the CUs it leaves free,
+  // and otherwise a shared-prefix pass runs before the decode.
   // With an explicit split each decode is cut into equal parts of at most
   // `split` keys, one item per list, longest first.
-  int64_t dec_tokens = 0;
-  for (int i = 0; i < nd; ++i) dec_tokens += seq_lens[hp.order[i]] - P;
-  const int dec_units = Hkv * ((g + 15) / 16);
-  const int dec_nw = decode_waves_per_wg(dec_units);
-  const bool balanced = p.kv_split_tokens == 0 && nd > 0 && decode_wgs_per_cu > 0;
   int split = p.kv_split_tokens;
   int list_tokens = 0;
   if (balanced) {
     // resident list groups: workgroups per CU x CUs / workgroups per list
-    int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * std::max(num_cus, 1) * dec_nw / dec_units);
+    const int prefix_cus = hp.prefix_beside ? n_pc * (int)ceil_div(hp.T, QB) * Hkv * hp.ps.head_groups : 0;
+    const int dec_cus = std::max(num_cus - prefix_cus, 1);
+    int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * dec_cus * dec_nw / dec_units);
     if (np > 0) lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
     // A list is closed with up to 31 keys of room unused (cuts inside a
@@ -402,6 +448,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   in.decode_tokens_read = dec_read * Hkv;
   in.prefill_tokens_read = pre_read * Hkv;
   in.prefix_tokens_read = pfx_read * Hkv;
+  in.prefix_tokens_unique = (int64_t)P * Hkv;
+  in.prefix_beside_decode = hp.prefix_beside ? 1 : 0;
   in.kv_tokens_read = in.decode_tokens_read + in.prefill_tokens_read + in.prefix_tokens_read;
   return PA_OK;
 }

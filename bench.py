@@ -602,7 +602,10 @@ def main(argv=None) -> int:
                    "num_heads": batch.num_heads, "num_kv_heads": batch.num_kv_heads,
                    "head_size": batch.head_size, "block_size": batch.block_size,
                    "common_prefix_len": batch.common_prefix_len, "seed": cfg,
-                   "kv_split_tokens": m["plan"]["kv_split_tokens"]},
+                   "kv_split_tokens": m["plan"]["kv_split_tokens"],
+                   "decode_lists": m["plan"]["num_decode_lists"],
+                   "prefix_beside_decode": m["plan"]["prefix_beside_decode"],
+                   "prefix_items": m["plan"]["num_prefix_items"]},
         "step_event_ms": {k: round(v, 5) for k, v in t["step_event_ms"].items()},
         "kernels_us": {k: round(v["avg_us"], 3) for k, v in t["kernels"].items()},
         "kernel_launch_us": {k: launch_stats(v) for k, v in t["kernels"].items()},

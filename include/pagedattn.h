@@ -136,6 +136,13 @@ typedef struct pa_plan_info {
   int64_t prefix_tokens_read;   /* of which rows of the shared prefix */
   int64_t decode_tokens_read;   /* of which by decode work items */
   int64_t prefill_tokens_read;  /* of which by prefill work items */
+  int64_t prefix_tokens_unique; /* distinct (KV head, prefix token) rows the prefix pass reads: P * Hkv
+                                   (prefix_tokens_read counts each column group's read; groups of
+                                   one KV head and chunk run together on one XCD and share its L2) */
+  int32_t prefix_beside_decode; /* 1: the shared-prefix pass runs beside the decode on CUs of its
+                                   own (one prefix workgroup per CU; the decode lists cover the
+                                   others); 0: before it, or no prefix */
+  int32_t pad_;
 } pa_plan_info;
 
 /* Arrays a plan exposes through pa_plan_get_array. */

@@ -77,14 +77,19 @@ def test_wide_prefill_takes_eight_waves_beside_decodes():
     """bf16 pool, head size 128, g = 4: a prefill alone runs 4-wave workgroups
     of 8 column tiles (32 positions of 4 heads); beside decodes, 8-wave
     workgroups of 16 tiles (64 positions), which fill a CU each; a shared
-    prefix keeps the 4-wave shape, and so do an e4m3 pool and fp32 queries."""
+    prefix beside decodes alone takes the 8-wave shape too, with prefills the
+    4-wave one; an e4m3 pool and fp32 queries keep 4 waves."""
     _, alone = host_plan([100], [100])
     _, mixed = host_plan([1, 100], [300, 100])
     assert alone["prefill_rows_per_item"] == 32 and mixed["prefill_rows_per_item"] == 64
     bt = np.zeros((2, 20), dtype=np.int32)
     bt[1, 1:] = np.arange(1, 20)
+    # a shared prefix with decodes alone runs beside the decode in 8-wave
+    # workgroups; with a prefill as well, before it in 4-wave workgroups
     _, casc = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
-    assert casc["prefill_rows_per_item"] == 32
+    assert casc["prefill_rows_per_item"] == 64 and casc["prefix_beside_decode"] == 1
+    _, cpre = host_plan([1, 20], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
+    assert cpre["prefill_rows_per_item"] == 32 and cpre["prefix_beside_decode"] == 0
     _, f32 = host_plan([1, 100], [300, 100], dtype="fp32")
     assert f32["prefill_rows_per_item"] == 32
     params = pa.make_params(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=40,
@@ -141,6 +146,9 @@ def test_cascade_read_counts_match_the_read_model():
     casc_info = ic
     assert ip["kv_tokens_read"] == model["naive"] * Hkv
     groups = -(-R // casc_info["prefill_rows_per_item"])
+    # the prefix rows the plan reads, each once per KV head (the page's model),
+    # and the reads of its column groups, which run together on one XCD
+    assert ic["prefix_tokens_unique"] == model["prefix_cascade"] * Hkv
     assert ic["prefix_tokens_read"] == groups * P * Hkv
     assert ic["decode_tokens_read"] == int(s.sum()) * Hkv
     assert ic["kv_tokens_read"] == (groups * P + int(s.sum())) * Hkv
@@ -332,3 +340,37 @@ def test_decode_lists_beside_prefills_take_a_share_of_the_machine(heavy):
     else:
         assert n <= 128
     _covers_decodes_in_order(plan, np.asarray(lens), spans[:, :3])
+
+
+def test_prefix_beside_decode_takes_cus_of_its_own():
+    """Shared prefix, decodes alone (the cascade workload's shape): the prefix
+    pass is cut into chunks whose 8-wave units (chunk, 64-row column group, KV
+    head) each take one CU, and the decode lists cover the other CUs; the
+    chunks tile [0, P) and every row merges the prefix chunks with its suffix
+    pieces."""
+    qlens, lens, sp = config_lengths(5)
+    R, P, bs, Hkv = len(lens), 16384, 16, 8
+    mbs = int(max(-(-int(L) // bs) for L in lens))
+    bt = np.zeros((R, mbs), dtype=np.int32)
+    nxt = P // bs
+    for b in range(R):
+        bt[b, :P // bs] = np.arange(P // bs)
+        own = -(-int(lens[b]) // bs) - P // bs
+        bt[b, P // bs:P // bs + own] = np.arange(nxt, nxt + own)
+        nxt += own
+    plan, info = host_plan(qlens, lens, H=32, Hkv=Hkv, bs=bs, block_table=bt, num_blocks=nxt, mbs=mbs, prefix=P)
+    assert info["prefix_beside_decode"] == 1 and info["prefill_rows_per_item"] == 64
+    groups = -(-R // 64)
+    units = info["num_prefix_items"] * Hkv
+    chunks = info["num_prefix_items"] // groups
+    assert info["num_prefix_items"] == chunks * groups and 1 <= chunks <= P // 64
+    assert 8 <= units <= 256 - 8
+    # decode lists: one 8-wave group per CU the prefix leaves free (host-only
+    # plans assume 256 CUs and one decode workgroup per CU)
+    assert info["num_decode_lists"] <= 256 - units
+    assert info["prefix_tokens_read"] == groups * P * Hkv and info["prefix_tokens_unique"] == P * Hkv
+    parts = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS)
+    spans = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_SPANS).reshape(-1, 3)
+    pieces = np.bincount(spans[:, 0], minlength=R)
+    assert np.all(spans[:, 1] >= P)
+    assert np.array_equal(parts, chunks + pieces)
