@@ -924,24 +924,23 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   // clamped); looked up one block ahead so the lookup's latency is covered by
   // the wait before the next barrier
   auto page_of = [&](int kb) { return btrow[page_index(a, min(kb + RPW * wave, kv_hi - 1))]; };
-  // e4m3: this wave's slab of the next block, 16 codes per lane and load (row
-  // 8 i + lane / 8 of the slab, codes 16 (lane % 8) .. +15): K in st8[0..1],
-  // V in st8[2..3]
-  u32x4 st8[4];
-  auto issue = [&](int kb, int stage, int pid) {
+  // e4m3: this wave's slab of the next block's K codes, or of its V codes
+  // (part 0 / 1; staged one after the other, so that only one is held in
+  // registers at a time), 16 codes per lane and load (row 8 i + lane / 8 of
+  // the slab, codes 16 (lane % 8) .. +15)
+  u32x4 st8[2];
+  auto issue = [&](int kb, int stage, int pid, int part = 0) {
     pid = __builtin_amdgcn_readfirstlane(pid);
     const int key0 = kb + RPW * wave;  // wave-uniform
     if constexpr (F8) {
       // rows past the end re-read the last valid key (masked later); the
       // slab lies in one physical block
       const int pst = page_index(a, min(key0, kv_hi - 1)) * a.bs;
-      const KV* page = kvh_base + (int64_t)pid * blk_stride;
+      const KV* page = kvh_base + (int64_t)pid * blk_stride + (part ? v_half : 0);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int key = min(key0 + 8 * i + (lane >> 3), kv_hi - 1);
-        const KV* src = page + (int64_t)(key - pst) * slot_stride + 16 * (lane & 7);
-        st8[i] = *reinterpret_cast<const u32x4*>(src);
-        st8[2 + i] = *reinterpret_cast<const u32x4*>(src + v_half);
+        st8[i] = *reinterpret_cast<const u32x4*>(page + (int64_t)(key - pst) * slot_stride + 16 * (lane & 7));
       }
       return;
     }
@@ -978,12 +977,12 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       }
     }
   };
-  // e4m3: widen the staged codes into LDS stage `stage` (bf16, same swizzled
-  // layout as the direct-to-LDS loads); chunk 2 (lane % 8) and its successor of
-  // the row hold codes 0..7 and 8..15 of the lane's load
-  auto commit = [&](int stage) {
+  // e4m3: widen the staged codes (part 0: K, 1: V) into LDS stage `stage`
+  // (bf16, same swizzled layout as the direct-to-LDS loads); chunk 2 (lane % 8)
+  // and its successor of the row hold codes 0..7 and 8..15 of the lane's load
+  auto commit = [&](int stage, int part = 0) {
     if constexpr (F8) {
-      unsigned char* base = stage ? lds1 : lds0;
+      unsigned char* base = (stage ? lds1 : lds0) + (part ? kWideBlk : 0);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = RPW * wave + 8 * i + (lane >> 3);
@@ -992,8 +991,6 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
         unsigned char* rk = base + row * kWideRow;
         *reinterpret_cast<u32x4*>(rk + 16 * (c ^ sw)) = e4m3x8_to_bf16(st8[i][0], st8[i][1]);
         *reinterpret_cast<u32x4*>(rk + 16 * ((c + 1) ^ sw)) = e4m3x8_to_bf16(st8[i][2], st8[i][3]);
-        *reinterpret_cast<u32x4*>(rk + kWideBlk + 16 * (c ^ sw)) = e4m3x8_to_bf16(st8[2 + i][0], st8[2 + i][1]);
-        *reinterpret_cast<u32x4*>(rk + kWideBlk + 16 * ((c + 1) ^ sw)) = e4m3x8_to_bf16(st8[2 + i][2], st8[2 + i][3]);
       }
     }
   };
@@ -1036,12 +1033,23 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
     // have, and every wave is done reading the other stage (block jb - 1)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (jb + 1 < nblk) {
-      issue(kb + kWideKT, STAGE ^ 1, pnext);
+    // the next block's loads: direct-to-LDS; or e4m3 K codes now, widened
+    // into LDS after the first half, then the V codes, widened at the end
+    const bool more = jb + 1 < nblk;
+    const int pid = pnext;
+    if (more) {
+      issue(kb + kWideKT, STAGE ^ 1, pid);
       pnext = page_of(kb + 2 * kWideKT);
     }
+    auto next_v = [&]() {
+      if (F8 && more) {
+        commit(STAGE ^ 1, 0);
+        issue(kb + kWideKT, STAGE ^ 1, pid, 1);
+      }
+    };
     if (MASKED && kb > wave_max_lim) {
-      if (F8 && jb + 1 < nblk) commit(STAGE ^ 1);
+      next_v();
+      if (F8 && more) commit(STAGE ^ 1, 1);
       return;
     }
 
@@ -1070,6 +1078,7 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
     });
     static_for<2>([&](auto hh) {
       constexpr int h = decltype(hh)::value;
+      if (h == 1) next_v();
       if (h == 1 && !half1) return;
       float x[2][8], p[2][8];
 #pragma unroll
@@ -1144,11 +1153,16 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       }
     });
     // the other stage was last read in block jb - 1, before this block's barrier
-    if (F8 && jb + 1 < nblk) commit(STAGE ^ 1);
+    if (F8 && more) commit(STAGE ^ 1, 1);
   };
   if (nblk > 0) {
-    issue(kv_lo, 0, page_of(kv_lo));
-    if (F8) commit(0);
+    const int pid0 = page_of(kv_lo);
+    issue(kv_lo, 0, pid0);
+    if (F8) {
+      commit(0, 0);
+      issue(kv_lo, 0, pid0, 1);
+      commit(0, 1);
+    }
     pnext = page_of(kv_lo + kWideKT);
   }
   using I0 = std::integral_constant<int, 0>;
@@ -1177,10 +1191,15 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   // barrier is needed.  (The e4m3 variant keeps the
   // direct stores: the staging code makes its register allocation spill.)
   unsigned char* ost = ((nblk & 1) ? lds1 : lds0) + wave * (NW == 4 ? 8192 : 4096);
+  // the lane index, read again from the hardware counter: nothing derived
+  // from it then has to stay in a register across the block loops (the e4m3
+  // variant would otherwise spill two of them)
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int er = elane & 15, eqd = elane >> 4;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const float l = xlane_sum(l_run[c]);
-    const int pos = pos0[c] + r;
+    const int pos = pos0[c] + er;
     const bool valid = pos < it.nrows;
     const bool direct = !valid || a.row_pbase[it.row0 + pos] < 0;
     if (!F8 && __all(direct)) {
@@ -1190,22 +1209,22 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
       for (int dt = 0; dt < 8; ++dt) {
         // d = 16 dt + 4 qd .. +3: 16-byte chunk 2 dt + qd / 2, half qd % 2
         const f32x4 v = o[c][dt] * inv;
-        *reinterpret_cast<u32x2*>(tb + r * 256 + 16 * ((2 * dt + (qd >> 1)) ^ r) + 8 * (qd & 1)) =
+        *reinterpret_cast<u32x2*>(tb + er * 256 + 16 * ((2 * dt + (eqd >> 1)) ^ er) + 8 * (eqd & 1)) =
             u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
-      if (valid && qd == 0 && a.lse)
+      if (valid && eqd == 0 && a.lse)
         a.lse[(int64_t)(it.row0 + pos) * a.H + head] = l > 0.f ? (m_run[c] + log2f(l)) * kLn2 : -INFINITY;
-      const int j = lane & 15;
+      const int j = elane & 15;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int t = 4 * k + (lane >> 4);
+        const int t = 4 * k + (elane >> 4);
         const u32x4 x = *reinterpret_cast<const u32x4*>(tb + t * 256 + 16 * (j ^ t));
         if (pos0[c] + t < it.nrows)
           __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) +
                                                                   ((int64_t)(it.row0 + pos0[c] + t) * a.H + head) * D + 8 * j));
       }
     } else if (valid) {
-      write_column_dmajor(a, it.row0 + pos, head, it.slot, qd, o[c], m_run[c], l, omul);
+      write_column_dmajor(a, it.row0 + pos, head, it.slot, eqd, o[c], m_run[c], l, omul);
     }
   }
 }

@@ -47,13 +47,15 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // Share of the resident decode wave groups that the decode lists take when
 // prefills run beside them: the decode's time alone over the sum of both
 // parts' times alone, estimated from the KV bytes the decodes read (at the
-// decode kernel's rate, about 6 TB/s) and the prefills' attention FLOPs (at
-// the prefill kernel's rate: about 0.9 PFLOP/s on bf16 MFMA, far less in
-// fp32), kept within [0.25, 0.75].  On MI355X the decode keeps HBM near its
+// decode kernel's rate, about 6 TB/s) and the attention FLOPs of the side
+// stream (the prefills', and a shared-prefix pass's: every row against the
+// prefix; at the prefill kernel's rate: about 0.9 PFLOP/s on bf16 MFMA, far
+// less in fp32), kept within [0.25, 0.75].  On MI355X the decode keeps HBM near its
 // rate with about 70 % of the groups, while the prefill waits for free CUs
 // when the decode holds them all: on a mixed step of 192 decodes and four
 // 512-token chunks the step takes 1.29 ms at 70-75 % against 1.41 ms at 100 %.
-double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t* seq_lens, int64_t dec_tokens) {
+double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t* seq_lens, int64_t dec_tokens,
+                    int32_t T) {
   constexpr double kDecodeBytesPerSec = 6.0e12;
   const double pre_flops_per_sec = p.dtype == PA_BF16 ? 0.9e15 : 0.1e15;
   const double elem = p.kv_dtype == PA_KV_FP8_E4M3 ? 1.0 : (p.dtype == PA_BF16 ? 2.0 : 4.0);
@@ -63,6 +65,14 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
     if (qb <= 1) continue;
     const double L = seq_lens[b];
     pairs += p.causal ? qb * (L - qb) + 0.5 * qb * (qb + 1.0) : qb * L;
+  }
+  // the shared-prefix pass runs on the same side stream: every row against
+  // the P prefix keys (prefill rows then see only their keys past P)
+  const double P = p.common_prefix_len;
+  if (P > 0) {
+    for (int b = 0; b < B; ++b)
+      if (qsl[b + 1] - qsl[b] > 1) pairs -= (double)(qsl[b + 1] - qsl[b]) * P;
+    pairs += (double)T * P;
   }
   const double t_dec = (double)dec_tokens * 2.0 * p.num_kv_heads * p.head_size * elem / kDecodeBytesPerSec;
   const double t_pre = 4.0 * p.head_size * p.num_heads * pairs / pre_flops_per_sec;
@@ -270,7 +280,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     const int prefix_cus = hp.prefix_beside ? n_pc * (int)ceil_div(hp.T, QB) * Hkv * hp.ps.head_groups : 0;
     const int dec_cus = std::max(num_cus - prefix_cus, 1);
     int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * dec_cus * dec_nw / dec_units);
-    if (np > 0) lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens)));
+    if (np > 0)
+      lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens, hp.T)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
     // A list is closed with up to 31 keys of room unused (cuts inside a
     // sequence fall on multiples of 32), so each holds 32 keys more than the
