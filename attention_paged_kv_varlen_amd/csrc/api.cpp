@@ -22,10 +22,9 @@ struct pa_plan {
   pa::DeviceSchedule ds{};
   size_t ws_bytes = 0;
   // side stream and fork/join events, created with the plan when it holds both
-  // decode work and prefill work, or a shared-prefix pass that runs beside the
-  // decode on CUs of its own, so that the MFMA-bound launches overlap the
-  // HBM-bound decode (otherwise a shared-prefix pass runs before the decode on
-  // the caller's stream)
+  // decode work and prefill work, so that the MFMA-bound launches overlap the
+  // HBM-bound decode (a shared-prefix pass with decodes alone runs in the
+  // decode's own launch, or before it)
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   // Held by a forward from its event record on the caller's stream to the
@@ -250,7 +249,7 @@ pa_status pa_plan_create(const pa_params* params, const int32_t* query_start_loc
     plan->dev_seq_lens = reinterpret_cast<const int32_t*>(base + sec[7].off);
     plan->dev_bt = hp.block_table.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + sec[8].off);
     plan->dev_check = reinterpret_cast<int32_t*>(base + sec[9].off);
-    if (!hp.decode_items.empty() && (!hp.prefill_items.empty() || hp.prefix_beside)) {
+    if (!hp.decode_items.empty() && !hp.prefill_items.empty()) {
       e = hipStreamCreateWithFlags(&plan->aux, hipStreamNonBlocking);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_fork, hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&plan->ev_join, hipEventDisableTiming);

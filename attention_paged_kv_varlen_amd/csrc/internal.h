@@ -167,8 +167,9 @@ struct HostPlan {
   pa_plan_info info{};
   PrefillShape ps{};
   int num_partials = 0;
-  // the shared-prefix pass runs beside the decode on CUs of its own (8-wave
-  // prefix workgroups, decode lists sized for the other CUs)
+  // the shared-prefix pass runs beside the decode on CUs of its own, in the
+  // decode's launch (8-wave prefix workgroups, decode lists sized for the
+  // other CUs)
   bool prefix_beside = false;
 };
 

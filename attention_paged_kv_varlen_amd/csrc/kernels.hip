@@ -411,7 +411,7 @@ __device__ __forceinline__ typename Ops<T, VE>::VRaw widen_v(const RawVOf<KV, VE
 // and the V scale multiplies the output.
 // ---------------------------------------------------------------------------
 template <typename T, typename KV, int D, bool DB, bool NT>
-__global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
+__device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
   constexpr bool F8 = std::is_same<KV, uint8_t>::value;
   static_assert(!F8 || std::is_same<T, uint16_t>::value, "e4m3 pools take bf16 queries");
   constexpr int VE = D / 16;
@@ -428,11 +428,10 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
   // one list, so the Hkv slices of a page row (one contiguous 2 KB row at
   // Hkv = 8, d = 128) are read by one CU at about the same time; the list's
   // items run one after the other
-  const int nw = (int)(blockDim.x >> 6);
   const int nhg = a.Hkv * a.head_groups;
   const int wgs_per_list = nhg / nw;
-  const int list = (int)(blockIdx.x / (unsigned)wgs_per_list);
-  const int hgi = (int)(blockIdx.x % (unsigned)wgs_per_list) * nw + wave;
+  const int list = (int)((unsigned)wg / (unsigned)wgs_per_list);
+  const int hgi = (int)((unsigned)wg % (unsigned)wgs_per_list) * nw + wave;
   const int kvh = hgi / a.head_groups;
   const int hgrp = hgi % a.head_groups;
   const float sl2 = F8 ? a.scale_log2 * kv_scale_of(a.k_scale, a.n_scales, kvh) : a.scale_log2;
@@ -574,6 +573,11 @@ __global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
     l_run += __shfl_xor(l_run, 32);
     if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run, omul);
   }
+}
+
+template <typename T, typename KV, int D, bool DB, bool NT>
+__global__ void __launch_bounds__(512) decode_kernel(KArgs a) {
+  decode_body<T, KV, D, DB, NT>(a, (int)blockIdx.x, (int)(blockDim.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -851,7 +855,7 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
 // LDS is unchanged.  The K scale joins the softmax scale, the V scale
 // multiplies the output.
 template <bool F8, int NW>
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+__device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char* lds0, unsigned char* lds1) {
   using KV = std::conditional_t<F8, uint8_t, uint16_t>;
   static_assert(NW == 4 || (NW == 8 && !F8), "4 waves, or 8 waves over a bf16 pool");
   constexpr int RPW = kWideKT / NW;  // block rows each wave loads: one 16-key tile
@@ -859,10 +863,9 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   using O = Ops<uint16_t, VE>;
   using Frag = O::Frag;
 
-  // one array per stage, so that the compiler can tell the blocks being
-  // filled by direct-to-LDS loads apart from the block being read
-  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * kWideBlk];  // K | V of even blocks
-  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * kWideBlk];  // K | V of odd blocks
+  // lds0 / lds1: K | V of even / odd blocks (kWideBlk each), one array per
+  // stage so that the compiler can tell the blocks being filled by
+  // direct-to-LDS loads apart from the block being read
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -870,8 +873,8 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   // within an item the KV head is the fastest-varying workgroup index, then
   // the head group (see launch_prefill)
   const int nhg = a.Hkv * a.head_groups;
-  const int hgi = (int)(blockIdx.x % (unsigned)nhg);
-  const WorkItem it = a.items[blockIdx.x / (unsigned)nhg];
+  const int hgi = (int)((unsigned)wg % (unsigned)nhg);
+  const WorkItem it = a.items[(unsigned)wg / (unsigned)nhg];
   const int kvh = hgi % a.Hkv;
   const int hgrp = hgi / a.Hkv;
   const int r = lane & 15, qd = lane >> 4;
@@ -1229,6 +1232,29 @@ __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
+template <bool F8, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_wide_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * kWideBlk];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * kWideBlk];
+  wide_body<F8, NW>(a, (int)blockIdx.x, lds0, lds1);
+}
+
+// The shared-prefix pass beside the decode, in one launch: workgroups
+// [0, n_pre) run prefix units (8-wave wide prefill, one unit each), the rest
+// run decode lists (8 waves: one list, all KV heads).  Each workgroup fills a
+// CU's registers, and the plan sizes both parts to fit the chip together, so
+// they run side by side; unlike two launches on two streams, nothing waits on
+// an event between them and the merge.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefix_decode_kernel(KArgs pre, KArgs dec, int n_pre) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * kWideBlk];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * kWideBlk];
+  if ((int)blockIdx.x < n_pre)
+    wide_body<false, 8>(pre, (int)blockIdx.x, lds0, lds1);
+  else
+    decode_body<uint16_t, uint16_t, 128, true, false>(dec, (int)blockIdx.x - n_pre, 8);
+}
+
 // ---------------------------------------------------------------------------
 // Merge of several partial records per row by their LSE.
 // ---------------------------------------------------------------------------
@@ -1539,77 +1565,89 @@ int forward_impl(const LaunchGeom& g, const DeviceSchedule& s, const Tensors& t,
   a.n_scales = t.n_scales;
   char name[48];
   int err = 0;
-
-  // cascade prefix pass (all rows against the shared prefix) and prefills
-  // first, on the side stream when there is one (plans with decodes and
-  // prefills: the MFMA-bound workgroups are then resident before the
-  // decode's fill the machine; otherwise one after the other on the caller's
-  // stream), decodes on the caller's stream, then the LSE merge of rows with
-  // several parts
+  // launch arguments of the prefill-type passes and of the decode
+  auto prefill_args = [&](const WorkItem* items, int n) {
+    KArgs p = a;
+    p.items = items;
+    p.n_items = n;
+    p.head_groups = g.ps.head_groups;
+    p.heads_per_grp = g.ps.heads_per_wg;
+    p.tiles_per_head = g.ps.tiles_per_head;
+    p.tiles_per_wg = g.ps.tiles;
+    return p;
+  };
+  KArgs d = a;
+  d.items = s.decode;
+  d.n_items = s.n_decode;
+  d.head_groups = (g.g + 15) / 16;
+  d.heads_per_grp = 16;
+  d.tiles_per_head = 1;
+  d.lists = s.decode_lists;
+  const int dec_nhg = g.Hkv * d.head_groups;
+  const int dec_nw = decode_waves_per_wg(dec_nhg);
+  const int64_t dec_wgs = (int64_t)s.n_decode_lists * (dec_nhg / dec_nw);
   void* stream = st.main;
-  const bool fork = st.aux && s.n_decode > 0 && (s.n_prefill > 0 || s.n_prefix > 0);
-  void* mstream = fork ? st.aux : stream;
-  if (fork) {
-    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_fork), static_cast<hipStream_t>(stream));
-    if (e == hipSuccess)
-      e = hipStreamWaitEvent(static_cast<hipStream_t>(st.aux), static_cast<hipEvent_t>(st.ev_fork), 0);
-    if (e != hipSuccess) return (int)e;
-  }
-  if (s.n_prefix > 0) {
-    KArgs p = a;
-    p.items = s.prefix;
-    p.n_items = s.n_prefix;
-    p.head_groups = g.ps.head_groups;
-    p.heads_per_grp = g.ps.heads_per_wg;
-    p.tiles_per_head = g.ps.tiles_per_head;
-    p.tiles_per_wg = g.ps.tiles;
-    snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
-    err = launch_prefill<T, KV, D>(name, s.n_prefix, mstream, p);
-    if (err) return err;
-  }
-  if (s.n_prefill > 0) {
-    KArgs p = a;
-    p.items = s.prefill;
-    p.n_items = s.n_prefill;
-    p.head_groups = g.ps.head_groups;
-    p.heads_per_grp = g.ps.heads_per_wg;
-    p.tiles_per_head = g.ps.tiles_per_head;
-    p.tiles_per_wg = g.ps.tiles;
-    snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
-    err = launch_prefill<T, KV, D>(name, s.n_prefill, mstream, p);
-    if (err) return err;
-  }
-  if (s.n_decode > 0) {
-    KArgs d = a;
-    d.items = s.decode;
-    d.n_items = s.n_decode;
-    d.head_groups = (g.g + 15) / 16;
-    d.heads_per_grp = 16;
-    d.tiles_per_head = 1;
-    snprintf(name, sizeof(name), "decode_%s_d%d", tag, D);
-    const int nhg = g.Hkv * d.head_groups;
-    const int nw = decode_waves_per_wg(nhg);
-    d.lists = s.decode_lists;
-    const int64_t nwg = (int64_t)s.n_decode_lists * (nhg / nw);
-    if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-    // two steps in flight (bf16 queries); non-temporal K/V loads unless
-    // MFMA work (prefills, the shared-prefix pass) runs beside the decode
-    const dim3 dg((unsigned)nwg), db(64 * nw);
-    const bool beside = s.n_prefill > 0 || s.prefix_beside;
-    if constexpr (sizeof(T) == 2) {
-      err = beside ? launch(name, decode_kernel<T, KV, D, true, false>, dg, db, stream, d)
-                   : launch(name, decode_kernel<T, KV, D, true, true>, dg, db, stream, d);
+
+  if (s.prefix_beside) {
+    // the shared-prefix pass and the decode side by side in one launch (the
+    // planner sets prefix_beside only for this kernel's shapes)
+    if constexpr (std::is_same<T, uint16_t>::value && std::is_same<KV, uint16_t>::value && D == 128) {
+      const int64_t n_pre = (int64_t)s.n_prefix * g.Hkv * g.ps.head_groups;
+      if (dec_nw != 8 || g.ps.tiles != 16 || n_pre + dec_wgs > INT32_MAX)
+        return (int)hipErrorInvalidConfiguration;
+      snprintf(name, sizeof(name), "prefix_decode_%s_d%d", tag, D);
+      err = launch(name, prefix_decode_kernel, dim3((unsigned)(n_pre + dec_wgs)), dim3(512), stream,
+                   prefill_args(s.prefix, s.n_prefix), d, (int)n_pre);
     } else {
-      err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, false, false>, dg, db, stream, d)
-                            : launch(name, decode_kernel<T, KV, D, false, true>, dg, db, stream, d);
+      err = (int)hipErrorInvalidConfiguration;
     }
     if (err) return err;
-  }
-  if (fork) {
-    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_join), static_cast<hipStream_t>(st.aux));
-    if (e == hipSuccess)
-      e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(st.ev_join), 0);
-    if (e != hipSuccess) return (int)e;
+  } else {
+    // cascade prefix pass (all rows against the shared prefix) and prefills
+    // first, on the side stream when there is one (plans with decodes and
+    // prefills: the MFMA-bound workgroups are then resident before the
+    // decode's fill the machine; otherwise one after the other on the
+    // caller's stream), decodes on the caller's stream, then the LSE merge of
+    // rows with several parts
+    const bool fork = st.aux && s.n_decode > 0 && (s.n_prefill > 0 || s.n_prefix > 0);
+    void* mstream = fork ? st.aux : stream;
+    if (fork) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_fork), static_cast<hipStream_t>(stream));
+      if (e == hipSuccess)
+        e = hipStreamWaitEvent(static_cast<hipStream_t>(st.aux), static_cast<hipEvent_t>(st.ev_fork), 0);
+      if (e != hipSuccess) return (int)e;
+    }
+    if (s.n_prefix > 0) {
+      snprintf(name, sizeof(name), "prefix_%s_d%d", tag, D);
+      err = launch_prefill<T, KV, D>(name, s.n_prefix, mstream, prefill_args(s.prefix, s.n_prefix));
+      if (err) return err;
+    }
+    if (s.n_prefill > 0) {
+      snprintf(name, sizeof(name), "prefill_%s_d%d", tag, D);
+      err = launch_prefill<T, KV, D>(name, s.n_prefill, mstream, prefill_args(s.prefill, s.n_prefill));
+      if (err) return err;
+    }
+    if (s.n_decode > 0) {
+      snprintf(name, sizeof(name), "decode_%s_d%d", tag, D);
+      if (dec_wgs > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+      // two steps in flight (bf16 queries); non-temporal K/V loads unless
+      // prefills run beside the decode
+      const dim3 dg((unsigned)dec_wgs), db(64 * dec_nw);
+      if constexpr (sizeof(T) == 2) {
+        err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, true, false>, dg, db, stream, d)
+                              : launch(name, decode_kernel<T, KV, D, true, true>, dg, db, stream, d);
+      } else {
+        err = s.n_prefill > 0 ? launch(name, decode_kernel<T, KV, D, false, false>, dg, db, stream, d)
+                              : launch(name, decode_kernel<T, KV, D, false, true>, dg, db, stream, d);
+      }
+      if (err) return err;
+    }
+    if (fork) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(st.ev_join), static_cast<hipStream_t>(st.aux));
+      if (e == hipSuccess)
+        e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(st.ev_join), 0);
+      if (e != hipSuccess) return (int)e;
+    }
   }
   if (s.n_merge > 0) {
     snprintf(name, sizeof(name), "merge_%s_d%d", tag, D);

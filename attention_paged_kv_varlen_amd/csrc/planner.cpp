@@ -229,13 +229,14 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   int n_pc = P > 0 ? (int)ceil_div(P, kPrefixChunk) : 0;
 
   // Shared prefix beside the decode.  With decodes only (bf16 pool, head size
-  // 128, automatic split) the prefix pass runs at the same time as the decode,
-  // on CUs of its own: one 8-wave workgroup per prefix unit (chunk, column
-  // group, KV head), each filling a CU's registers, while the decode lists are
-  // sized for the remaining CUs.  The chunk count sets how many CUs the prefix
+  // 128, automatic split, 8-wave decode workgroups) the prefix pass runs at
+  // the same time as the decode, in the same launch, on CUs of its own: one
+  // 8-wave workgroup per prefix unit (chunk, column group, KV head), each
+  // filling a CU's registers, while the decode lists are sized for the
+  // remaining CUs.  The chunk count sets how many CUs the prefix
   // takes; it is chosen so that the two finish together (the rates above).
   if (P > 0 && np == 0 && balanced && use_wide_prefill(p.dtype, p.head_size, p.kv_dtype) &&
-      p.kv_dtype == PA_KV_SAME) {
+      p.kv_dtype == PA_KV_SAME && dec_nw == 8) {
     const PrefillShape s16 = prefill_shape(g, 16, 8);
     const int per_chunk = (int)ceil_div(hp.T, s16.rows_per_item) * Hkv * s16.head_groups;
     const double dec_bytes = (double)dec_tokens * 2.0 * Hkv * p.head_size * 2.0;

@@ -615,10 +615,16 @@ def main(argv=None) -> int:
         value = counts["decode_bytes"] / (ms * 1e-3) / 1e9
         line.update(value=round(value, 2), unit="GB/s")
         kname, k = _kernel(t, "decode_")
-        ach = counts["decode_bytes"] / (k["avg_us"] * 1e-6) / 1e9
-        if cfg == 5:  # cascade: the decode kernel reads only the suffixes
-            suffix = counts["decode_bytes"] - batch.common_prefix_len * 2 * batch.num_kv_heads * batch.head_size * 2
-            ach = suffix / (k["avg_us"] * 1e-6) / 1e9
+        ach = counts["decode_bytes"] / (k["avg_us"] * 1e-6) / 1e9 if k else 0.0
+        if cfg == 5:
+            fused, kf = _kernel(t, "prefix_decode_")
+            if kf:  # the prefix pass and the decode in one launch: all the cascade's bytes
+                kname, k = fused, kf
+                ach = counts["decode_bytes"] / (k["avg_us"] * 1e-6) / 1e9
+            else:  # the decode kernel reads only the suffixes
+                elem = 1 if kv_dtype == "fp8_e4m3" else (2 if dtype == "bf16" else 4)
+                suffix = counts["decode_bytes"] - batch.common_prefix_len * 2 * batch.num_kv_heads * batch.head_size * elem
+                ach = suffix / (k["avg_us"] * 1e-6) / 1e9
             line["cascade"] = {"effective_GBps_vs_naive_bytes": round(counts["decode_bytes_naive"] / (ms * 1e-3) / 1e9, 1),
                                "naive_bytes": counts["decode_bytes_naive"], "cascade_bytes": counts["decode_bytes"]}
         roof = {"bound": bound, "kernel": kname, "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

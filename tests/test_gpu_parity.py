@@ -116,6 +116,11 @@ CASCADE_DECODES = {
     "bf16_hnd_bs128_P256": dict(P=256, block_size=128, kv_layout="HND"),
     "e4m3_bs16_P144": dict(P=144, block_size=16, kv_dtype="fp8_e4m3"),
     "bf16_g8_bs64_P192": dict(P=192, block_size=64, num_heads=16),
+    # 8 KV heads: 8-wave decode workgroups, so the prefix pass runs in the
+    # decode's own launch (prefix_decode_kernel), on CUs of its own
+    "fused_hkv8_bs16_P16x37": dict(P=16 * 37, block_size=16, num_heads=32, num_kv_heads=8),
+    "fused_hkv8_hnd_bs128_P1024": dict(P=1024, block_size=128, num_heads=32, num_kv_heads=8, kv_layout="HND"),
+    "fused_hkv8_g8_bs64_P2048": dict(P=2048, block_size=64, num_heads=64, num_kv_heads=8),
 }
 
 
@@ -124,15 +129,18 @@ def test_cascade_decodes_only_match_oracle(name):
     kw = dict(CASCADE_DECODES[name])
     P = kw.pop("P")
     kw.setdefault("num_heads", 8)
+    kw.setdefault("num_kv_heads", 2)
     rng = np.random.default_rng(23)
     extra = rng.integers(1, 900, size=14).tolist() + [1, 31, 33, 1000]
     lens = [P + e for e in extra]
-    batch = make_batch([1] * len(lens), lens, num_kv_heads=2, head_size=128, seed=24,
-                       shared_prefix_blocks=P // kw["block_size"], **kw)
+    batch = make_batch([1] * len(lens), lens, head_size=128, seed=24, shared_prefix_blocks=P // kw["block_size"],
+                       **kw)
     announce(f"cascade decodes only {name} B={batch.num_seqs} P={P}")
     co, cl, db = run_gpu(batch)
     info = pa.pa_plan_get_info(db.plan)
     assert info["num_prefill_items"] == 0 and info["num_prefix_items"] > 0
+    fused = name.startswith("fused")
+    assert info["prefix_beside_decode"] == (1 if fused else 0)
     assert 0 < info["num_decode_lists"] < info["num_decode_items"] and info["decode_list_tokens"] > 0
     ref_o, ref_l = oracle_full(batch)
     assert_close(co, cl, ref_o, ref_l, f"{name} cascade vs oracle")

@@ -85,10 +85,13 @@ def test_wide_prefill_takes_eight_waves_beside_decodes():
     bt = np.zeros((2, 20), dtype=np.int32)
     bt[1, 1:] = np.arange(1, 20)
     # a shared prefix with decodes alone runs beside the decode in 8-wave
-    # workgroups; with a prefill as well, before it in 4-wave workgroups
-    _, casc = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
+    # workgroups when the decode's workgroups have 8 waves (8 KV heads); with 2
+    # KV heads, or with a prefill as well, before it in 4-wave workgroups
+    _, casc = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40, H=32, Hkv=8)
     assert casc["prefill_rows_per_item"] == 64 and casc["prefix_beside_decode"] == 1
-    _, cpre = host_plan([1, 20], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
+    _, c2 = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
+    assert c2["prefill_rows_per_item"] == 32 and c2["prefix_beside_decode"] == 0
+    _, cpre = host_plan([1, 20], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40, H=32, Hkv=8)
     assert cpre["prefill_rows_per_item"] == 32 and cpre["prefix_beside_decode"] == 0
     _, f32 = host_plan([1, 100], [300, 100], dtype="fp32")
     assert f32["prefill_rows_per_item"] == 32
