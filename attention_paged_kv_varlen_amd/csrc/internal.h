@@ -54,14 +54,14 @@ PrefillShape prefill_shape(int group, int tiles, int max_heads);
 inline bool use_wide_prefill(int dtype, int head_size, int kv_dtype) {
   return dtype == PA_BF16 && head_size == 128 && (kv_dtype == PA_KV_SAME || kv_dtype == PA_KV_FP8_E4M3);
 }
-// Column tiles per wide-prefill workgroup.  Beside decodes (and without a
-// shared prefix) a bf16 pool's prefill runs 8-wave workgroups, each filling
-// the register file of its CU: a 4-wave prefill workgroup leaves a CU half
-// empty yet too full for an 8-wave decode workgroup, so the decode would get
-// fewer CUs.  Otherwise 4-wave workgroups, two per CU, whose independent
-// barriers let one's softmax overlap the other's MFMAs.
-inline int wide_prefill_tiles(bool beside_decodes, int common_prefix_len, int kv_dtype) {
-  return beside_decodes && common_prefix_len == 0 && kv_dtype == PA_KV_SAME ? 16 : 8;
+// Column tiles per wide-prefill workgroup.  Beside decodes a bf16 pool's
+// prefill runs 8-wave workgroups, each filling the register file of its CU: a
+// 4-wave prefill workgroup leaves a CU half empty yet too full for an 8-wave
+// decode workgroup, so the decode would get fewer CUs.  Otherwise 4-wave
+// workgroups, two per CU, whose independent barriers let one's softmax
+// overlap the other's MFMAs.
+inline int wide_prefill_tiles(bool beside_decodes, int kv_dtype) {
+  return beside_decodes && kv_dtype == PA_KV_SAME ? 16 : 8;
 }
 
 // Everything the kernels need besides the caller's tensors.

@@ -48,14 +48,14 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // prefills run beside them: the decode's time alone over the sum of both
 // parts' times alone, estimated from the KV bytes the decodes read (at the
 // decode kernel's rate, about 6 TB/s) and the attention FLOPs of the side
-// stream (the prefills', and a shared-prefix pass's: every row against the
-// prefix; at the prefill kernel's rate: about 0.9 PFLOP/s on bf16 MFMA, far
-// less in fp32), kept within [0.25, 0.75].  On MI355X the decode keeps HBM near its
+// stream (the prefills', and a shared-prefix pass's: every decode row against
+// the prefix; at the prefill kernel's rate: about 0.9 PFLOP/s on bf16 MFMA,
+// far less in fp32), kept within [0.25, 0.75].  On MI355X the decode keeps HBM near its
 // rate with about 70 % of the groups, while the prefill waits for free CUs
 // when the decode holds them all: on a mixed step of 192 decodes and four
 // 512-token chunks the step takes 1.29 ms at 70-75 % against 1.41 ms at 100 %.
 double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t* seq_lens, int64_t dec_tokens,
-                    int32_t T) {
+                    int32_t n_decode_rows) {
   constexpr double kDecodeBytesPerSec = 6.0e12;
   const double pre_flops_per_sec = p.dtype == PA_BF16 ? 0.9e15 : 0.1e15;
   const double elem = p.kv_dtype == PA_KV_FP8_E4M3 ? 1.0 : (p.dtype == PA_BF16 ? 2.0 : 4.0);
@@ -66,14 +66,9 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
     const double L = seq_lens[b];
     pairs += p.causal ? qb * (L - qb) + 0.5 * qb * (qb + 1.0) : qb * L;
   }
-  // the shared-prefix pass runs on the same side stream: every row against
-  // the P prefix keys (prefill rows then see only their keys past P)
-  const double P = p.common_prefix_len;
-  if (P > 0) {
-    for (int b = 0; b < B; ++b)
-      if (qsl[b + 1] - qsl[b] > 1) pairs -= (double)(qsl[b + 1] - qsl[b]) * P;
-    pairs += (double)T * P;
-  }
+  // the shared-prefix pass runs on the same side stream: every decode row
+  // against the P prefix keys
+  pairs += (double)n_decode_rows * p.common_prefix_len;
   const double t_dec = (double)dec_tokens * 2.0 * p.num_kv_heads * p.head_size * elem / kDecodeBytesPerSec;
   const double t_pre = 4.0 * p.head_size * p.num_heads * pairs / pre_flops_per_sec;
   if (t_dec + t_pre <= 0.0) return 0.75;
@@ -221,7 +216,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   const bool balanced = p.kv_split_tokens == 0 && nd > 0 && decode_wgs_per_cu > 0;
   // the wide kernel needs both tiles of a wave on one head (at most tiles / 2 heads)
   if (use_wide_prefill(p.dtype, p.head_size, p.kv_dtype)) {
-    const int tiles = wide_prefill_tiles(nd > 0, P, p.kv_dtype);
+    const int tiles = wide_prefill_tiles(nd > 0 && np > 0, p.kv_dtype);
     hp.ps = prefill_shape(g, tiles, tiles / 2);
   } else {
     hp.ps = prefill_shape(g, 8, 8);
@@ -282,7 +277,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     const int dec_cus = std::max(num_cus - prefix_cus, 1);
     int64_t lanes = std::max<int64_t>(1, (int64_t)decode_wgs_per_cu * dec_cus * dec_nw / dec_units);
     if (np > 0)
-      lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens, hp.T)));
+      lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens, nd)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
     // A list is closed with up to 31 keys of room unused (cuts inside a
     // sequence fall on multiples of 32), so each holds 32 keys more than the
@@ -366,33 +361,48 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
         it.row0 = qsl[b] + i0;
         it.nrows = std::min(QB, qb - i0);
         it.lim0 = ctx + i0;
-        it.kv_begin = P;
+        // prefill rows attend to their whole context in their own items, the
+        // shared prefix included: many queries per key, so sharing the
+        // prefix's reads would save little and cost partial records
+        it.kv_begin = 0;
         it.kv_end = p.causal ? std::min(L, ctx + i0 + it.nrows) : L;
-        it.slot = n_pc;
+        it.slot = 0;
         it.causal = p.causal;
         hp.prefill_items.push_back(it);
         pre_read += (int64_t)(it.kv_end - it.kv_begin) * hp.ps.head_groups;
       }
-      for (int r = qsl[b]; r < qsl[b + 1]; ++r) contrib[r] = n_pc + 1;
+      for (int r = qsl[b]; r < qsl[b + 1]; ++r) contrib[r] = 1;
     }
   }
   if (P > 0) {
-    // chunk-major: the row groups that read one prefix chunk are dispatched
-    // back to back (on the same XCD), so the chunk is fetched once into L2
+    // The prefix pass covers the decode rows, run by run of consecutive rows
+    // (one run in a decode-first batch).  Chunk-major: the row groups that
+    // read one prefix chunk are dispatched back to back (on the same XCD), so
+    // the chunk is fetched once into L2.
+    std::vector<std::pair<int, int>> runs;  // decode rows [first, end)
+    for (int b = 0; b < B; ++b) {
+      if (qsl[b + 1] - qsl[b] != 1) continue;
+      if (!runs.empty() && runs.back().second == qsl[b])
+        runs.back().second += 1;
+      else
+        runs.push_back({qsl[b], qsl[b] + 1});
+    }
     for (int j = 0; j < n_pc; ++j) {
-      for (int r0 = 0; r0 < hp.T; r0 += QB) {
-        WorkItem it{};
-        it.seq = 0;
-        it.row0 = r0;
-        it.nrows = std::min(QB, hp.T - r0);
-        it.lim0 = 0;
-        it.kv_begin = j * pc_len;
-        it.kv_end = std::min(P, (j + 1) * pc_len);
-        it.slot = j;
-        it.causal = 0;
-        if (it.kv_begin >= it.kv_end) continue;
-        hp.prefix_items.push_back(it);
-        pfx_read += (int64_t)(it.kv_end - it.kv_begin) * hp.ps.head_groups;
+      for (const auto& run : runs) {
+        for (int r0 = run.first; r0 < run.second; r0 += QB) {
+          WorkItem it{};
+          it.seq = 0;
+          it.row0 = r0;
+          it.nrows = std::min(QB, run.second - r0);
+          it.lim0 = 0;
+          it.kv_begin = j * pc_len;
+          it.kv_end = std::min(P, (j + 1) * pc_len);
+          it.slot = j;
+          it.causal = 0;
+          if (it.kv_begin >= it.kv_end) continue;
+          hp.prefix_items.push_back(it);
+          pfx_read += (int64_t)(it.kv_end - it.kv_begin) * hp.ps.head_groups;
+        }
       }
     }
   }

@@ -47,6 +47,7 @@ WORKLOADS = {
     "cascade": 5,
     "tiny": 1,
     "decode_e4m3": 2,
+    "cascade_chunks": 6,
 }
 KV_DTYPES = {"decode_e4m3": "fp8_e4m3"}
 DESCRIPTIONS = {
@@ -57,6 +58,8 @@ DESCRIPTIONS = {
        "64 q / 8 kv heads, d=128, bs=64, bf16, decode-first",
     5: "cascade: 128 decodes sharing a 16384-token prefix + suffixes U[256,2048]; 32 q / 8 kv heads, d=128, "
        "bs=16, bf16",
+    6: "cascade with chunks: the cascade batch plus 4 chunks of 512 sharing its prefix (own context "
+       "U[256,2048]); 32 q / 8 kv heads, d=128, bs=16, bf16",
 }
 
 
@@ -205,14 +208,22 @@ def _traffic(kernel_name: str, workload: str):
 # ---------------------------------------------------------------------------
 
 def _cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, family, model,
+    stepping, and the logical CPUs the file lists."""
+    fields, n = {}, 0
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                key = line.split(":", 1)[0].strip()
+                if key == "processor":
+                    n += 1
+                if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                    fields[key] = line.split(":", 1)[1].strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    return (f"{name} (family {fields.get('cpu family', '?')}, model {fields.get('model', '?')}, "
+            f"stepping {fields.get('stepping', '?')}; {n} logical CPUs listed)")
 
 
 def _blas_name() -> str:

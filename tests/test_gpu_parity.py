@@ -333,8 +333,8 @@ def test_profile_records_kernel_times():
 
 def full_config_rows(batch, cfg):
     """Rows of a full-size workload compared with the oracle: every row of the
-    decode-only, chunked-prefill mixed and cascade workloads (the oracle takes
-    seconds for them), and for the causal varlen prefill (1.7 TFLOP of dense
+    decode-only, chunked-prefill mixed and cascade workloads and of the cascade
+    with chunks (the oracle takes seconds for them), and for the causal varlen prefill (1.7 TFLOP of dense
     float64 work in all) the first and last 8 rows of every prompt plus 48
     spread between them (so every prompt's first, middle and last tiles and
     its ragged tail are covered)."""
@@ -357,7 +357,7 @@ def _row_kinds(batch, rows):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 6])
 def test_full_config_against_oracle(cfg):
     announce(f"full config {cfg}: generating")
     batch = config_batch(cfg)
@@ -368,7 +368,7 @@ def test_full_config_against_oracle(cfg):
     n_dec, n_pre, n_pre_seqs = _row_kinds(batch, rows)
     announce(f"full config {cfg}: comparing {len(rows)} of {batch.num_tokens} rows with the oracle "
              f"({n_dec} decode rows, {n_pre} prefill rows of {n_pre_seqs} sequences)")
-    if cfg == 4:  # all four chunks, every row
+    if cfg in (4, 6):  # all four chunks, every row
         assert n_pre == 4 * 512 and n_pre_seqs == 4
     ref_o, ref_l = oracle.attention_rows(batch.q, batch.kv_cache, batch.block_table, batch.query_start_loc,
                                          batch.seq_lens, batch.scale, rows, dtype=batch.dtype)

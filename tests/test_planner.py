@@ -37,11 +37,11 @@ def check_against_oracle(qlens, lens, **kw):
     return plan, info
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_config_metadata_is_bit_exact(cfg):
     qlens, lens, sp = config_lengths(cfg)
     H, Hkv, d, bs = {1: (4, 2, 64, 16), 2: (32, 8, 128, 16), 3: (32, 8, 128, 16), 4: (64, 8, 128, 64),
-                     5: (32, 8, 128, 16)}[cfg]
+                     5: (32, 8, 128, 16), 6: (32, 8, 128, 16)}[cfg]
     check_against_oracle(qlens, lens, H=H, Hkv=Hkv, d=d, bs=bs)
 
 
@@ -76,23 +76,23 @@ def test_split_items_cover_each_decode_exactly():
 def test_wide_prefill_takes_eight_waves_beside_decodes():
     """bf16 pool, head size 128, g = 4: a prefill alone runs 4-wave workgroups
     of 8 column tiles (32 positions of 4 heads); beside decodes, 8-wave
-    workgroups of 16 tiles (64 positions), which fill a CU each; a shared
-    prefix beside decodes alone takes the 8-wave shape too, with prefills the
-    4-wave one; an e4m3 pool and fp32 queries keep 4 waves."""
+    workgroups of 16 tiles (64 positions), which fill a CU each, with or
+    without a shared prefix; an e4m3 pool and fp32 queries keep 4 waves."""
     _, alone = host_plan([100], [100])
     _, mixed = host_plan([1, 100], [300, 100])
     assert alone["prefill_rows_per_item"] == 32 and mixed["prefill_rows_per_item"] == 64
     bt = np.zeros((2, 20), dtype=np.int32)
     bt[1, 1:] = np.arange(1, 20)
-    # a shared prefix with decodes alone runs beside the decode in 8-wave
-    # workgroups when the decode's workgroups have 8 waves (8 KV heads); with 2
-    # KV heads, or with a prefill as well, before it in 4-wave workgroups
+    # a shared prefix with decodes alone runs in the decode's launch (8-wave
+    # workgroups) when the decode's workgroups have 8 waves (8 KV heads); with
+    # 2 KV heads before the decode (4 waves); with prefills, the prefix pass
+    # and the prefills run on the side stream beside the decode (8 waves)
     _, casc = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40, H=32, Hkv=8)
     assert casc["prefill_rows_per_item"] == 64 and casc["prefix_beside_decode"] == 1
     _, c2 = host_plan([1, 1], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40)
     assert c2["prefill_rows_per_item"] == 32 and c2["prefix_beside_decode"] == 0
     _, cpre = host_plan([1, 20], [300, 200], prefix=16, block_table=bt, mbs=20, num_blocks=40, H=32, Hkv=8)
-    assert cpre["prefill_rows_per_item"] == 32 and cpre["prefix_beside_decode"] == 0
+    assert cpre["prefill_rows_per_item"] == 64 and cpre["prefix_beside_decode"] == 0
     _, f32 = host_plan([1, 100], [300, 100], dtype="fp32")
     assert f32["prefill_rows_per_item"] == 32
     params = pa.make_params(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, num_blocks=40,
@@ -377,3 +377,38 @@ def test_prefix_beside_decode_takes_cus_of_its_own():
     pieces = np.bincount(spans[:, 0], minlength=R)
     assert np.all(spans[:, 1] >= P)
     assert np.array_equal(parts, chunks + pieces)
+
+
+def test_prefix_pass_covers_decode_rows_only():
+    """With a shared prefix, prefill rows attend to their whole context in
+    their own items (one contribution, no partial record); the prefix pass
+    covers the decode rows, one run of consecutive rows at a time, and each
+    decode row merges its prefix chunks with its suffix pieces."""
+    P, bs = 64, 16
+    qlens = np.array([1, 1, 30, 1, 20, 1, 1])       # decode runs: rows [0, 2), [32, 33), [53, 55)
+    lens = np.array([P + 40, P + 300, P + 50, P + 7, P + 100, P + 1, P + 64])
+    mbs = int(max(-(-int(L) // bs) for L in lens))
+    bt = np.zeros((len(lens), mbs), dtype=np.int32)
+    nxt = P // bs
+    for b in range(len(lens)):
+        bt[b, :P // bs] = np.arange(P // bs)
+        own = -(-int(lens[b]) // bs) - P // bs
+        bt[b, P // bs:P // bs + own] = np.arange(nxt, nxt + own)
+        nxt += own
+    plan, info = host_plan(qlens, lens, H=8, Hkv=2, block_table=bt, num_blocks=nxt, mbs=mbs, prefix=P)
+    qsl = np.concatenate([[0], np.cumsum(qlens)])
+    parts = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS)
+    pre_rows = np.concatenate([np.arange(qsl[b], qsl[b + 1]) for b in range(len(lens)) if qlens[b] > 1])
+    dec_rows = qsl[:-1][qlens == 1]
+    assert np.all(parts[pre_rows] == 0)
+    assert np.all(parts[dec_rows] >= 2)                 # at least one prefix chunk and one suffix piece
+    Q = info["prefill_rows_per_item"]
+    runs = [(0, 2), (32, 33), (53, 55)]
+    items_per_chunk = sum(-(-(e - s) // Q) for s, e in runs)
+    assert info["num_prefix_items"] % items_per_chunk == 0
+    # every row group of every run reads the whole prefix once per KV head (2)
+    assert info["prefix_tokens_read"] == items_per_chunk * P * info["prefill_head_groups"] * 2
+    # prefill items read their whole context, prefix included
+    pre_keys = sum(sum(min(int(lens[b]), int(lens[b]) - int(qlens[b]) + i0 + min(Q, int(qlens[b]) - i0))
+                       for i0 in range(0, int(qlens[b]), Q)) for b in range(len(lens)) if qlens[b] > 1)
+    assert info["prefill_tokens_read"] == pre_keys * 2 * info["prefill_head_groups"]

@@ -264,7 +264,9 @@ def make_batch(
 
 # ---------------------------------------------------------------------------
 # The five workload shapes.  Configuration 1 is fixed; 2-5 draw their lengths
-# from a PCG64 stream seeded with the configuration number.
+# from a PCG64 stream seeded with the configuration number.  Shape 6 is an
+# extra beyond the five: the cascade batch with four 512-token prefill chunks
+# that share its prefix (a shared-prefix step with decodes and prefills).
 # ---------------------------------------------------------------------------
 
 CONFIG_NAMES = {
@@ -273,6 +275,7 @@ CONFIG_NAMES = {
     3: "prefill_causal_varlen",
     4: "chunked_prefill_mixed",
     5: "cascade_shared_prefix",
+    6: "cascade_shared_prefix_with_chunks",
 }
 
 CONFIG_SHAPES = {
@@ -281,6 +284,7 @@ CONFIG_SHAPES = {
     3: dict(num_heads=32, num_kv_heads=8, head_size=128, block_size=16, dtype="bf16"),
     4: dict(num_heads=64, num_kv_heads=8, head_size=128, block_size=64, dtype="bf16"),
     5: dict(num_heads=32, num_kv_heads=8, head_size=128, block_size=16, dtype="bf16"),
+    6: dict(num_heads=32, num_kv_heads=8, head_size=128, block_size=16, dtype="bf16"),
 }
 
 
@@ -306,12 +310,21 @@ def config_lengths(cfg: int, seed: int | None = None):
         P = 16384
         s = rng.integers(256, 2048, size=128, endpoint=True)
         return np.ones(128, dtype=np.int64), P + s, P // 16
+    if cfg == 6:
+        # the cascade batch's decodes, then 4 chunks of 512 queries whose
+        # context is the shared prefix plus 256..2048 tokens of their own
+        P = 16384
+        s = rng.integers(256, 2048, size=128, endpoint=True)
+        own = rng.integers(256, 2048, size=4, endpoint=True)
+        q = np.concatenate([np.ones(128, dtype=np.int64), np.full(4, 512)])
+        return q, np.concatenate([P + s, P + own + 512]), P // 16
     raise ValueError(f"unknown configuration {cfg}")
 
 
 def config_batch(cfg: int, seed: int | None = None, poison: bool = True, kv_dtype: str = "same",
                  kv_layout: str = "NHD", block_size: int | None = None) -> Batch:
-    """Draw the full-size batch of configuration ``cfg`` (1..5); ``kv_dtype``
+    """Draw the full-size batch of configuration ``cfg`` (1..5, or the extra
+    shape 6); ``kv_dtype``
     "fp8_e4m3" gives the same lengths and placement over an e4m3 pool."""
     seed = cfg if seed is None else seed
     qlens, lens, sp = config_lengths(cfg, seed)
