@@ -382,7 +382,7 @@ def _kernel(t, prefix):
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str, workload: str,
-                  kernels=("decode_kernel", "prefill_wide_kernel", "merge_kernel")) -> dict:
+                  kernels=("prefix_decode_kernel", "decode_kernel", "prefill_wide_kernel", "merge_kernel")) -> dict:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) of `bench.py --workload <workload>` into HBM bytes per launch of
     each kernel, each counter scaled by what it reads for the plain device copy
@@ -421,13 +421,17 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_bytes: int, command: str,
         res = {}
     calib = {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale, "command": command}
     res["_calibration"] = calib
+    families = {"prefix_decode_kernel": "prefix_decode", "decode_kernel": "decode", "prefill_wide_kernel": "prefill",
+                "merge_kernel": "merge"}
     for name in fetch:
-        fam = next((k for k in kernels if k in name), None)
+        # the longest family name that the kernel's name holds (prefix_decode_kernel holds decode_kernel)
+        fam = max((k for k in kernels if k in name), key=len, default=None)
         if fam is None or name not in write:
             continue
-        family = {"decode_kernel": "decode", "prefill_wide_kernel": "prefill", "merge_kernel": "merge"}[fam]
+        family = families[fam]
         tag = ("bf16_e4m3_d128" if "unsigned char, 128" in name else
-               "bf16_d128" if "unsigned short, 128" in name or "prefill_wide" in name else None)
+               "bf16_d128" if "unsigned short, 128" in name or "prefill_wide" in name or fam == "prefix_decode_kernel"
+               else None)
         if tag is None:
             continue
         fb = fetch[name] * 1024.0 * f_scale
@@ -551,7 +555,7 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-command", default="", help="command recorded with --summarize-pmc")
-    ap.add_argument("--pmc-kernels", default="decode_kernel,prefill_wide_kernel,merge_kernel",
+    ap.add_argument("--pmc-kernels", default="prefix_decode_kernel,decode_kernel,prefill_wide_kernel,merge_kernel",
                     help="kernel families --summarize-pmc records (comma-separated)")
     ap.add_argument("--pmc-workload", default="decode",
                     help="the --workload of the profiled runs that --summarize-pmc reads (default workload "
