@@ -133,7 +133,9 @@ typedef struct pa_plan_info {
                                    wave per KV head) in order; one item per list unless balanced */
   int32_t decode_list_tokens;   /* balanced lists: keys per list (equal up to the last); else 0 */
   int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
-  int64_t prefix_tokens_read;   /* of which rows of the shared prefix */
+  int64_t prefix_tokens_read;   /* of which rows of the shared prefix (the prefix pass covers the
+                                   decode rows; prefill rows read their whole context in their own
+                                   items) */
   int64_t decode_tokens_read;   /* of which by decode work items */
   int64_t prefill_tokens_read;  /* of which by prefill work items */
   int64_t prefix_tokens_unique; /* distinct (KV head, prefix token) rows the prefix pass reads: P * Hkv
@@ -203,8 +205,12 @@ pa_status pa_kv_cache_stride_order(int32_t layout, int32_t order_out[5]);
  * Cascade («El especialista del plato estrella», §Qué aporta FlashInfer): with
  * P = common_prefix_len > 0 the first P / bs block ids must be identical in every
  * row, P must be a multiple of bs, and P <= c_b for every sequence (the prefix
- * is context of all of them).  Violations -> INVALID_ARG.
- * The plan copies its work lists to device memory it owns (a few KB).
+ * is context of all of them).  Violations -> INVALID_ARG.  The decode rows
+ * attend to the prefix in one shared pass, merged with their own suffix by
+ * LSE; prefill rows attend to their whole context (the result is the same
+ * attention).
+ * The plan copies its work lists and the metadata (for pa_plan_check_metadata)
+ * to device memory it owns.
  * Errors: INVALID_ARG (any rule above, H % Hkv != 0, NULL pointers),
  * UNSUPPORTED (head_size, dtype), HIP / OOM (device copy).
  */
