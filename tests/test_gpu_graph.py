@@ -15,6 +15,12 @@ CASES = {
     "decode_only_lists": dict(qlens=[1] * 9, lens=[5, 300, 1200, 4096, 1, 77, 900, 2500, 33]),
     "cascade": dict(qlens=[1, 1, 1, 9], lens=[128 + 5, 128 + 300, 128 + 40, 128 + 9], shared_prefix_blocks=8),
     "e4m3_hnd_mixed": dict(qlens=[1, 1, 70], lens=[300, 2000, 200], kv_dtype="fp8_e4m3", kv_layout="HND"),
+    # 8 KV heads, decodes alone: the prefix pass and the decode in one launch
+    "cascade_fused_hkv8": dict(qlens=[1] * 6, lens=[256 + 5, 256 + 300, 256 + 40, 256 + 1, 256 + 900, 256 + 64],
+                               shared_prefix_blocks=16, num_heads=32, num_kv_heads=8),
+    # 8 KV heads with a prefill: prefix pass and prefill on the side stream
+    "cascade_prefill_hkv8": dict(qlens=[1, 1, 1, 40], lens=[256 + 5, 256 + 300, 256 + 40, 256 + 90],
+                                 shared_prefix_blocks=16, num_heads=32, num_kv_heads=8),
 }
 
 
@@ -23,7 +29,9 @@ def test_graph_replays_match_eager(name):
     import torch
     kw = dict(CASES[name])
     qlens, lens = kw.pop("qlens"), kw.pop("lens")
-    b = make_batch(qlens, lens, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, seed=80, **kw)
+    kw.setdefault("num_heads", 8)
+    kw.setdefault("num_kv_heads", 2)
+    b = make_batch(qlens, lens, head_size=128, block_size=16, seed=80, **kw)
     announce(f"graph {name}")
     out_e, lse_e, db = run_gpu(b)
     s = torch.cuda.Stream()

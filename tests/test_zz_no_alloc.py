@@ -2,7 +2,8 @@
 device array.  Its output must equal pa_forward's (same kernels) bit for bit,
 on two calls in a row, the second with a smaller batch (the array keeps the
 first call's contents), and it must refuse a plan whose workspace exceeds the
-array, launching nothing."""
+array, launching nothing; captured into a HIP graph (a caller that cannot
+allocate), every replay must give the eager result."""
 import numpy as np
 import pytest
 
@@ -62,3 +63,34 @@ def test_noalloc_rejects_a_plan_larger_than_the_scratch():
     assert ei.value.status == pa.PA_ERR_INVALID_ARG and "static scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert bool(torch.all(out.float() == 3.0))
+
+
+def test_noalloc_in_a_graph():
+    import torch
+    batch = make_batch([1, 1, 1, 30], [700, 64, 1500, 130], num_heads=8, num_kv_heads=2, head_size=128,
+                       block_size=16, seed=82)
+    announce("noalloc captured into a graph")
+    db = _device(batch, 64)
+    assert pa.pa_plan_workspace_bytes(db.plan) > 0
+    db.forward()
+    torch.cuda.synchronize()
+    want_o, want_l = db.out.clone(), db.lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the capture stream (the first call looks the array up)
+        pa.pa_forward_noalloc(db.plan, db.q, db.kv_cache, db.block_table, db.query_start_loc, db.seq_lens, db.out,
+                              db.lse, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.pa_forward_noalloc(db.plan, db.q, db.kv_cache, db.block_table, db.query_start_loc, db.seq_lens, db.out,
+                              db.lse)
+    for rep in range(3):
+        db.out.zero_()
+        db.lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(db.out, want_o) and torch.equal(db.lse, want_l), f"replay {rep} differs"
+        db.forward()  # eager work between replays
+        torch.cuda.synchronize()
