@@ -298,7 +298,8 @@ pa_status pa_forward(const pa_plan* plan, const void* q, const void* kv_cache,
  * 64 MiB that the library holds on each device it runs on (until the process
  * ends) instead of caller memory.  The call itself allocates nothing; its first
  * call for a device looks the array's address up.
- *  Arguments as pa_forward, without workspace.
+ *  Arguments as pa_forward, without workspace; the plan's pool holds q's
+ *  element type (an e4m3 plan -> INVALID_ARG, as for pa_forward).
  * Every call on one device shares that device's array: calls that overlap in
  * time on one GPU (other streams, other threads) race on it and must be
  * serialised by the caller.  Nothing in the array needs clearing: every

@@ -412,3 +412,59 @@ def test_prefix_pass_covers_decode_rows_only():
     pre_keys = sum(sum(min(int(lens[b]), int(lens[b]) - int(qlens[b]) + i0 + min(Q, int(qlens[b]) - i0))
                        for i0 in range(0, int(qlens[b]), Q)) for b in range(len(lens)) if qlens[b] > 1)
     assert info["prefill_tokens_read"] == pre_keys * 2 * info["prefill_head_groups"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_cascade_schedules_cover_rows_and_fit_the_chip(seed):
+    """Random batches with a shared prefix (8 KV heads, so decodes alone take
+    the fused launch): the prefix chunks tile [0, P); with decodes alone, the
+    prefix units (chunks x 64-row groups x KV heads) and the decode lists fit
+    the 256 CUs a host-only plan assumes; every decode row merges its prefix
+    chunks with its suffix pieces, and prefill rows have no partial record."""
+    rng = np.random.default_rng(100 + seed)
+    bs = 16
+    P = bs * int(rng.integers(1, 300))
+    B = int(rng.integers(1, 200))
+    prefills = seed % 2 == 1
+    qlens = np.where(rng.random(B) < (0.1 if prefills else 0.0), rng.integers(2, 300, size=B), 1)
+    lens = P + qlens - 1 + rng.integers(1, 3000, size=B)
+    mbs = int(max(-(-int(L) // bs) for L in lens))
+    bt = np.zeros((B, mbs), dtype=np.int32)
+    nxt = P // bs
+    for b in range(B):
+        bt[b, :P // bs] = np.arange(P // bs)
+        own = -(-int(lens[b]) // bs) - P // bs
+        bt[b, P // bs:P // bs + own] = np.arange(nxt, nxt + own)
+        nxt += own
+    plan, info = host_plan(qlens, lens, H=32, Hkv=8, bs=bs, block_table=bt, num_blocks=nxt, mbs=mbs, prefix=P)
+    qsl = np.concatenate([[0], np.cumsum(qlens)])
+    dec = qlens == 1
+    parts = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ROW_PARTIALS)
+    spans = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_SPANS).reshape(-1, 3)
+    pieces = np.bincount(spans[:, 0], minlength=B)
+    assert np.all(spans[:, 1] >= P)
+    assert info["prefix_beside_decode"] == (0 if prefills and (~dec).any() else 1)
+    # decode rows: consecutive runs of decode rows, grouped by the prefix item row count
+    Q = info["prefill_rows_per_item"]
+    runs, start = [], None
+    for b in range(B):
+        if dec[b] and start is None:
+            start = b
+        if (not dec[b] or b == B - 1) and start is not None:
+            end = b + 1 if dec[b] else b
+            runs.append(end - start)
+            start = None
+    groups = sum(-(-n // Q) for n in runs)
+    assert info["num_prefix_items"] % groups == 0
+    chunks = info["num_prefix_items"] // groups
+    assert 1 <= chunks <= -(-P // 64)
+    assert info["prefix_tokens_read"] == groups * P * info["prefill_head_groups"] * 8
+    rows_dec = qsl[:-1][dec]
+    want = np.where(chunks + pieces[dec] > 1, chunks + pieces[dec], 0)
+    assert np.array_equal(parts[rows_dec], want)
+    if (~dec).any():
+        pre_rows = np.concatenate([np.arange(qsl[b], qsl[b + 1]) for b in range(B) if not dec[b]])
+        assert np.all(parts[pre_rows] == 0)
+    if info["prefix_beside_decode"]:
+        units = info["num_prefix_items"] * 8 * info["prefill_head_groups"]
+        assert units + info["num_decode_lists"] <= 256
