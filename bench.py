@@ -17,8 +17,9 @@ Prints ONE JSON line.  Algorithmic work counts each KV byte once per KV head
 (decode) and 4*H*d FLOPs per visible (query, key) pair (prefill); masked and
 skipped work is not counted.  ``roofline.achieved`` divides that by the
 dominant kernel's average launch duration, measured with HIP events recorded
-on the launch stream by the library (pa_profile_start/stop) over the timed
-region.
+on the launch stream by the library (pa_profile_start/stop) over a pass of the
+same number of steps run right after the timed one: those records sit between
+the launches of a step and would lengthen it, so the timed steps go without.
 """
 from __future__ import annotations
 
@@ -123,10 +124,13 @@ def _batch_to_device(batch, common_prefix_len=None, kv_split_tokens=0):
 
 def time_steps(db, steps: int, warmup: int) -> dict:
     """Warm up, then time `steps` forwards: wall clock between synchronisations
-    (ms_per_step), HIP events on the caller's stream around each forward (the
-    step's device time; the side stream joins it before the forward ends), and
-    HIP events the library records around each of its launches (per kernel:
-    average, median, shortest and longest launch)."""
+    (ms_per_step) and HIP events on the caller's stream around each forward
+    (the step's device time; the side stream joins it before the forward
+    ends).  Then the same number of forwards again with the HIP events the
+    library records around each of its launches (per kernel: average, median,
+    shortest and longest launch): those records sit between the launches and
+    lengthen a step of several kernels by about 20 us, so the step is timed
+    without them."""
     import torch
 
     import attention_paged_kv_varlen_amd as pa
@@ -135,7 +139,6 @@ def time_steps(db, steps: int, warmup: int) -> dict:
         db.forward(stream)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    pa.pa_profile_start(steps * 8 + 8)
     t0 = time.perf_counter()
     for e0, e1 in ev:
         e0.record(stream)
@@ -143,6 +146,10 @@ def time_steps(db, steps: int, warmup: int) -> dict:
         e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    pa.pa_profile_start(steps * 8 + 8)
+    for _ in range(steps):
+        db.forward(stream)
+    torch.cuda.synchronize()
     kern = pa.pa_profile_stop()
     step = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     return {
@@ -487,12 +494,16 @@ def kvwrite_line(steps: int, warmup: int, cpu: bool, kv_dtype: str = "same") -> 
     for _ in range(warmup):
         write(stream)
     torch.cuda.synchronize()
-    pa.pa_profile_start(steps + 8)
     t0 = time.perf_counter()
     for _ in range(steps):
         write(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    # per-launch events in a pass of their own (they are not part of the step)
+    pa.pa_profile_start(steps + 8)
+    for _ in range(steps):
+        write(stream)
+    torch.cuda.synchronize()
     kern = pa.pa_profile_stop()
     us = {x["name"]: 1e3 * x["total_ms"] / max(x["launches"], 1) for x in kern}
     # K and V rows read once (bf16) and written once (bf16, or one-byte codes)
