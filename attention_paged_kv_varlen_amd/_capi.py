@@ -52,7 +52,7 @@ class pa_plan_info(ctypes.Structure):
         ("num_decode_lists", c_int32), ("decode_list_tokens", c_int32),
         ("kv_tokens_read", c_int64), ("prefix_tokens_read", c_int64),
         ("decode_tokens_read", c_int64), ("prefill_tokens_read", c_int64),
-        ("prefix_tokens_unique", c_int64), ("prefix_beside_decode", c_int32), ("pad_", c_int32),
+        ("prefix_tokens_unique", c_int64), ("prefix_beside_decode", c_int32), ("decode_item_keys", c_int32),
     ]
 
 

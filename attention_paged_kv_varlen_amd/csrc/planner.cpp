@@ -81,6 +81,10 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
 // from HBM (the decode as a whole at most about 6.5 TB/s).  A unit's fixed
 // cost (its Q rows in, the first K/V block's latency, its output out) is
 // worth about 192 keys.
+// A decode work item's start (its row of Q, its first block-table entries,
+// then its first K/V step, one after the other) costs a decode workgroup
+// about as much time as streaming 64 keys; the balanced lists count it.
+constexpr int kDecodeItemKeys = 64;
 constexpr double kPrefixFlopsPerCu = 3.6e12;
 constexpr double kDecodeBytesPerCu = 25.0e9;
 constexpr double kDecodeBytesAll = 6.5e12;
@@ -279,12 +283,41 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     if (np > 0)
       lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens, nd)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
-    // A list is closed with up to 31 keys of room unused (cuts inside a
-    // sequence fall on multiples of 32), so each holds 32 keys more than the
-    // even share: every closed list then takes more than the share, and the
-    // keys never spill into lists beyond n_lists (which would run as a second,
-    // nearly empty round of workgroups).
-    list_tokens = (int)round_up(ceil_div(dec_tokens, n_lists), 32) + 32;
+    // Each list gets a budget of W keys, each of its items counting
+    // kDecodeItemKeys more.  A list is closed with up to 31 (after an item) or
+    // 31 + kDecodeItemKeys (before one) of its budget unused, so W is the
+    // smallest multiple of 32 from the even share up whose cut needs at most
+    // n_lists lists: keys never spill into a second, nearly empty round of
+    // workgroups.
+    auto lists_needed = [&](int W) {
+      int64_t n = 0;
+      int filled = 0;
+      for (int oi = 0; oi < nd; ++oi) {
+        const int L = seq_lens[hp.order[oi]];
+        for (int k0 = P; k0 < L;) {
+          if (W - filled - kDecodeItemKeys < 32) {
+            ++n;
+            filled = 0;
+          }
+          filled += kDecodeItemKeys;
+          const int room = W - filled;
+          const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
+          k0 += take;
+          filled += take;
+          if (W - filled < 32) {
+            ++n;
+            filled = 0;
+          }
+        }
+      }
+      return n + (filled > 0 ? 1 : 0);
+    };
+    // (every sequence is at least one item: the even share of keys and item
+    // starts is a lower bound)
+    int W = (int)std::max<int64_t>(32 + kDecodeItemKeys,
+                                   round_up(ceil_div(dec_tokens + (int64_t)nd * kDecodeItemKeys, n_lists), 32));
+    while (lists_needed(W) > n_lists) W += 32;
+    list_tokens = W;
     split = list_tokens;
   } else if (split == 0) {
     const int64_t target_items = std::max<int64_t>(1, (int64_t)32 * std::max(num_cus, 1) / Hkv);
@@ -296,14 +329,20 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   if (balanced) {
     // Cuts inside a sequence fall on multiples of 32 keys (the decode kernel's
     // 16-key tiles must not straddle a physical block); a list is closed once
-    // less than 32 keys of room are left.
-    int filled = 0;  // keys in the open list
+    // less than 32 keys of room are left, or before an item that would start
+    // with less (the same cut lists_needed counts).
+    int filled = 0;  // budget used in the open list
     hp.decode_lists.push_back(0);
     for (int oi = 0; oi < nd; ++oi) {
       const int b = hp.order[oi];
       const int L = seq_lens[b];
       int part = 0;
       for (int k0 = P; k0 < L;) {
+        if (list_tokens - filled - kDecodeItemKeys < 32) {
+          hp.decode_lists.push_back((int32_t)hp.decode_items.size());
+          filled = 0;
+        }
+        filled += kDecodeItemKeys;
         const int room = list_tokens - filled;  // >= 32
         const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
         WorkItem it{};
@@ -472,6 +511,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   in.prefix_tokens_read = pfx_read * Hkv;
   in.prefix_tokens_unique = (int64_t)P * Hkv;
   in.prefix_beside_decode = hp.prefix_beside ? 1 : 0;
+  in.decode_item_keys = list_tokens > 0 ? kDecodeItemKeys : 0;
   in.kv_tokens_read = in.decode_tokens_read + in.prefill_tokens_read + in.prefix_tokens_read;
   return PA_OK;
 }

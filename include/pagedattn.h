@@ -131,7 +131,9 @@ typedef struct pa_plan_info {
   int32_t prefill_head_groups;  /* prefill work items per KV head and position block */
   int32_t num_decode_lists;     /* decode work lists: each is run by one group of waves (one
                                    wave per KV head) in order; one item per list unless balanced */
-  int32_t decode_list_tokens;   /* balanced lists: keys per list (equal up to the last); else 0 */
+  int32_t decode_list_tokens;   /* balanced lists: the budget of each list, in keys, where each of
+                                   its items also counts decode_item_keys (every list but the last
+                                   comes within 32 + decode_item_keys of it); else 0 */
   int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
   int64_t prefix_tokens_read;   /* of which rows of the shared prefix (the prefix pass covers the
                                    decode rows; prefill rows read their whole context in their own
@@ -144,7 +146,7 @@ typedef struct pa_plan_info {
   int32_t prefix_beside_decode; /* 1: the shared-prefix pass runs beside the decode on CUs of its
                                    own (one prefix workgroup per CU; the decode lists cover the
                                    others); 0: before it, or no prefix */
-  int32_t pad_;
+  int32_t decode_item_keys;     /* balanced lists: what one work item's start costs, in keys */
 } pa_plan_info;
 
 /* Arrays a plan exposes through pa_plan_get_array. */

@@ -223,17 +223,19 @@ def _decode_schedule(plan, info):
 @pytest.mark.parametrize("seed", range(4))
 def test_balanced_decode_lists_partition_the_keys(seed):
     """A batch of decodes alone, automatic split: the lists cut the decode keys,
-    sequence after sequence in decode-first order, into equal runs; every key
-    of every sequence is covered exactly once, in order."""
+    sequence after sequence in decode-first order, into runs of equal cost
+    (keys, plus decode_item_keys for each item); every key of every sequence
+    is covered exactly once, in order."""
     rng = np.random.default_rng(100 + seed)
     B = int(rng.integers(1, 60))
     lens = rng.integers(1, 9000, size=B)
     plan, info = host_plan([1] * B, lens, H=32, Hkv=8)
     lists, spans = _decode_schedule(plan, info)
-    W = info["decode_list_tokens"]
-    assert W > 0 and W % 32 == 0 and info["kv_split_tokens"] == W
+    W, ik = info["decode_list_tokens"], info["decode_item_keys"]
+    assert W > 0 and W % 32 == 0 and info["kv_split_tokens"] == W and ik > 0
     sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
-    assert np.all(sizes[:-1] > W - 32) and np.all(sizes <= W) and sizes[-1] > 0
+    cost = sizes + ik * np.diff(lists)
+    assert np.all(cost[:-1] > W - 32 - ik) and np.all(cost <= W) and sizes[-1] > 0
     # items start on 32-key boundaries of their sequence (16-key tiles never
     # straddle a physical block)
     assert np.all(spans[:, 1] % 32 == 0)
@@ -253,13 +255,35 @@ def test_balanced_decode_lists_partition_the_keys(seed):
     assert info["decode_tokens_read"] == int(lens.sum()) * 8
 
 
+def _lists_needed(lens, W, ik):
+    """The list cut of the balanced decode schedule, counted: a list closes
+    when less than 32 of its budget W is left, or before an item (which costs
+    ik) that would start with less."""
+    n, filled = 0, 0
+    for L in lens:
+        k0 = 0
+        while k0 < L:
+            if W - filled - ik < 32:
+                n, filled = n + 1, 0
+            filled += ik
+            room = W - filled
+            take = L - k0 if L - k0 <= room else room // 32 * 32
+            k0 += take
+            filled += take
+            if W - filled < 32:
+                n, filled = n + 1, 0
+    return n + (1 if filled > 0 else 0)
+
+
 def test_balanced_decode_lists_never_exceed_the_resident_groups():
-    """Each list may close with up to 31 keys of room unused (cuts inside a
-    sequence fall on 32-key boundaries); the planner sizes the lists so that
-    the keys still fit in one list per resident group of waves (host plans: 256
-    CUs, one 8-wave workgroup per CU at Hkv = 8), never spilling into a second
-    round.  The suffix lengths of the cascade batch (128 decodes, U[256, 2048])
-    once gave 258 lists."""
+    """Each list may close with up to 31 keys of its budget unused (cuts inside
+    a sequence fall on 32-key boundaries), or 31 + decode_item_keys before an
+    item; the planner sizes the lists so that the keys still fit in one list
+    per resident group of waves (host plans: 256 CUs, one 8-wave workgroup per
+    CU at Hkv = 8), never spilling into a second round, and takes the smallest
+    budget that does (one budget step less would need more lists).  The
+    suffix lengths of the cascade batch (128 decodes, U[256, 2048]) once gave
+    258 lists."""
     from workloads import config_lengths
     _, L, sp = config_lengths(5)
     suffix = [int(x) - 16 * sp for x in L]
@@ -270,9 +294,13 @@ def test_balanced_decode_lists_never_exceed_the_resident_groups():
         lists, spans = _decode_schedule(plan, info)
         need = -(-int(np.sum(lens)) // 256)
         assert info["num_decode_lists"] <= min(256, need), (len(lens), info["num_decode_lists"])
-        W = info["decode_list_tokens"]
+        W, ik = info["decode_list_tokens"], info["decode_item_keys"]
         sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
-        assert sizes.sum() == int(np.sum(lens)) and np.all(sizes <= W) and np.all(sizes[:-1] > W - 32)
+        cost = sizes + ik * np.diff(lists)
+        assert sizes.sum() == int(np.sum(lens)) and np.all(cost <= W) and np.all(cost[:-1] > W - 32 - ik)
+        # the smallest budget: the same cut with W - 32 needs more lists
+        if W - 32 >= 32 + ik:
+            assert _lists_needed(lens, W - 32, ik) > min(256, need)
 
 
 def test_decode_lists_are_single_items_with_an_explicit_split():
