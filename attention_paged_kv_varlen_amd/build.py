@@ -3,7 +3,9 @@
 Usage: ``python -m attention_paged_kv_varlen_amd.build`` (or ``build()``).  Every
 call recompiles.  The packed-FP32 target feature is switched off for the device
 code (ordinary float code only); the host-only sources (planner, C ABI) are
-compiled as plain C++ without it.
+compiled as plain C++ without it.  The same call builds ``chip_probe``, a
+stand-alone measurement program (csrc/chip_probe.hip) that shares no code with
+the library.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedattn.so")
+PROBE = os.path.join(PKG, "chip_probe")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -56,6 +59,13 @@ def build(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         os.replace(out_tmp, LIB)
+        probe_tmp = PROBE + ".tmp"
+        cmd = [cc, "-x", "hip", f"--offload-arch={ARCH}", *DEVICE_FLAGS, "-O3", "-std=c++17", "-Wall",
+               os.path.join(CSRC, "chip_probe.hip"), "-o", probe_tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(probe_tmp, PROBE)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return LIB

@@ -1,0 +1,231 @@
+// chip_probe: measured rates of the gfx950 units that bound the attention
+// kernels, printed as text.  It is a measurement program beside the library
+// (built with it, linked against nothing of it): the roofline figures of the
+// prefill are quoted against these numbers next to the specification's peak.
+//
+//   issue  short single launches (~0.3 ms, before the clock settles): SIMD
+//          cycles per wave instruction (launch time x the clock read from the
+//          shader clock counter, over the two waves' instructions), for an
+//          FMA, an exp2, a 16x16x32 and a 32x32x16 bf16 MFMA, and for one
+//          16x16x32 MFMA followed by k independent FMAs (k = 1..4): how much
+//          VALU work one MFMA's execution hides.
+//   power  20 back-to-back launches (~90 ms) of an MFMA loop on random bf16
+//          operands, alone and interleaved with the VALU work the softmax
+//          spends per score (an FMA, an exp2, an add and half a bf16 pack per
+//          score, 0.5 scores per lane and 16x16x32 MFMA): sustained TFLOP/s
+//          and the clock the chip settles at under that power draw; and the
+//          bare MFMA loop once more on all-zero operands, whose bits never
+//          toggle.
+//
+// Every workgroup fills one CU (8 waves, two per SIMD; 96 KB of LDS keeps a
+// second workgroup off the CU), one workgroup per CU.  The instruction order
+// inside each loop is fixed with inline asm (compute instructions only: no
+// loads or stores in asm).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 512;
+constexpr size_t kLds = 96 * 1024;
+
+#define CHECK(x)                                                                 \
+  do {                                                                           \
+    hipError_t e_ = (x);                                                         \
+    if (e_ != hipSuccess) {                                                      \
+      fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));             \
+      exit(1);                                                                   \
+    }                                                                            \
+  } while (0)
+
+// Loop bodies.  M16/M32: one MFMA on accumulator i with operand pair
+// (ra[i], rb[i + 1]); F, E, A, C: independent VALU chains (FMA, exp2, add,
+// bf16 pack).
+#define M16(i) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[i]) : "v"(ra[i]), "v"(rb[((i) + 1) & 3]))
+#define M32(i) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc2[i]) : "v"(ra[2 * (i)]), "v"(rb[2 * (i) + 1]))
+#define F(i) asm volatile("v_fma_f32 %0, %0, %1, 0.5" : "+v"(fv[i]) : "v"(x))
+#define E(i) asm volatile("v_exp_f32 %0, %0" : "+v"(ev[i]))
+#define A(i) asm volatile("v_add_f32 %0, %0, %1" : "+v"(sv[i]) : "v"(x))
+#define C(i) asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(cv[i]) : "v"(fv[i]), "v"(x))
+
+enum Body {
+  kFma16,      // 16 FMAs
+  kExp16,      // 16 exp2
+  kMfma16,     // 4 x 16x16x32
+  kMfma32,     // 2 x 32x32x16 (same FLOPs)
+  kMfmaFma1,   // 4 x (16x16x32, 1 FMA)
+  kMfmaFma2,   // 4 x (16x16x32, 2 FMA)
+  kMfmaFma3,   // 4 x (16x16x32, 3 FMA)
+  kMfmaFma4,   // 4 x (16x16x32, 4 FMA)
+  kSoft16,     // 4 x 16x16x32 with 2 scores' softmax work (2 FMA, 2 exp2, 2 add, 1 pack)
+  kSoft32,     // 2 x 32x32x16 with the same VALU work
+  kMfma16Zero, // 4 x 16x16x32 on all-zero operands (no bit toggling)
+};
+
+template <int B>
+__global__ void __launch_bounds__(kThreads) probe_kernel(const float* in, unsigned long long* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  const float x = in[lane];
+  // pseudo-random bf16 operands (sums of uniforms: roughly normal), four
+  // pairs per lane, so that consecutive MFMAs see different data
+  bf16x8 ra[4], rb[4];
+  const bool zero = B == kMfma16Zero;
+  unsigned st = 0x9E3779B9u * (threadIdx.x + 1) + 7919u * blockIdx.x;
+  for (int q = 0; q < 4; ++q)
+    for (int i = 0; i < 8; ++i) {
+      float u = 0.f;
+      for (int t = 0; t < 4; ++t) {
+        st = st * 1664525u + 1013904223u;
+        u += (float)(st >> 8) * (1.0f / 16777216.0f);
+      }
+      ra[q][i] = (__bf16)(zero ? x : (u - 2.0f) * 1.7f + x);
+      st = st * 1664525u + 1013904223u;
+      rb[q][i] = (__bf16)(zero ? x : ((float)(st >> 8) * (1.0f / 16777216.0f) - 0.5f) * 3.4f + x);
+    }
+  f32x4 acc[4] = {};
+  f32x16 acc2[2] = {};
+  float fv[16], ev[16], sv[4];
+  unsigned cv[4];
+  for (int j = 0; j < 16; ++j) {
+    fv[j] = x + j;
+    ev[j] = -x - j;
+  }
+  for (int j = 0; j < 4; ++j) {
+    sv[j] = x;
+    cv[j] = j;
+  }
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), w0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (B == kFma16) {
+      F(0); F(1); F(2); F(3); F(4); F(5); F(6); F(7); F(8); F(9); F(10); F(11); F(12); F(13); F(14); F(15);
+    } else if constexpr (B == kExp16) {
+      E(0); E(1); E(2); E(3); E(4); E(5); E(6); E(7); E(8); E(9); E(10); E(11); E(12); E(13); E(14); E(15);
+    } else if constexpr (B == kMfma16 || B == kMfma16Zero) {
+      M16(0); M16(1); M16(2); M16(3);
+    } else if constexpr (B == kMfma32) {
+      M32(0); M32(1);
+    } else if constexpr (B == kMfmaFma1) {
+      M16(0); F(0); M16(1); F(1); M16(2); F(2); M16(3); F(3);
+    } else if constexpr (B == kMfmaFma2) {
+      M16(0); F(0); F(1); M16(1); F(2); F(3); M16(2); F(4); F(5); M16(3); F(6); F(7);
+    } else if constexpr (B == kMfmaFma3) {
+      M16(0); F(0); F(1); F(2); M16(1); F(3); F(4); F(5); M16(2); F(6); F(7); F(8); M16(3); F(9); F(10); F(11);
+    } else if constexpr (B == kMfmaFma4) {
+      M16(0); F(0); F(1); F(2); F(3); M16(1); F(4); F(5); F(6); F(7);
+      M16(2); F(8); F(9); F(10); F(11); M16(3); F(12); F(13); F(14); F(15);
+    } else if constexpr (B == kSoft16) {
+      M16(0); F(0); E(0); M16(1); A(0); C(0); M16(2); F(1); E(1); M16(3); A(1);
+    } else if constexpr (B == kSoft32) {
+      M32(0); F(0); E(0); A(0); M32(1); F(1); E(1); A(1); C(0);
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), w1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+  for (int j = 0; j < 16; ++j) s += fv[j] + ev[j];
+  for (int j = 0; j < 4; ++j) s += sv[j] + (float)cv[j] + acc[j][0] + acc[j][3];
+  for (int k = 0; k < 2; ++k) s += acc2[k][0] + acc2[k][15];
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = t1 - t0;
+    out[2 * blockIdx.x + 1] = w1 - w0;
+  }
+  // never true for the zero input; keeps every result live
+  if (in[64 + lane] == 12345.f) out[2 * gridDim.x + threadIdx.x] = (unsigned long long)s;
+}
+
+struct Result {
+  double ms;         // average per launch
+  double clock_ghz;  // shader cycles over real time (100 MHz counter), averaged over workgroups, last launch
+};
+
+template <int B>
+Result run(int n_cu, int iters, int launches, const float* in, unsigned long long* d_out, unsigned long long* h_out) {
+  auto k = probe_kernel<B>;
+  CHECK(hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds));
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  hipLaunchKernelGGL(k, dim3(n_cu), dim3(kThreads), kLds, 0, in, d_out, iters);  // warm-up
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e0));
+  for (int r = 0; r < launches; ++r) hipLaunchKernelGGL(k, dim3(n_cu), dim3(kThreads), kLds, 0, in, d_out, iters);
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  CHECK(hipMemcpy(h_out, d_out, sizeof(unsigned long long) * 2 * n_cu, hipMemcpyDeviceToHost));
+  double clk = 0.0;
+  for (int i = 0; i < n_cu; ++i) clk += (double)h_out[2 * i] / ((double)h_out[2 * i + 1] * 10.0);
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return Result{ms / launches, clk / n_cu};
+}
+
+}  // namespace
+
+int main() {
+  int dev = 0;
+  CHECK(hipSetDevice(dev));
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, dev));
+  const int n_cu = prop.multiProcessorCount;
+  float* in;
+  unsigned long long *d_out, *h_out;
+  CHECK(hipMalloc(&in, 128 * sizeof(float)));
+  CHECK(hipMemset(in, 0, 128 * sizeof(float)));
+  const size_t out_bytes = sizeof(unsigned long long) * (2 * (size_t)n_cu + kThreads);
+  CHECK(hipMalloc(&d_out, out_bytes));
+  h_out = static_cast<unsigned long long*>(malloc(out_bytes));
+  if (!h_out) return 1;
+  printf("device %s, %d CUs, %d waves per CU (2 per SIMD)\n", prop.gcnArchName, n_cu, kThreads / 64);
+
+  // issue rates: one short launch each; SIMD cycles per loop iteration of one
+  // wave = launch cycles / (2 waves x iterations)
+  const int it_short = 8192;
+  struct Row { const char* name; double instr; Result r; };
+  Row rows[] = {
+      {"16 x v_fma_f32", 16, run<kFma16>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"16 x v_exp_f32", 16, run<kExp16>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"4 x mfma 16x16x32 bf16", 4, run<kMfma16>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"2 x mfma 32x32x16 bf16", 2, run<kMfma32>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"4 x (mfma 16x16x32 + 1 fma)", 4, run<kMfmaFma1>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"4 x (mfma 16x16x32 + 2 fma)", 4, run<kMfmaFma2>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"4 x (mfma 16x16x32 + 3 fma)", 4, run<kMfmaFma3>(n_cu, it_short, 1, in, d_out, h_out)},
+      {"4 x (mfma 16x16x32 + 4 fma)", 4, run<kMfmaFma4>(n_cu, it_short, 1, in, d_out, h_out)},
+  };
+  printf("\n[issue] short launches (%d iterations per wave, two waves per SIMD)\n", it_short);
+  printf("%-30s %14s %14s %10s\n", "loop body", "cycles/iter", "cycles/instr", "clock GHz");
+  for (const Row& w : rows) {
+    const double per_iter = w.r.ms * 1e6 * w.r.clock_ghz / (2.0 * it_short);
+    printf("%-30s %14.2f %14.2f %10.2f\n", w.name, per_iter, per_iter / w.instr, w.r.clock_ghz);
+  }
+
+  // sustained: 20 launches of ~4.5 ms each
+  const int it_long = 65536, launches = 20;
+  const double flops = (double)it_long * 4 * (16.0 * 16 * 32 * 2) * n_cu * (kThreads / 64);
+  struct SRow { const char* name; Result r; };
+  SRow srows[] = {
+      {"mfma 16x16x32 bf16", run<kMfma16>(n_cu, it_long, launches, in, d_out, h_out)},
+      {"mfma 32x32x16 bf16", run<kMfma32>(n_cu, it_long, launches, in, d_out, h_out)},
+      {"mfma 16x16x32 + softmax VALU", run<kSoft16>(n_cu, it_long, launches, in, d_out, h_out)},
+      {"mfma 32x32x16 + softmax VALU", run<kSoft32>(n_cu, it_long, launches, in, d_out, h_out)},
+      {"mfma 16x16x32, zero operands", run<kMfma16Zero>(n_cu, it_long, launches, in, d_out, h_out)},
+  };
+  printf("\n[power] %d back-to-back launches, random bf16 operands (last row: zeros)\n", launches);
+  printf("%-30s %12s %14s %10s\n", "loop body", "TFLOP/s", "of 2500 TF/s", "clock GHz");
+  for (const SRow& w : srows) {
+    const double tf = flops / (w.r.ms * 1e-3) / 1e12;
+    printf("%-30s %12.0f %13.1f%% %10.2f\n", w.name, tf, 100.0 * tf / 2500.0, w.r.clock_ghz);
+  }
+  CHECK(hipFree(in));
+  CHECK(hipFree(d_out));
+  free(h_out);
+  return 0;
+}

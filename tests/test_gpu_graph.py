@@ -21,6 +21,10 @@ CASES = {
     # 8 KV heads with a prefill: prefix pass and prefill on the side stream
     "cascade_prefill_hkv8": dict(qlens=[1, 1, 1, 40], lens=[256 + 5, 256 + 300, 256 + 40, 256 + 90],
                                  shared_prefix_blocks=16, num_heads=32, num_kv_heads=8),
+    # 8 KV heads, decodes and prefills (g = 8): the 8-wave prefill on the side
+    # stream beside 8-wave decode workgroups
+    "mixed_hkv8_g8": dict(qlens=[1, 1, 1, 1, 70, 33], lens=[40, 700, 2100, 3000, 500, 33],
+                          num_heads=64, num_kv_heads=8),
 }
 
 

@@ -63,6 +63,34 @@ def test_small_batch_matches_oracle(name):
     assert_close(out, lse, ref_o, ref_l, name)
 
 
+# Decodes beside prefills with 4 and 8 KV heads over a bf16 pool, head size
+# 128: the 8-wave wide prefill on the side stream beside 8-wave (Hkv = 8) or
+# 4-wave (Hkv = 4) decode workgroups.  Ragged prompts, chunks with context,
+# non-causal rows, HND order and 64- and 128-token pages.
+WIDE_HKV = {
+    "hkv8_g4_bs16": ([1, 1, 1, 1, 1, 37, 130, 200], [1, 16, 17, 700, 2100, 337, 130, 264],
+                     dict(num_heads=32, num_kv_heads=8, block_size=16)),
+    "hkv4_g8_bs64": ([1, 1, 1, 64, 100, 1], [65, 640, 1500, 600, 100, 64],
+                     dict(num_heads=32, num_kv_heads=4, block_size=64)),
+    "hkv4_g2_noncausal": ([1, 40, 7, 1], [64, 100, 7, 999], dict(num_heads=8, num_kv_heads=4, block_size=16,
+                                                                  causal=False)),
+    "hkv8_g8_hnd_bs128": ([1, 1, 300, 1, 17], [4000, 129, 2300, 1, 17],
+                          dict(num_heads=64, num_kv_heads=8, block_size=128, kv_layout="HND")),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_HKV))
+def test_decodes_beside_wide_prefill_match_oracle(name):
+    qlens, lens, kw = WIDE_HKV[name]
+    batch = make_batch(qlens, lens, head_size=128, seed=61, **kw)
+    announce(f"wide hkv {name} B={batch.num_seqs} T={batch.num_tokens}")
+    out, lse, db = run_gpu(batch)
+    info = pa.pa_plan_get_info(db.plan)
+    assert info["num_decode_items"] > 0 and info["num_prefill_items"] > 0
+    ref_o, ref_l = oracle_full(batch)
+    assert_close(out, lse, ref_o, ref_l, f"wide hkv {name}")
+
+
 # Batches of decodes alone with the automatic split: balanced work lists that
 # cross sequence boundaries, under every decode launch shape (waves per
 # workgroup = the largest divisor of Hkv x ceil(g / 16) up to 8).
