@@ -17,6 +17,10 @@
 //          bare MFMA loop once more on all-zero operands, whose bits never
 //          toggle.
 //
+// With --json only the two 16x16x32 random-operand power rows run (about
+// 0.2 s), printed as one JSON object: the benchmark quotes them next to the
+// specification's peak.
+//
 // Every workgroup fills one CU (8 waves, two per SIMD; 96 KB of LDS keeps a
 // second workgroup off the CU), one workgroup per CU.  The instruction order
 // inside each loop is fixed with inline asm (compute instructions only: no
@@ -25,6 +29,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 namespace {
 
@@ -170,7 +175,8 @@ Result run(int n_cu, int iters, int launches, const float* in, unsigned long lon
 
 }  // namespace
 
-int main() {
+int main(int argc, char** argv) {
+  const bool json = argc > 1 && std::strcmp(argv[1], "--json") == 0;
   int dev = 0;
   CHECK(hipSetDevice(dev));
   hipDeviceProp_t prop;
@@ -184,6 +190,20 @@ int main() {
   CHECK(hipMalloc(&d_out, out_bytes));
   h_out = static_cast<unsigned long long*>(malloc(out_bytes));
   if (!h_out) return 1;
+  if (json) {
+    const int it_long = 65536, launches = 20;
+    const double flops = (double)it_long * 4 * (16.0 * 16 * 32 * 2) * n_cu * (kThreads / 64);
+    const Result bare = run<kMfma16>(n_cu, it_long, launches, in, d_out, h_out);
+    const Result soft = run<kSoft16>(n_cu, it_long, launches, in, d_out, h_out);
+    printf("{\"device\": \"%s\", \"mfma_bf16_TFLOPs\": %.1f, \"mfma_bf16_clock_GHz\": %.3f, "
+           "\"mfma_bf16_softmax_valu_TFLOPs\": %.1f, \"mfma_bf16_softmax_valu_clock_GHz\": %.3f}\n",
+           prop.gcnArchName, flops / (bare.ms * 1e-3) / 1e12, bare.clock_ghz, flops / (soft.ms * 1e-3) / 1e12,
+           soft.clock_ghz);
+    CHECK(hipFree(in));
+    CHECK(hipFree(d_out));
+    free(h_out);
+    return 0;
+  }
   printf("device %s, %d CUs, %d waves per CU (2 per SIMD)\n", prop.gcnArchName, n_cu, kThreads / 64);
 
   // issue rates: one short launch each; SIMD cycles per loop iteration of one

@@ -262,6 +262,23 @@ def copy_gbs(nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / best / 1e9
 
 
+def sustained_mfma() -> dict | None:
+    """The chip's sustained bf16 MFMA rate on random operands, bare and with
+    the softmax's per-score VALU work interleaved, and the clock it settles at
+    (attention_paged_kv_varlen_amd/chip_probe --json, run as a child process,
+    about 0.2 s of GPU time): the measured figure reported beside the spec
+    peak of MFMA-bound lines.  None when the probe is not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "attention_paged_kv_varlen_amd", "chip_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, "--json"], capture_output=True, text=True, timeout=60)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError, ValueError, IndexError):
+        return None
+
+
 def cpu_threads() -> int:
     """Host cores this process may run on."""
     try:
@@ -686,6 +703,11 @@ def main(argv=None) -> int:
     # a kernel trace holds only the step's own launches)
     if roof["bound"] == "hbm" and not args.no_secondary:
         roof["copy_kernel_GBps"] = round(copy_gbs(), 1)
+    if roof["bound"] == "mfma" and dtype == "bf16" and not args.no_secondary:
+        sm = sustained_mfma()
+        if sm:
+            roof["sustained_mfma"] = sm
+            roof["frac_of_sustained_softmax_mix"] = round(roof["achieved"] / sm["mfma_bf16_softmax_valu_TFLOPs"], 4)
     line["roofline"] = roof
     if counts["decode_seqs"] and counts["prefill_tokens"] and not args.no_secondary:
         line["sub_plans"] = measure_sub_plans(m, args.steps, args.warmup)
@@ -721,6 +743,11 @@ def main(argv=None) -> int:
                          "frac_at_median_launch": round(pf / (k["median_us"] * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                          "traffic": _traffic(kp, "prefill")},
         }
+        sm = sustained_mfma()
+        if sm:
+            rf = line["secondary"]["roofline"]
+            rf["sustained_mfma"] = sm
+            rf["frac_of_sustained_softmax_mix"] = round(rf["achieved"] / sm["mfma_bf16_softmax_valu_TFLOPs"], 4)
         del p
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(batch, counts, args.cpu_budget)
