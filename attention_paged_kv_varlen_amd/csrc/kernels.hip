@@ -1471,6 +1471,14 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, co
   const int64_t s = slots[t];
   if (s < 0 || s >= n_slots) return;
   const float sc = kv_scale_of(half ? vs : ks, n_scales, off / D);
+  // The quotient x / sc, correctly rounded to float32, without a division per
+  // element: with yr = RN(1 / sc) (one IEEE division), q0 = RN(x * yr) and
+  // the exact residual r = x - q0 * sc (one FMA), RN(q0 + r * yr) is the
+  // correctly rounded quotient for quotients in the normal range (Markstein's
+  // theorem for FMA-based division).  Below it every quotient encodes to an
+  // e4m3 zero of the input's sign either way.  r = 0 keeps q0 (so -0 stays
+  // -0), and infinite or NaN products stand (their residual is NaN).
+  const float yr = 1.0f / sc;
   const uint16_t* src = (half ? v : k) + (int64_t)t * row + off;
   const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
   const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
@@ -1488,7 +1496,10 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, co
     float q[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float x = y[4 * j + e] / sc;
+      const float v = y[4 * j + e];
+      const float q0 = v * yr;
+      const float r = __builtin_fmaf(-q0, sc, v);
+      const float x = (r != 0.f && __builtin_isfinite(q0)) ? __builtin_fmaf(r, yr, q0) : q0;
       q[e] = x != x ? x : fminf(fmaxf(x, -448.f), 448.f);
     }
     uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);

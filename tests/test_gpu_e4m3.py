@@ -168,6 +168,48 @@ def test_write_is_bit_exact(num_scales):
                           f"{got[tuple(bad[0])]:#x} vs {want[tuple(bad[0])]:#x}"
 
 
+def _near_ties(rng, n, scale):
+    """bf16 patterns whose float32 quotient by `scale` lies within a few ulps of
+    a midpoint between two e4m3 values (where the code depends on the last bit
+    of the quotient), of either sign, plus values far past the saturation
+    point and below the smallest e4m3 step."""
+    vals = np.sort(oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = (vals[:-1] + vals[1:]) / 2
+    base = f32_to_bf16_bits((mids * np.float64(scale)).astype(np.float32)).astype(np.int64)
+    cand = np.concatenate([base + k for k in (-2, -1, 0, 1, 2)])
+    cand = np.concatenate([cand, cand | 0x8000, f32_to_bf16_bits(np.array([1e30, -1e30, 3e-38, -3e-38, 1e-40],
+                                                                              dtype=np.float32)).astype(np.int64)])
+    return rng.choice(cand, size=n).astype(np.uint16)
+
+
+@pytest.mark.parametrize("scales", [(0.37, 3.1), (1.0 / 3.0, 7.77), (0.1, 1.7e-3)])
+def test_write_near_ties_is_bit_exact(scales):
+    """The quotient by the scale decides the code near e4m3 midpoints: every
+    code matches the oracle's float32 division."""
+    import torch
+    Hkv, d, bs, nb, T = 2, 128, 16, 8, 64
+    rng = np.random.default_rng(50)
+    ks = np.array(scales, dtype=np.float32)
+    vs = np.array(scales[::-1], dtype=np.float32)
+    kb = np.stack([_near_ties(rng, T * d, ks[h]).reshape(T, d) for h in range(Hkv)], axis=1)
+    vb = np.stack([_near_ties(rng, T * d, vs[h]).reshape(T, d) for h in range(Hkv)], axis=1)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    pool0 = np.zeros((nb, 2, bs, Hkv, d), dtype=np.uint8)
+    announce(f"e4m3 write near ties scales={scales}")
+    params = pa.make_params(num_seqs=1, num_heads=Hkv, num_kv_heads=Hkv, head_size=d, block_size=bs,
+                            num_blocks=nb, max_blocks_per_seq=nb, dtype="bf16", scale=0.1, kv_dtype="fp8_e4m3")
+    pool = torch.from_numpy(pool0.copy()).cuda()
+    pa.pa_write_kv_fp8(torch.from_numpy(kb).view(torch.bfloat16).cuda(), torch.from_numpy(vb).view(torch.bfloat16).cuda(),
+                       torch.from_numpy(slots).cuda(), T, params, torch.from_numpy(ks).cuda(),
+                       torch.from_numpy(vs).cuda(), pool)
+    torch.cuda.synchronize()
+    want = oracle.write_kv_fp8(pool0, oracle.to_f64(kb, "bf16"), oracle.to_f64(vb, "bf16"), slots, ks, vs)
+    got = pool.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}: " \
+                          f"{got[tuple(bad[0])]:#x} vs {want[tuple(bad[0])]:#x}"
+
+
 def test_write_then_attention_matches_oracle():
     import torch
     b = SMALL["mixed_d128_g4_bs16"]()
