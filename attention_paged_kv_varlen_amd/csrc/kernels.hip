@@ -1475,10 +1475,12 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, co
   // element: with yr = RN(1 / sc) (one IEEE division), q0 = RN(x * yr) and
   // the exact residual r = x - q0 * sc (one FMA), RN(q0 + r * yr) is the
   // correctly rounded quotient for quotients in the normal range (Markstein's
-  // theorem for FMA-based division).  Below it every quotient encodes to an
-  // e4m3 zero of the input's sign either way.  r = 0 keeps q0 (so -0 stays
-  // -0), and infinite or NaN products stand (their residual is NaN).
+  // theorem for FMA-based division; it needs sc and yr normal: other scales
+  // take the division).  Below that range every quotient encodes to an e4m3
+  // zero of the input's sign either way.  r = 0 keeps q0 (so -0 stays -0),
+  // and infinite or NaN products stand (their residual is NaN).
   const float yr = 1.0f / sc;
+  const bool fma_div = __builtin_isnormal(sc) && __builtin_isnormal(yr);
   const uint16_t* src = (half ? v : k) + (int64_t)t * row + off;
   const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
   const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
@@ -1491,24 +1493,37 @@ __global__ void __launch_bounds__(256) write_kv_fp8_kernel(const uint16_t* k, co
     y[8 + 2 * j + 1] = __uint_as_float(w1[j] & 0xFFFF0000u);
   }
   u32x4 out;
+  auto encode = [&](auto fma_c) {
+    constexpr bool FMA_DIV = decltype(fma_c)::value;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float q[4];
+    for (int j = 0; j < 4; ++j) {
+      float q[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = y[4 * j + e];
-      const float q0 = v * yr;
-      const float r = __builtin_fmaf(-q0, sc, v);
-      const float x = (r != 0.f && __builtin_isfinite(q0)) ? __builtin_fmaf(r, yr, q0) : q0;
-      q[e] = x != x ? x : fminf(fmaxf(x, -448.f), 448.f);
+      for (int e = 0; e < 4; ++e) {
+        const float v = y[4 * j + e];
+        float x;
+        if constexpr (FMA_DIV) {
+          const float q0 = v * yr;
+          const float r = __builtin_fmaf(-q0, sc, v);
+          x = (r != 0.f && __builtin_isfinite(q0)) ? __builtin_fmaf(r, yr, q0) : q0;
+        } else {
+          x = v / sc;
+        }
+        q[e] = x != x ? x : fminf(fmaxf(x, -448.f), 448.f);
+      }
+      uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)pk, true);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q[e] != q[e]) pk = (pk & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+      out[j] = pk;
     }
-    uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-    pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], (int)pk, true);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (q[e] != q[e]) pk = (pk & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
-    out[j] = pk;
-  }
+  };
+  // (a wave-uniform choice: normal scales take the FMA form in every lane)
+  if (__all(fma_div))
+    encode(std::true_type{});
+  else
+    encode(std::false_type{});
   const int64_t blk = s / bs, in = s % bs;
   unsigned char* dst = kv + (blk * 2 + half) * bs * (int64_t)row + (off / D) * head_stride + in * slot_stride + off % D;
   *reinterpret_cast<u32x4*>(dst) = out;

@@ -182,10 +182,11 @@ def _near_ties(rng, n, scale):
     return rng.choice(cand, size=n).astype(np.uint16)
 
 
-@pytest.mark.parametrize("scales", [(0.37, 3.1), (1.0 / 3.0, 7.77), (0.1, 1.7e-3)])
+@pytest.mark.parametrize("scales", [(0.37, 3.1), (1.0 / 3.0, 7.77), (0.1, 1.7e-3), (1e-40, 2.0e38)])
 def test_write_near_ties_is_bit_exact(scales):
     """The quotient by the scale decides the code near e4m3 midpoints: every
-    code matches the oracle's float32 division."""
+    code matches the oracle's float32 division (also for a subnormal scale
+    and one whose reciprocal is subnormal)."""
     import torch
     Hkv, d, bs, nb, T = 2, 128, 16, 8, 64
     rng = np.random.default_rng(50)
