@@ -240,6 +240,24 @@ __device__ __forceinline__ int page_index(const KArgs& a, int n) {
   return a.bs_log2 >= 0 ? (int)((unsigned)n >> a.bs_log2) : (int)((unsigned)n / (unsigned)a.bs);
 }
 
+// Read-only plan data (block-table entries, work items, list bounds) read
+// through the constant address space: at a wave-uniform index this is a
+// scalar load, counted apart from the vector loads.  A vector load of a page
+// id would make the wait for it also wait for every K/V load issued before it
+// (vector loads complete in order), so the next step's K/V loads could not be
+// issued while the previous step's are still in flight.
+template <typename X>
+__device__ __forceinline__ X ld_plan(const X* p, int64_t i) {
+  static_assert(sizeof(X) % 4 == 0, "plan records are whole 32-bit words");
+  struct Words {
+    int32_t w[sizeof(X) / 4];
+  } r;
+  const __attribute__((address_space(4))) int32_t* c = (const __attribute__((address_space(4))) int32_t*)(p + i);
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(X) / 4); ++k) r.w[k] = c[k];
+  return __builtin_bit_cast(X, r);
+}
+
 // Scale of KV head kvh from a per-tensor (n = 1) or per-head scale array.
 __device__ __forceinline__ float kv_scale_of(const float* sc, int n, int kvh) { return sc[n > 1 ? kvh : 0]; }
 
@@ -436,9 +454,9 @@ __device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
   const int hgrp = hgi % a.head_groups;
   const float sl2 = F8 ? a.scale_log2 * kv_scale_of(a.k_scale, a.n_scales, kvh) : a.scale_log2;
   const float omul = F8 ? kv_scale_of(a.v_scale, a.n_scales, kvh) : 1.f;
-  const int item_end = a.lists[list + 1];
-  for (int idx = a.lists[list]; idx < item_end; ++idx) {
-    const WorkItem it = a.items[idx];
+  const int item_end = ld_plan(a.lists, list + 1);
+  for (int idx = ld_plan(a.lists, list); idx < item_end; ++idx) {
+    const WorkItem it = ld_plan(a.items, idx);
     const int r = lane & 15, qd = lane >> 4;
 
     const T* q = static_cast<const T*>(a.q);
@@ -531,30 +549,36 @@ __device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
       });
     };
     const int kb0 = it.kv_begin;
-    int pid[2] = {btrow[tile_block(kb0)], btrow[tile_block(kb0 + 16)]};
+    int pid[2] = {ld_plan(btrow, tile_block(kb0)), ld_plan(btrow, tile_block(kb0 + 16))};
     if constexpr (DB) {
       static_assert(sizeof(T) == 2, "two steps in flight are built for bf16 queries");
+      // Each loop pass issues the next step's loads with no branch around
+      // them (block ids are clamped, so the lookups are always valid) and
+      // leaves by its own path when the item ends, so on the path that
+      // computes a step the loads of the step after it are still counted as
+      // outstanding: no control-flow join makes the wait for one step's
+      // data also wait for the next step's.
       Raw wa, wb;
-      int pidb[2] = {0, 0};
+      int pidb[2];
       load_step(kb0, pid, wa);
-      if (kb0 + 32 < kv_end) {
-        pidb[0] = btrow[tile_block(kb0 + 32)];
-        pidb[1] = btrow[tile_block(kb0 + 48)];
-      }
-      for (int t0 = kb0; t0 < kv_end; t0 += 64) {
-        const bool has_b = t0 + 32 < kv_end;
-        if (has_b) load_step(t0 + 32, pidb, wb);
-        if (t0 + 64 < kv_end) {
-          pid[0] = btrow[tile_block(t0 + 64)];
-          pid[1] = btrow[tile_block(t0 + 80)];
+      pidb[0] = ld_plan(btrow, tile_block(kb0 + 32));
+      pidb[1] = ld_plan(btrow, tile_block(kb0 + 48));
+      for (int t0 = kb0;; t0 += 64) {
+        if (t0 + 32 >= kv_end) {
+          compute_step(t0, wa);
+          break;
         }
+        load_step(t0 + 32, pidb, wb);
+        pid[0] = ld_plan(btrow, tile_block(t0 + 64));
+        pid[1] = ld_plan(btrow, tile_block(t0 + 80));
         compute_step(t0, wa);
-        if (!has_b) break;
-        if (t0 + 64 < kv_end) load_step(t0 + 64, pid, wa);
-        if (t0 + 96 < kv_end) {
-          pidb[0] = btrow[tile_block(t0 + 96)];
-          pidb[1] = btrow[tile_block(t0 + 112)];
+        if (t0 + 64 >= kv_end) {
+          compute_step(t0 + 32, wb);
+          break;
         }
+        load_step(t0 + 64, pid, wa);
+        pidb[0] = ld_plan(btrow, tile_block(t0 + 96));
+        pidb[1] = ld_plan(btrow, tile_block(t0 + 112));
         compute_step(t0 + 32, wb);
       }
     } else {
@@ -562,8 +586,8 @@ __device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
         Raw w;
         load_step(t0, pid, w);
         if (t0 + 32 < kv_end) {
-          pid[0] = btrow[tile_block(t0 + 32)];
-          pid[1] = btrow[tile_block(t0 + 48)];
+          pid[0] = ld_plan(btrow, tile_block(t0 + 32));
+          pid[1] = ld_plan(btrow, tile_block(t0 + 48));
         }
         compute_step(t0, w);
       }
