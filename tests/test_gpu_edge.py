@@ -83,3 +83,22 @@ def test_wide_groups(heads):
     out, lse, _ = run_gpu(b)
     ref_o, ref_l = oracle_full(b)
     assert_close(out, lse, ref_o, ref_l, f"groups {heads}")
+
+
+@pytest.mark.parametrize("kv_dtype,split", [("same", 0), ("same", 32), ("same", 64), ("same", 96),
+                                            ("fp8_e4m3", 0), ("fp8_e4m3", 32)])
+def test_every_short_decode_length(kv_dtype, split):
+    # decodes of every length from 1 to 160 keys: work items that end after
+    # one 32-key step, after an even or an odd number of steps, at every
+    # offset inside a 16-key page; automatic lists (items cut on 32-key
+    # boundaries, several sequences per list) and explicit splits
+    lens = list(range(1, 161))
+    b = make_batch([1] * len(lens), lens, num_heads=32, num_kv_heads=8, head_size=128, block_size=16, seed=76,
+                   kv_dtype=kv_dtype)
+    announce(f"every short decode length {kv_dtype} split={split}")
+    out, lse, db = run_gpu(b, kv_split_tokens=split)
+    info = pa.pa_plan_get_info(db.plan)
+    if split == 0:
+        assert info["decode_list_tokens"] > 0
+    ref_o, ref_l = oracle_full(b)
+    assert_close(out, lse, ref_o, ref_l, f"short lengths {kv_dtype} split={split}")
