@@ -898,7 +898,7 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
   // the head group (see launch_prefill)
   const int nhg = a.Hkv * a.head_groups;
   const int hgi = (int)((unsigned)wg % (unsigned)nhg);
-  const WorkItem it = a.items[(unsigned)wg / (unsigned)nhg];
+  const WorkItem it = ld_plan(a.items, (unsigned)wg / (unsigned)nhg);
   const int kvh = hgi % a.Hkv;
   const int hgrp = hgi / a.Hkv;
   const int r = lane & 15, qd = lane >> 4;
@@ -950,7 +950,7 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
   // physical block of this wave's slab of the block at key kb (its first key,
   // clamped); looked up one block ahead so the lookup's latency is covered by
   // the wait before the next barrier
-  auto page_of = [&](int kb) { return btrow[page_index(a, min(kb + RPW * wave, kv_hi - 1))]; };
+  auto page_of = [&](int kb) { return ld_plan(btrow, page_index(a, min(kb + RPW * wave, kv_hi - 1))); };
   // e4m3: this wave's slab of the next block's K codes, or of its V codes
   // (part 0 / 1; staged one after the other, so that only one is held in
   // registers at a time), 16 codes per lane and load (row 8 i + lane / 8 of
