@@ -17,9 +17,19 @@
 //          bare MFMA loop once more on all-zero operands, whose bits never
 //          toggle.
 //
+//   read   a streaming read of a 4 GiB buffer with 16-byte loads, each
+//          workgroup over a contiguous range (plain and non-temporal loads,
+//          8 or 16 in flight per lane, workgroups of 512 or 256 lanes, 1 to 4
+//          per CU): the HBM read rate the chip delivers to a simple stream,
+//          the measured ceiling of the decode, which reads each KV byte once;
+//          and the decode's own access pattern (page rows split among the
+//          waves of a workgroup, K tiles in the MFMA operand layout) with its
+//          arithmetic left out.
+//
 // With --json only the two 16x16x32 random-operand power rows run (about
-// 0.2 s), printed as one JSON object: the benchmark quotes them next to the
-// specification's peak.
+// 0.2 s), printed as one JSON object; with --read-json only the streaming
+// read (about 0.1 s): the benchmark quotes them next to the specification's
+// peaks.
 //
 // Every workgroup fills one CU (8 waves, two per SIMD; 96 KB of LDS keeps a
 // second workgroup off the CU), one workgroup per CU.  The instruction order
@@ -149,6 +159,149 @@ struct Result {
   double clock_ghz;  // shader cycles over real time (100 MHz counter), averaged over workgroups, last launch
 };
 
+// Streaming read: workgroup b reads its own contiguous range of 16-byte
+// words, U * blockDim words per step (lane t takes words t + j * blockDim of
+// the step, U loads in flight), and folds them with xor; the fold is written
+// only if it equals a value the buffer's fill cannot give, so the loads stay
+// and nothing is written.  words_per_wg is a multiple of U * blockDim.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT, int U>
+__global__ void __launch_bounds__(512) read_kernel(const u32x4* src, size_t words_per_wg, unsigned* sink) {
+  const u32x4* p = src + (size_t)blockIdx.x * words_per_wg + threadIdx.x;
+  const size_t step = (size_t)U * blockDim.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t base = 0; base < words_per_wg; base += step) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4* q = p + base + (size_t)u * blockDim.x;
+      v[u] = NT ? __builtin_nontemporal_load(q) : *q;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) sink[0] = 1u;
+}
+
+struct ReadRow {
+  const char* loads;
+  int threads, wgs_per_cu, in_flight;
+  double gbps;
+};
+
+// GB/s of one read configuration over the n-word buffer (10 launches)
+template <bool NT, int U>
+double time_read(const u32x4* buf, size_t n, unsigned* sink, int n_cu, int threads, int wgs_per_cu) {
+  const int wgs = n_cu * wgs_per_cu;
+  const size_t step = (size_t)U * threads;
+  const size_t words_per_wg = n / wgs / step * step;
+  auto k = read_kernel<NT, U>;
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const int launches = 10;
+  hipLaunchKernelGGL(k, dim3(wgs), dim3(threads), 0, 0, buf, words_per_wg, sink);  // warm-up
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e0));
+  for (int r = 0; r < launches; ++r) hipLaunchKernelGGL(k, dim3(wgs), dim3(threads), 0, 0, buf, words_per_wg, sink);
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return (double)words_per_wg * wgs * 16.0 * launches / (ms * 1e-3) / 1e9;
+}
+
+// The decode's access pattern without its arithmetic: a pool of 64 KB pages
+// (K half: 16 rows of 2 KB, V half likewise), read page after page by 8-wave
+// workgroups, wave w taking the 256-byte slice w of every row (one KV head),
+// two pages (32 keys, 16 loads per lane) per step.  K tiles: load j of lane
+// (r, qd) reads row r, bytes 64 j + 16 qd .. +15 (16 rows x 64 B per
+// instruction, the MFMA operand layout); V tiles: row 4 qd + j, bytes 16 r ..
+// +15 (4 whole 256-byte rows per instruction).  KPAT_V: the K half read with
+// the K pattern as well (half a 128-byte line per row and instruction).
+template <bool KPAT_V>
+__global__ void __launch_bounds__(512) page_read_kernel(const unsigned char* pool, int pages_per_wg, unsigned* sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, qd = lane >> 4;
+  const unsigned char* base = pool + (size_t)blockIdx.x * pages_per_wg * 65536 + 256 * wave;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int pg = 0; pg + 1 < pages_per_wg; pg += 2) {
+    u32x4 v[16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned char* half = base + (size_t)(pg + t) * 65536 + h * 32768;
+        const bool kpat = h == 0 || KPAT_V;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned char* q = kpat ? half + r * 2048 + 64 * j + 16 * qd : half + (4 * qd + j) * 2048 + 16 * r;
+          v[8 * t + 4 * h + j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc ^= v[i];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9E3779B9u) sink[0] = 1u;
+}
+
+// GB/s of the page pattern over the 4 GiB buffer (one 8-wave workgroup per
+// CU, 10 launches)
+template <bool KPAT_V>
+double time_pages(const unsigned char* pool, size_t bytes, unsigned* sink, int n_cu) {
+  const int pages_per_wg = (int)(bytes / 65536 / n_cu) & ~1;
+  auto k = page_read_kernel<KPAT_V>;
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  const int launches = 10;
+  hipLaunchKernelGGL(k, dim3(n_cu), dim3(512), 0, 0, pool, pages_per_wg, sink);  // warm-up
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e0));
+  for (int i = 0; i < launches; ++i) hipLaunchKernelGGL(k, dim3(n_cu), dim3(512), 0, 0, pool, pages_per_wg, sink);
+  CHECK(hipGetLastError());
+  CHECK(hipEventRecord(e1));
+  CHECK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return (double)n_cu * pages_per_wg * 65536.0 * launches / (ms * 1e-3) / 1e9;
+}
+
+constexpr int kReadRows = 16;
+
+// The read rows over a 4 GiB buffer filled with a nonzero pattern: plain and
+// non-temporal loads; 8 or 16 loads in flight per lane; workgroups of 512
+// lanes (1 or 2 per CU) or 256 lanes (2 or 4 per CU).
+int read_rows(int n_cu, ReadRow (&rows)[kReadRows], double (&pages)[2]) {
+  const size_t bytes = (size_t)4 << 30, n = bytes / 16;
+  u32x4* buf = nullptr;
+  unsigned* sink = nullptr;
+  if (hipMalloc(&buf, bytes) != hipSuccess) return 1;
+  CHECK(hipMalloc(&sink, sizeof(unsigned)));
+  CHECK(hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(buf), 0x3C5A7E91, bytes / 4));
+  CHECK(hipDeviceSynchronize());
+  const int shape[4][2] = {{512, 1}, {512, 2}, {256, 2}, {256, 4}};
+  int r = 0;
+  for (const auto& sh : shape) {
+    rows[r++] = ReadRow{"plain", sh[0], sh[1], 8, time_read<false, 8>(buf, n, sink, n_cu, sh[0], sh[1])};
+    rows[r++] = ReadRow{"non-temporal", sh[0], sh[1], 8, time_read<true, 8>(buf, n, sink, n_cu, sh[0], sh[1])};
+    rows[r++] = ReadRow{"plain", sh[0], sh[1], 16, time_read<false, 16>(buf, n, sink, n_cu, sh[0], sh[1])};
+    rows[r++] = ReadRow{"non-temporal", sh[0], sh[1], 16, time_read<true, 16>(buf, n, sink, n_cu, sh[0], sh[1])};
+  }
+  const unsigned char* pool = reinterpret_cast<const unsigned char*>(buf);
+  pages[0] = time_pages<false>(pool, bytes, sink, n_cu);
+  pages[1] = time_pages<true>(pool, bytes, sink, n_cu);
+  CHECK(hipFree(buf));
+  CHECK(hipFree(sink));
+  return 0;
+}
+
 template <int B>
 Result run(int n_cu, int iters, int launches, const float* in, unsigned long long* d_out, unsigned long long* h_out) {
   auto k = probe_kernel<B>;
@@ -177,6 +330,7 @@ Result run(int n_cu, int iters, int launches, const float* in, unsigned long lon
 
 int main(int argc, char** argv) {
   const bool json = argc > 1 && std::strcmp(argv[1], "--json") == 0;
+  const bool read_json = argc > 1 && std::strcmp(argv[1], "--read-json") == 0;
   int dev = 0;
   CHECK(hipSetDevice(dev));
   hipDeviceProp_t prop;
@@ -190,6 +344,23 @@ int main(int argc, char** argv) {
   CHECK(hipMalloc(&d_out, out_bytes));
   h_out = static_cast<unsigned long long*>(malloc(out_bytes));
   if (!h_out) return 1;
+  if (read_json) {
+    ReadRow rr[kReadRows];
+    double pg[2];
+    if (read_rows(n_cu, rr, pg)) return 1;
+    int best = 0;
+    for (int j = 1; j < kReadRows; ++j)
+      if (rr[j].gbps > rr[best].gbps) best = j;
+    printf("{\"device\": \"%s\", \"hbm_read_GBps\": %.1f, \"hbm_read_loads\": \"%s\", "
+           "\"hbm_read_threads\": %d, \"hbm_read_wgs_per_cu\": %d, \"hbm_read_in_flight\": %d, "
+           "\"decode_pattern_GBps\": %.1f, \"buffer_GiB\": 4}\n",
+           prop.gcnArchName, rr[best].gbps, rr[best].loads, rr[best].threads, rr[best].wgs_per_cu,
+           rr[best].in_flight, pg[0]);
+    CHECK(hipFree(in));
+    CHECK(hipFree(d_out));
+    free(h_out);
+    return 0;
+  }
   if (json) {
     const int it_long = 65536, launches = 20;
     const double flops = (double)it_long * 4 * (16.0 * 16 * 32 * 2) * n_cu * (kThreads / 64);
@@ -244,6 +415,19 @@ int main(int argc, char** argv) {
     const double tf = flops / (w.r.ms * 1e-3) / 1e12;
     printf("%-30s %12.0f %13.1f%% %10.2f\n", w.name, tf, 100.0 * tf / 2500.0, w.r.clock_ghz);
   }
+
+  ReadRow rr[kReadRows];
+  double pg[2];
+  if (read_rows(n_cu, rr, pg)) return 1;
+  printf("\n[read] streaming read of 4 GiB, 16-byte loads, one contiguous range per workgroup, 10 launches\n");
+  printf("%-14s %8s %11s %10s %10s %14s\n", "loads", "lanes", "WGs per CU", "in flight", "GB/s", "of 8000 GB/s");
+  for (const ReadRow& w : rr)
+    printf("%-14s %8d %11d %10d %10.0f %13.1f%%\n", w.loads, w.threads, w.wgs_per_cu, w.in_flight, w.gbps,
+           w.gbps / 80.0);
+  printf("\n[read] the decode's access pattern without its arithmetic (64 KB pages, 8 waves per CU, non-temporal)\n");
+  printf("%-46s %10s %14s\n", "pattern", "GB/s", "of 8000 GB/s");
+  printf("%-46s %10.0f %13.1f%%\n", "K tiles 16 rows x 64 B, V tiles 4 rows x 256 B", pg[0], pg[0] / 80.0);
+  printf("%-46s %10.0f %13.1f%%\n", "both halves 16 rows x 64 B", pg[1], pg[1] / 80.0);
   CHECK(hipFree(in));
   CHECK(hipFree(d_out));
   free(h_out);

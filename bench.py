@@ -279,6 +279,24 @@ def sustained_mfma() -> dict | None:
         return None
 
 
+def hbm_read_probe() -> dict | None:
+    """The chip's streaming HBM read rate: a 4 GiB buffer read once per launch
+    with 16-byte loads, best of plain / non-temporal loads and 2 / 4 / 8
+    workgroups per CU (attention_paged_kv_varlen_amd/chip_probe --read-json,
+    run as a child process, about 0.1 s of GPU time): the measured ceiling
+    reported beside the spec peak of HBM-bound lines.  None when the probe is
+    not built or fails."""
+    import subprocess
+    exe = os.path.join(ROOT, "attention_paged_kv_varlen_amd", "chip_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe, "--read-json"], capture_output=True, text=True, timeout=60)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError, ValueError, IndexError):
+        return None
+
+
 def cpu_threads() -> int:
     """Host cores this process may run on."""
     try:
@@ -703,6 +721,10 @@ def main(argv=None) -> int:
     # a kernel trace holds only the step's own launches)
     if roof["bound"] == "hbm" and not args.no_secondary:
         roof["copy_kernel_GBps"] = round(copy_gbs(), 1)
+        rp = hbm_read_probe()
+        if rp:
+            roof["hbm_read_probe"] = rp
+            roof["frac_of_measured_read"] = round(roof["achieved"] / rp["hbm_read_GBps"], 4)
     if roof["bound"] == "mfma" and dtype == "bf16" and not args.no_secondary:
         sm = sustained_mfma()
         if sm:
