@@ -878,7 +878,7 @@ __device__ __forceinline__ void write_column_dmajor(const KArgs& a, int row, int
 // end, after the block's own reads of the other stage; everything that reads
 // LDS is unchanged.  The K scale joins the softmax scale, the V scale
 // multiplies the output.
-template <bool F8, int NW>
+template <bool F8, int NW, bool NT_KV = false>
 __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char* lds0, unsigned char* lds1) {
   using KV = std::conditional_t<F8, uint8_t, uint16_t>;
   static_assert(NW == 4 || (NW == 8 && !F8), "4 waves, or 8 waves over a bf16 pool");
@@ -939,6 +939,10 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
   const int64_t v_half = (int64_t)a.bs * a.Hkv * D;
   const int32_t* btrow = a.bt + (int64_t)it.seq * a.max_blocks;
   const KV* kvh_base = kv + (int64_t)kvh * a.head_stride;
+  // cache policy of the direct-to-LDS loads: with NT_KV the non-temporal bit
+  // (the shared-prefix units beside the decode, whose prefix blocks are each
+  // read by one or two workgroups of one XCD)
+  constexpr int kDmaAux = NT_KV ? 2 : 0;
   // per-lane byte offset of its 16-byte chunk inside the wave's slab of RPW
   // rows (rows 4i + lane/16, XOR-swizzled chunk): constant across blocks
   uint32_t loff[RPW / 4];
@@ -980,10 +984,10 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
 #pragma unroll
       for (int i = 0; i < RPW / 4; ++i) {
         __builtin_amdgcn_global_load_lds((const void*)(base + loff[i]),
-                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
+                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, kDmaAux);
         __builtin_amdgcn_global_load_lds((const void*)(base + 2 * v_half + loff[i]),
                                          (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
-                                         16, 0, 0);
+                                         16, 0, kDmaAux);
       }
     } else {
       // tail: rows past the end re-read the last valid key (masked later)
@@ -997,10 +1001,10 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
         const int key = min(kb + row, kv_hi - 1);
         const KV* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row));
         __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, 0);
+                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, kDmaAux);
         __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
                                          (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
-                                         16, 0, 0);
+                                         16, 0, kDmaAux);
       }
     }
   };
@@ -1274,7 +1278,7 @@ prefix_decode_kernel(KArgs pre, KArgs dec, int n_pre) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[2 * kWideBlk];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[2 * kWideBlk];
   if ((int)blockIdx.x < n_pre)
-    wide_body<false, 8>(pre, (int)blockIdx.x, lds0, lds1);
+    wide_body<false, 8, true>(pre, (int)blockIdx.x, lds0, lds1);
   else
     decode_body<uint16_t, uint16_t, 128, true, false>(dec, (int)blockIdx.x - n_pre, 8);
 }
