@@ -240,6 +240,10 @@ __device__ __forceinline__ int page_index(const KArgs& a, int n) {
   return a.bs_log2 >= 0 ? (int)((unsigned)n >> a.bs_log2) : (int)((unsigned)n / (unsigned)a.bs);
 }
 
+// Word 3 of a raw (untyped) buffer descriptor on gfx9-family chips: a 32-bit
+// data format, so that dword loads are in range; no swizzle, no index stride.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Read-only plan data (block-table entries, work items, list bounds) read
 // through the constant address space: at a wave-uniform index this is a
 // scalar load, counted apart from the vector loads.  A vector load of a page
@@ -976,35 +980,42 @@ __device__ __forceinline__ void wide_body(const KArgs& a, int wg, unsigned char*
       return;
     }
     lds_u8* dst = (lds_u8*)(stage ? lds1 : lds0) + RPW * wave * kWideRow;
+    // Direct-to-LDS loads in their buffer form: one descriptor per slab, based
+    // at the slab's page (wave-uniform), the lanes' byte offsets 32-bit (a
+    // page holds 2 bs Hkv d elements).  With the global form in flight the
+    // compiler treats the LDS counter as out of order and waits for every
+    // outstanding LDS read before each group of MFMAs; with the buffer form
+    // it waits only for the reads a group consumes.
+    auto dma = [&](const unsigned char* base, uint32_t off, lds_u8* to) {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, kRawBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)to, 16, (int)off, 0, 0,
+                                               kDmaAux);
+    };
+    const uint32_t v_off = (uint32_t)(2 * v_half);  // bytes from a page's K half to its V half
     if (key0 + RPW - 1 < kv_hi) {
-      // whole slab valid and inside one physical block: scalar base + lane offset
+      // whole slab valid and inside one physical block: slab base + lane offset
       const int blk = page_index(a, key0);
       const unsigned char* base = reinterpret_cast<const unsigned char*>(
           kvh_base + (int64_t)pid * blk_stride + (int64_t)(key0 - blk * a.bs) * slot_stride);
 #pragma unroll
       for (int i = 0; i < RPW / 4; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(base + loff[i]),
-                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, kDmaAux);
-        __builtin_amdgcn_global_load_lds((const void*)(base + 2 * v_half + loff[i]),
-                                         (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
-                                         16, 0, kDmaAux);
+        dma(base, loff[i], dst + 4 * i * kWideRow);
+        dma(base, v_off + loff[i], dst + kWideBlk + 4 * i * kWideRow);
       }
     } else {
       // tail: rows past the end re-read the last valid key (masked later)
       const int ks = min(key0, kv_hi - 1);
       const int blk = page_index(a, ks);
       const int pst = blk * a.bs;
-      const KV* page = kvh_base + (int64_t)pid * blk_stride;
+      const unsigned char* page = reinterpret_cast<const unsigned char*>(kvh_base + (int64_t)pid * blk_stride);
 #pragma unroll
       for (int i = 0; i < RPW / 4; ++i) {
         const int row = RPW * wave + 4 * i + (lane >> 4);
         const int key = min(kb + row, kv_hi - 1);
-        const KV* src = page + (int64_t)(key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row));
-        __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (void __attribute__((address_space(3)))*)(dst + 4 * i * kWideRow), 16, 0, kDmaAux);
-        __builtin_amdgcn_global_load_lds((const void*)(src + v_half),
-                                         (void __attribute__((address_space(3)))*)(dst + kWideBlk + 4 * i * kWideRow),
-                                         16, 0, kDmaAux);
+        const uint32_t off = (uint32_t)(((key - pst) * slot_stride + 8 * ((lane & 15) ^ wide_swizzle(row))) * 2);
+        dma(page, off, dst + 4 * i * kWideRow);
+        dma(page, v_off + off, dst + kWideBlk + 4 * i * kWideRow);
       }
     }
   };
