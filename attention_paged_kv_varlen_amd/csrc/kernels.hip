@@ -792,9 +792,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 
 // ---------------------------------------------------------------------------
 // Wide prefill for bf16 with head size 128 (the fast path): a workgroup owns
-// 8 column tiles; 64-key K/V blocks are double-buffered in LDS and filled with
-// global_load_lds_dwordx4, which writes lane l's 16 bytes at LDS base + 16 l
-// (no register staging, no LDS store instructions).  A 256-byte key row is 16
+// 8 column tiles; 64-key K/V blocks are double-buffered in LDS and filled by
+// direct-to-LDS loads (buffer_load_dwordx4 ... lds), which write lane l's 16
+// bytes at LDS base + 16 l (no register staging, no LDS store instructions).  A 256-byte key row is 16
 // chunks of 16 bytes, stored XOR-swizzled (wide_swizzle) so that neither the
 // K operand reads nor the V^T transposing reads conflict on LDS banks.
 // Cross-lane reductions over the four 16-lane groups use permlane swaps (VALU)
