@@ -265,14 +265,34 @@ __device__ __forceinline__ X ld_plan(const X* p, int64_t i) {
 // Scale of KV head kvh from a per-tensor (n = 1) or per-head scale array.
 __device__ __forceinline__ float kv_scale_of(const float* sc, int n, int kvh) { return sc[n > 1 ? kvh : 0]; }
 
+// Reductions over the four 16-lane groups of a wave (lanes r, r + 16, r + 32,
+// r + 48 hold one column) by permlane swaps: VALU instructions, where a
+// shuffle would go through the LDS crossbar and wait for it.
+__device__ __forceinline__ float xlane_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,1) and (2,3) exchanged
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves exchanged
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float xlane_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Online-softmax update of one 16-column tile with the 8 scores (log2 units,
 // masked = -inf) a lane holds for its column.  Returns P in `p`.
 template <int VE>
 __device__ __forceinline__ void softmax_step(float (&x)[8], float& m_run, float& l_run, f32x4 (&o)[VE],
                                              float (&p)[8]) {
   float mb = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  mb = xlane_max(mb);
   const bool need = mb > m_run + kRescaleThreshold;
   if (__any(need)) {
     const float m_new = need ? mb : m_run;
@@ -597,8 +617,7 @@ __device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
       }
     }
 
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = xlane_sum(l_run);
     if (colv) write_column<T, VE>(a, it.row0, head, it.slot, qd, o, m_run, l_run, omul);
   }
 }
@@ -783,8 +802,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(KArgs a) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float l = l_run[c];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = xlane_sum(l);
     const int pos = pos0[c] + r;
     if (pos < it.nrows) write_column<T, VE>(a, it.row0 + pos, head[c], it.slot, qd, o[c], m_run[c], l, omul);
   }
@@ -814,24 +832,6 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // the V^T transposing reads take from 8 consecutive rows are all distinct
 // (no bank conflicts with 64 banks of 4 bytes).
 __device__ __forceinline__ int wide_swizzle(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
-
-__device__ __forceinline__ float xlane_max(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows (0,1) and (2,3) exchanged
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t v = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);  // halves exchanged
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float xlane_sum(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t v = __float_as_uint(x);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 // 8 bytes of LDS through the transposing read (see the lane mapping above).
 __device__ __forceinline__ u32x2 tr_read_b64(const unsigned char* p) {
