@@ -74,3 +74,18 @@ def test_traffic_serves_only_its_workload_and_source(tmp_path, traffic_file, mon
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_chip_probe_readers_tolerate_a_missing_or_failing_probe(tmp_path, monkeypatch):
+    # no probe built: both readers return None (the bench line then leaves the
+    # measured ceilings out instead of failing)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.sustained_mfma() is None and bench.hbm_read_probe() is None
+    # a probe that prints JSON is parsed; one that fails is ignored
+    exe = tmp_path / "attention_paged_kv_varlen_amd" / "chip_probe"
+    exe.parent.mkdir()
+    exe.write_text('#!/bin/sh\nif [ "$1" = "--read-json" ]; then echo \'{"hbm_read_GBps": 7000.0}\'; '
+                   'else exit 3; fi\n')
+    exe.chmod(0o755)
+    assert bench.hbm_read_probe() == {"hbm_read_GBps": 7000.0}
+    assert bench.sustained_mfma() is None
