@@ -23,6 +23,10 @@ CASES = {
     "bf16_d128_g4_bs256": dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=256),
     "bf16_d128_g4_bs1024": dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=1024),
     "e4m3_d128_g8_bs512": dict(num_heads=16, num_kv_heads=2, head_size=128, block_size=512, kv_dtype="fp8_e4m3"),
+    # pages that are not powers of two: the lookups divide, and a prefill
+    # block's 16-row slabs start inside a page
+    "bf16_d128_g4_bs48": dict(num_heads=8, num_kv_heads=2, head_size=128, block_size=48),
+    "bf16_d128_g8_bs80": dict(num_heads=16, num_kv_heads=2, head_size=128, block_size=80),
 }
 
 
