@@ -102,3 +102,22 @@ def test_every_short_decode_length(kv_dtype, split):
         assert info["decode_list_tokens"] > 0
     ref_o, ref_l = oracle_full(b)
     assert_close(out, lse, ref_o, ref_l, f"short lengths {kv_dtype} split={split}")
+
+
+@pytest.mark.parametrize("dtype,head_size", [("bf16", 128), ("fp32", 64)])
+@pytest.mark.parametrize("scale", [4.0, 1.0, 1e-3])
+def test_extreme_softmax_scales(dtype, head_size, scale):
+    # scores of N(0,1) rows times a large scale span hundreds in the exponent:
+    # the running max moves by more than the speculative limit and the lazy
+    # threshold again and again (rescale paths), and the LSE is large; a tiny
+    # scale makes the softmax nearly flat (the mean of V).  With a peaked
+    # softmax a bf16 output is nearly one V element, rounded to bf16: half an
+    # ulp of a value in [4, 8) is 2^-7, most of the error seen at large scales
+    qlens = [1, 1, 1, 40, 150]
+    lens = [1, 300, 2100, 337, 150]
+    b = make_batch(qlens, lens, num_heads=8, num_kv_heads=2, head_size=head_size, block_size=16, seed=77,
+                   dtype=dtype, scale=scale)
+    announce(f"extreme scale {scale} {dtype} d={head_size}")
+    out, lse, _ = run_gpu(b)
+    ref_o, ref_l = oracle_full(b)
+    assert_close(out, lse, ref_o, ref_l, f"scale {scale} {dtype}")
