@@ -1321,63 +1321,127 @@ __device__ __forceinline__ f32x4 load4<float>(const float* src) {
 }
 
 // One wave per (row, head): lane s < count reads partial s's LSE, the wave
-// reduces max and sum of exponentials; then each half-wave takes every other
-// partial (lanes 32 h + j load elements 4 j .. 4 j + 3 of D = 128, 16-byte
-// loads, four partials in flight per half), and the halves are added at the end.
+// reduces max and sum of exponentials; each half-wave takes every other
+// partial (lanes 32 h + j hold elements 4 j .. 4 j + 3 of D = 128, 16-byte
+// loads), and the halves are added at the end.
+constexpr int kMergeFast = 16;
+
+// Max / sum over the 16 lanes of a DPP row: rotations by 1, 2, 4 and 8 lanes
+// (every lane of the row ends with the row's result).
+template <typename F>
+__device__ __forceinline__ float row16_reduce(float x, F op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  return row16_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  return row16_reduce(x, [](float a, float b) { return a + b; });
+}
 template <typename T, int D>
 __global__ void __launch_bounds__(256) merge_kernel(const MergeRow* rows, int n_rows, const float* ws_o,
                                                     const float* ws_lse, T* out, float* lse, int H) {
   constexpr int EPL = D / 32;  // output elements per lane of a half-wave
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, j = lane & 31;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head) pair
+  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (row, head) pair
   if (unit >= n_rows * H) return;
   const int h = unit % H;
-  const MergeRow mr = rows[unit / H];
-  float mx = -INFINITY, tot = 0.f;
-  for (int s0 = 0; s0 < mr.count; s0 += 64) {
-    const int s = s0 + lane;
-    const float ls = s < mr.count ? ws_lse[(int64_t)(mr.pbase + s) * H + h] : -INFINITY;
-    float m = ls;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float mnew = fmaxf(mx, m);
-    const float ms = (mnew == -INFINITY) ? 0.f : mnew;
-    float e = (ls == -INFINITY) ? 0.f : __expf(ls - ms);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
-    tot = tot * ((mx == -INFINITY) ? 0.f : __expf(mx - ms)) + e;
-    mx = mnew;
-  }
-  const float ms = (mx == -INFINITY) ? 0.f : mx;
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const MergeRow mr = ld_plan(rows, unit / H);
   float acc[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) acc[k] = 0.f;
-  auto add = [&](int s) {
-    const int64_t rec = (int64_t)(mr.pbase + s) * H + h;
-    const float w = __expf(ws_lse[rec] - ms) * inv;  // -inf -> 0
-    const float* src = ws_o + rec * D + EPL * j;
+  // one partial's o elements of this lane
+  auto load_o = [&](int s, float (&v)[EPL]) {
+    const float* src = ws_o + ((int64_t)(mr.pbase + s) * H + h) * D + EPL * j;
     if constexpr (EPL == 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += w * v[k];
+      for (int k = 0; k < 4; ++k) v[k] = x[k];
     } else {
-      const f32x2 v = *reinterpret_cast<const f32x2*>(src);
-      acc[0] += w * v[0];
-      acc[1] += w * v[1];
+      const f32x2 x = *reinterpret_cast<const f32x2*>(src);
+      v[0] = x[0];
+      v[1] = x[1];
     }
   };
-  int s = half;
-  for (; s + 6 < mr.count; s += 8) {
-    add(s);
-    add(s + 2);
-    add(s + 4);
-    add(s + 6);
-  }
-  for (; s < mr.count; s += 2) add(s);
+  float ms, tot;
+  if (mr.count <= kMergeFast) {
+    // Up to 16 partials: every load issued at once (lane s < count: partial
+    // s's LSE; half-wave hw: its partials hw, hw + 2, ...), max and sum over
+    // the 16 lanes of the first row by DPP rotations, each partial's weight
+    // read from its lane: one wait for memory, no LDS crossbar.
+    const float ls = lane < mr.count ? ws_lse[(int64_t)(mr.pbase + lane) * H + h] : -INFINITY;
+    float v[kMergeFast / 2][EPL];
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) acc[k] += __shfl_xor(acc[k], 32);
+    for (int i = 0; i < kMergeFast / 2; ++i) {
+      if (half + 2 * i < mr.count) {
+        load_o(half + 2 * i, v[i]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) v[i][k] = 0.f;
+      }
+    }
+    const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_max(ls))));
+    ms = (m == -INFINITY) ? 0.f : m;
+    const float e = (ls == -INFINITY) ? 0.f : __expf(ls - ms);
+    tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row16_sum(e))));
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergeFast / 2; ++i) {
+      // (the lane reads move 32-bit integers: the float's bits pass through)
+      const float we = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 2 * i));
+      const float wo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 2 * i + 1));
+      const float w = (half ? wo : we) * inv;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[k] += w * v[i][k];
+    }
+  } else {
+    // more partials: the LSE pass over 64 lanes at a time, then the o
+    // records, four in flight per half-wave
+    float mx = -INFINITY;
+    tot = 0.f;
+    for (int s0 = 0; s0 < mr.count; s0 += 64) {
+      const int s = s0 + lane;
+      const float ls = s < mr.count ? ws_lse[(int64_t)(mr.pbase + s) * H + h] : -INFINITY;
+      float m = ls;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float mnew = fmaxf(mx, m);
+      const float mss = (mnew == -INFINITY) ? 0.f : mnew;
+      float e = (ls == -INFINITY) ? 0.f : __expf(ls - mss);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
+      tot = tot * ((mx == -INFINITY) ? 0.f : __expf(mx - mss)) + e;
+      mx = mnew;
+    }
+    ms = (mx == -INFINITY) ? 0.f : mx;
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    auto add = [&](int s) {
+      const float w = __expf(ws_lse[(int64_t)(mr.pbase + s) * H + h] - ms) * inv;  // -inf -> 0
+      float v[EPL];
+      load_o(s, v);
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[k] += w * v[k];
+    };
+    int s = half;
+    for (; s + 6 < mr.count; s += 8) {
+      add(s);
+      add(s + 2);
+      add(s + 4);
+      add(s + 6);
+    }
+    for (; s < mr.count; s += 2) add(s);
+  }
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    const uint32_t u = __float_as_uint(acc[k]);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // the two half-waves exchanged
+    acc[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
   if (half == 0) {
     T* dst = out + ((int64_t)mr.row * H + h) * D + EPL * j;
     if constexpr (EPL == 4) {
