@@ -576,34 +576,35 @@ __device__ __forceinline__ void decode_body(const KArgs& a, int wg, int nw) {
     int pid[2] = {ld_plan(btrow, tile_block(kb0)), ld_plan(btrow, tile_block(kb0 + 16))};
     if constexpr (DB) {
       static_assert(sizeof(T) == 2, "two steps in flight are built for bf16 queries");
-      // Each loop pass issues the next step's loads with no branch around
-      // them (block ids are clamped, so the lookups are always valid) and
-      // leaves by its own path when the item ends, so on the path that
-      // computes a step the loads of the step after it are still counted as
-      // outstanding: no control-flow join makes the wait for one step's
-      // data also wait for the next step's.
+      // The loop runs whole pairs of steps with no exit inside (the last one
+      // or two steps follow it), so its body is a single path: each step's
+      // loads are issued with no branch around them (block ids are clamped,
+      // so the lookups are always valid) and the compiler's waits for one
+      // step's data leave the next step's loads outstanding.  (With exits
+      // inside the loop it merged the paths' counts and waited, before
+      // issuing a step's loads, for part of the step in flight.)
       Raw wa, wb;
       int pidb[2];
       load_step(kb0, pid, wa);
       pidb[0] = ld_plan(btrow, tile_block(kb0 + 32));
       pidb[1] = ld_plan(btrow, tile_block(kb0 + 48));
-      for (int t0 = kb0;; t0 += 64) {
-        if (t0 + 32 >= kv_end) {
-          compute_step(t0, wa);
-          break;
-        }
+      int t0 = kb0;
+      for (; t0 + 64 < kv_end; t0 += 64) {
         load_step(t0 + 32, pidb, wb);
         pid[0] = ld_plan(btrow, tile_block(t0 + 64));
         pid[1] = ld_plan(btrow, tile_block(t0 + 80));
         compute_step(t0, wa);
-        if (t0 + 64 >= kv_end) {
-          compute_step(t0 + 32, wb);
-          break;
-        }
         load_step(t0 + 64, pid, wa);
         pidb[0] = ld_plan(btrow, tile_block(t0 + 96));
         pidb[1] = ld_plan(btrow, tile_block(t0 + 112));
         compute_step(t0 + 32, wb);
+      }
+      if (t0 + 32 < kv_end) {
+        load_step(t0 + 32, pidb, wb);
+        compute_step(t0, wa);
+        compute_step(t0 + 32, wb);
+      } else {
+        compute_step(t0, wa);
       }
     } else {
       for (int t0 = kb0; t0 < kv_end; t0 += 32) {
