@@ -614,8 +614,8 @@ def main(argv=None) -> int:
         print(json.dumps(res, indent=1))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "sharding of the path is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); sharding the "
+              "batch over several GPUs is not built.", file=sys.stderr)
         return 2
 
     import torch
