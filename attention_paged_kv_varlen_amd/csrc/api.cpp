@@ -32,6 +32,9 @@ struct pa_plan {
   // cannot interleave their records of the two events (one side-stream pass
   // would then wait on the other caller's stream).
   std::mutex fork_mu;
+  // Held by a metadata check from its launch to the read of its result: the
+  // plan has one 4-byte result buffer for every caller.
+  std::mutex check_mu;
   // Device copies of the metadata the plan was built from, for
   // pa_plan_check_metadata: query_start_loc [B+1], seq_lens [B], the host block
   // table [B * max_blocks_per_seq] when one was given, and a 4-byte result.
@@ -318,6 +321,7 @@ pa_status check_metadata(const pa_plan* plan, const int32_t* block_table, const 
   const pa_params& p = hp.p;
   if (misaligned(block_table, 4) || misaligned(qsl, 4) || misaligned(seq_lens, 4))
     return set_err(PA_ERR_INVALID_ARG, "metadata arrays must be 4-byte aligned");
+  std::lock_guard<std::mutex> lock(const_cast<pa_plan*>(plan)->check_mu);
   int e = pa::launch_check_metadata(block_table, qsl, seq_lens, plan->dev_bt, plan->dev_qsl, plan->dev_seq_lens,
                                     p.num_seqs, p.max_blocks_per_seq, p.block_size, p.num_blocks, plan->dev_check,
                                     stream);
@@ -452,6 +456,12 @@ pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, 
   if (head_size != 64 && head_size != 128) return set_err(PA_ERR_UNSUPPORTED, "head_size not built (64, 128)");
   if (num_tokens == 0) return PA_OK;
   if (!o_a || !lse_a || !o_b || !lse_b || !o_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  // each thread moves four elements: 8 bytes of bf16, 16 of float32
+  const uintptr_t oal = dtype == PA_BF16 ? 8 : 16;
+  if (misaligned(o_a, oal) || misaligned(o_b, oal) || misaligned(o_out, oal))
+    return set_err(PA_ERR_INVALID_ARG, "o_a, o_b and o_out must be aligned to 4 elements (8 bytes bf16, 16 float32)");
+  if (misaligned(lse_a, 4) || misaligned(lse_b, 4) || misaligned(lse_out, 4))
+    return set_err(PA_ERR_INVALID_ARG, "lse_a, lse_b and lse_out must be 4-byte aligned");
   const int e = pa::launch_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out, num_tokens, num_heads, head_size,
                                         dtype, stream);
   if (e != 0) return hip_err((hipError_t)e, "kernel launch");
@@ -479,6 +489,8 @@ pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int
     return set_err(PA_ERR_INVALID_ARG, "block_size * head_size too large");
   if (seq_len == 0) return PA_OK;
   if (!kv_cache || !block_table_row || !k_out || !v_out) return set_err(PA_ERR_INVALID_ARG, "NULL pointer");
+  if (misaligned(kv_cache, 16) || misaligned(k_out, 16) || misaligned(v_out, 16) || misaligned(block_table_row, 4))
+    return set_err(PA_ERR_INVALID_ARG, "kv_cache, k_out and v_out must be 16-byte aligned, block_table_row 4-byte");
   int ss = 0, hs = 0;
   pa::pool_strides(params->kv_layout, params->block_size, params->num_kv_heads, params->head_size, ss, hs);
   const int e = pa::launch_gather(kv_cache, block_table_row, seq_len, params->block_size, params->num_kv_heads,

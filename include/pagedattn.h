@@ -245,7 +245,9 @@ size_t pa_plan_workspace_bytes(const pa_plan* plan);
  *                  checks that they lie in [0, num_blocks).
  *  query_start_loc device int32[B + 1] or NULL; must equal the plan's, entry for entry.
  *  seq_lens        device int32[B] or NULL; likewise.
- * Runs one small kernel on `stream` and waits for it (not capturable).
+ * Runs one small kernel on `stream` and waits for it (not capturable).  The
+ * plan holds one result word: checks on one plan from several host threads
+ * take turns (a lock held from the launch to the read of the result).
  * Errors: INVALID_ARG (host-only plan, misaligned arrays, any difference: the
  * message gives the count), HIP.
  */
@@ -340,9 +342,11 @@ pa_status pa_forward_fp8(const pa_plan* plan, const void* q, const void* kv_cach
  * fallos (partial softmax results combine through a natural-log LSE):
  *   lse = ln(e^lse_a + e^lse_b),  o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.
  * A part with lse = -inf contributes nothing; both -inf gives o = 0, lse = -inf.
- *  o_a, o_b, o_out device [num_tokens, num_heads, head_size] of `dtype`;
+ *  o_a, o_b, o_out device [num_tokens, num_heads, head_size] of `dtype`,
+ *                  aligned to 4 elements (8 bytes bf16, 16 bytes float32);
  *  lse_a, lse_b, lse_out device float32[num_tokens, num_heads] (lse_out may be NULL).
- * Errors: INVALID_ARG (sizes < 0, NULL pointers), UNSUPPORTED (dtype, head_size).
+ * Errors: INVALID_ARG (sizes < 0, NULL or misaligned pointers), UNSUPPORTED
+ * (dtype, head_size).
  */
 pa_status pa_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                           void* o_out, float* lse_out, int32_t num_tokens, int32_t num_heads,
@@ -393,12 +397,14 @@ pa_status pa_write_kv_fp8(const void* key, const void* value, const int64_t* slo
  * «El especialista del plato estrella», §Cómo lee el backend el KV paginado:
  * token t is slot t % bs of block block_table_row[t / bs].
  *  kv_cache        device pool of params->dtype (e4m3 codes when params->kv_dtype
- *                  is PA_KV_FP8_E4M3) in the memory order params->kv_layout.
+ *                  is PA_KV_FP8_E4M3) in the memory order params->kv_layout,
+ *                  16-byte aligned.
  *  block_table_row device int32[ceil(seq_len / bs)].
- *  k_out, v_out    device [seq_len, Hkv, d] each, the pool's element type.
+ *  k_out, v_out    device [seq_len, Hkv, d] each, the pool's element type,
+ *                  16-byte aligned.
  * Uses params->block_size, num_kv_heads, head_size, dtype, kv_dtype, kv_layout.  The ids are not
  * checked on the device: they must be in [0, num_blocks).
- * Errors: INVALID_ARG (sizes, NULL pointers), UNSUPPORTED (dtype).
+ * Errors: INVALID_ARG (sizes, NULL or misaligned pointers), UNSUPPORTED (dtype).
  */
 pa_status pa_gather_kv(const void* kv_cache, const int32_t* block_table_row, int32_t seq_len,
                        const pa_params* params, void* k_out, void* v_out, void* stream);

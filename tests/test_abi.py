@@ -151,3 +151,18 @@ def test_stride_order_and_layout_checks():
         with pytest.raises(pa.PagedAttnError) as ei:
             call()
         assert ei.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_merge_and_gather_reject_misaligned_pointers_before_any_launch():
+    # the addresses are never dereferenced: the checks come before any launch
+    for o_a, lse_a, dtype in ((4, 16, pa.PA_BF16), (8, 16, pa.PA_FP32), (16, 2, pa.PA_FP32)):
+        with pytest.raises(pa.PagedAttnError) as ei:
+            pa.pa_merge_states(o_a, lse_a, 16, 16, 16, None, num_tokens=3, num_heads=2, head_size=128,
+                               dtype=dtype, stream=0)
+        assert ei.value.status == pa.PA_ERR_INVALID_ARG and "aligned" in pa.pa_last_error()
+    p = pa.make_params(num_seqs=1, num_heads=2, num_kv_heads=2, head_size=128, block_size=16, num_blocks=4,
+                       max_blocks_per_seq=4, dtype="bf16", scale=0.1)
+    for kv, bt, k_out in ((8, 16, 16), (16, 2, 16), (16, 16, 24)):
+        with pytest.raises(pa.PagedAttnError) as ei:
+            pa.pa_gather_kv(kv, bt, 5, p, k_out, 16, stream=0)
+        assert ei.value.status == pa.PA_ERR_INVALID_ARG and "aligned" in pa.pa_last_error()
