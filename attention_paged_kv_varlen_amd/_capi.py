@@ -53,6 +53,7 @@ class pa_plan_info(ctypes.Structure):
         ("kv_tokens_read", c_int64), ("prefix_tokens_read", c_int64),
         ("decode_tokens_read", c_int64), ("prefill_tokens_read", c_int64),
         ("prefix_tokens_unique", c_int64), ("prefix_beside_decode", c_int32), ("decode_item_keys", c_int32),
+        ("decode_list_xcd_budgets", c_int32),
     ]
 
 

@@ -83,8 +83,18 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
 // worth about 192 keys.
 // A decode work item's start (its row of Q, its first block-table entries,
 // then its first K/V step, one after the other) costs a decode workgroup
-// about as much time as streaming 64 keys; the balanced lists count it.
+// time; the balanced lists count it in keys.  Timing every list of the
+// decode-only batch (256 lists, one per CU) and fitting their end times to
+// keys, items and XCD gives 0.112 us per key and 1.4 us per item (16 keys'
+// worth) for decodes alone; beside prefills or a shared-prefix pass a count
+// of 64 keys still times best.
+constexpr int kDecodeItemKeysAlone = 16;
 constexpr int kDecodeItemKeys = 64;
+// The same fit shows the lists on even-numbered XCDs (workgroup index even:
+// workgroups are dealt to the eight XCDs in turn) ending about 1.6 % later
+// than those on odd ones for equal work, on every MI355X timed; lists of
+// decodes alone are sized W - W/128 on even and W + W/128 on odd XCDs.
+inline int xcd_list_budget(int W, int64_t workgroup) { return workgroup % 2 == 0 ? W - W / 128 : W + W / 128; }
 constexpr double kPrefixFlopsPerCu = 3.6e12;
 constexpr double kDecodeBytesPerCu = 25.0e9;
 constexpr double kDecodeBytesAll = 6.5e12;
@@ -275,6 +285,13 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   // `split` keys, one item per list, longest first.
   int split = p.kv_split_tokens;
   int list_tokens = 0;
+  // decodes alone: the start cost of an item and the XCD budgets measured for
+  // them (see kDecodeItemKeysAlone); otherwise the figure that times best
+  // beside other work, and one budget for every list
+  const bool decodes_alone = np == 0 && P == 0;
+  const int item_keys = decodes_alone ? kDecodeItemKeysAlone : kDecodeItemKeys;
+  const bool xcd_budgets = decodes_alone && dec_units == dec_nw;  // list i is workgroup i
+  auto list_budget = [&](int W, int64_t list) { return xcd_budgets ? xcd_list_budget(W, list) : W; };
   if (balanced) {
     // resident list groups: workgroups per CU x CUs / workgroups per list
     const int prefix_cus = hp.prefix_beside ? n_pc * (int)ceil_div(hp.T, QB) * Hkv * hp.ps.head_groups : 0;
@@ -283,11 +300,12 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     if (np > 0)
       lanes = std::max<int64_t>(1, (int64_t)(lanes * decode_share(p, B, qsl, seq_lens, dec_tokens, nd)));
     const int64_t n_lists = std::max<int64_t>(1, std::min<int64_t>(lanes, ceil_div(dec_tokens, 256)));
-    // Each list gets a budget of W keys, each of its items counting
-    // kDecodeItemKeys more.  A list is closed with up to 31 (after an item) or
-    // 31 + kDecodeItemKeys (before one) of its budget unused, so W is the
-    // smallest multiple of 32 from the even share up whose cut needs at most
-    // n_lists lists: keys never spill into a second, nearly empty round of
+    // Each list gets a budget of keys (W, or W -+ W/128 by XCD for decodes
+    // alone when each list is one workgroup), each of its items counting
+    // item_keys more.  A list is closed with up to 31 (after an item) or
+    // 31 + item_keys (before one) of its budget unused, so W is the smallest
+    // multiple of 32 from the even share up whose cut needs at most n_lists
+    // lists: keys never spill into a second, nearly empty round of
     // workgroups.
     auto lists_needed = [&](int W) {
       int64_t n = 0;
@@ -295,16 +313,16 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
       for (int oi = 0; oi < nd; ++oi) {
         const int L = seq_lens[hp.order[oi]];
         for (int k0 = P; k0 < L;) {
-          if (W - filled - kDecodeItemKeys < 32) {
+          if (list_budget(W, n) - filled - item_keys < 32) {
             ++n;
             filled = 0;
           }
-          filled += kDecodeItemKeys;
-          const int room = W - filled;
+          filled += item_keys;
+          const int room = list_budget(W, n) - filled;
           const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
           k0 += take;
           filled += take;
-          if (W - filled < 32) {
+          if (list_budget(W, n) - filled < 32) {
             ++n;
             filled = 0;
           }
@@ -314,8 +332,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     };
     // (every sequence is at least one item: the even share of keys and item
     // starts is a lower bound)
-    int W = (int)std::max<int64_t>(32 + kDecodeItemKeys,
-                                   round_up(ceil_div(dec_tokens + (int64_t)nd * kDecodeItemKeys, n_lists), 32));
+    int W = (int)std::max<int64_t>(64 + item_keys,
+                                   round_up(ceil_div(dec_tokens + (int64_t)nd * item_keys, n_lists), 32));
     while (lists_needed(W) > n_lists) W += 32;
     list_tokens = W;
     split = list_tokens;
@@ -338,12 +356,13 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
       const int L = seq_lens[b];
       int part = 0;
       for (int k0 = P; k0 < L;) {
-        if (list_tokens - filled - kDecodeItemKeys < 32) {
+        if (list_budget(list_tokens, (int64_t)hp.decode_lists.size() - 1) - filled - item_keys < 32) {
           hp.decode_lists.push_back((int32_t)hp.decode_items.size());
           filled = 0;
         }
-        filled += kDecodeItemKeys;
-        const int room = list_tokens - filled;  // >= 32
+        const int Wl = list_budget(list_tokens, (int64_t)hp.decode_lists.size() - 1);
+        filled += item_keys;
+        const int room = Wl - filled;  // >= 32
         const int take = L - k0 <= room ? L - k0 : room / 32 * 32;
         WorkItem it{};
         it.seq = b;
@@ -358,7 +377,7 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
         dec_read += take;
         k0 += take;
         filled += take;
-        if (list_tokens - filled < 32) {
+        if (Wl - filled < 32) {
           hp.decode_lists.push_back((int32_t)hp.decode_items.size());
           filled = 0;
         }
@@ -511,7 +530,8 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   in.prefix_tokens_read = pfx_read * Hkv;
   in.prefix_tokens_unique = (int64_t)P * Hkv;
   in.prefix_beside_decode = hp.prefix_beside ? 1 : 0;
-  in.decode_item_keys = list_tokens > 0 ? kDecodeItemKeys : 0;
+  in.decode_item_keys = list_tokens > 0 ? item_keys : 0;
+  in.decode_list_xcd_budgets = list_tokens > 0 && xcd_budgets ? 1 : 0;
   in.kv_tokens_read = in.decode_tokens_read + in.prefill_tokens_read + in.prefix_tokens_read;
   return PA_OK;
 }

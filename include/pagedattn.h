@@ -131,9 +131,10 @@ typedef struct pa_plan_info {
   int32_t prefill_head_groups;  /* prefill work items per KV head and position block */
   int32_t num_decode_lists;     /* decode work lists: each is run by one group of waves (one
                                    wave per KV head) in order; one item per list unless balanced */
-  int32_t decode_list_tokens;   /* balanced lists: the budget of each list, in keys, where each of
+  int32_t decode_list_tokens;   /* balanced lists: the budget W of each list, in keys, where each of
                                    its items also counts decode_item_keys (every list but the last
-                                   comes within 32 + decode_item_keys of it); else 0 */
+                                   comes within 32 + decode_item_keys of its budget; see
+                                   decode_list_xcd_budgets); else 0 */
   int64_t kv_tokens_read;       /* K/V token rows the schedule reads, summed over KV heads */
   int64_t prefix_tokens_read;   /* of which rows of the shared prefix (the prefix pass covers the
                                    decode rows; prefill rows read their whole context in their own
@@ -147,6 +148,9 @@ typedef struct pa_plan_info {
                                    own (one prefix workgroup per CU; the decode lists cover the
                                    others); 0: before it, or no prefix */
   int32_t decode_item_keys;     /* balanced lists: what one work item's start costs, in keys */
+  int32_t decode_list_xcd_budgets; /* 1: list i's budget is W - W/128 for even i, W + W/128 for odd i
+                                   (decodes alone, one workgroup per list: workgroups are dealt to the
+                                   XCDs in turn, and lists on even XCDs run slower); 0: W for all */
 } pa_plan_info;
 
 /* Arrays a plan exposes through pa_plan_get_array. */

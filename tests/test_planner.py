@@ -212,6 +212,15 @@ def test_workspace_size_accounts_for_partials():
     assert ws >= n * 8 * 128 * 4 + n * 8 * 4
 
 
+def _list_budgets(info, n):
+    """Budget of each of n balanced lists: W, or W - W/128 (even list) and
+    W + W/128 (odd list) when the plan sizes them by XCD."""
+    W = info["decode_list_tokens"]
+    if not info["decode_list_xcd_budgets"]:
+        return np.full(n, W)
+    return np.array([W - W // 128 if i % 2 == 0 else W + W // 128 for i in range(n)])
+
+
 def _decode_schedule(plan, info):
     lists = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_LISTS)
     spans = pa.pa_plan_get_array(plan, pa.PA_ARRAY_DECODE_SPANS).reshape(-1, 3)
@@ -233,9 +242,13 @@ def test_balanced_decode_lists_partition_the_keys(seed):
     lists, spans = _decode_schedule(plan, info)
     W, ik = info["decode_list_tokens"], info["decode_item_keys"]
     assert W > 0 and W % 32 == 0 and info["kv_split_tokens"] == W and ik > 0
+    # decodes alone, one workgroup per list: the measured item cost and the
+    # XCD budgets
+    assert ik == 16 and info["decode_list_xcd_budgets"] == 1
     sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
     cost = sizes + ik * np.diff(lists)
-    assert np.all(cost[:-1] > W - 32 - ik) and np.all(cost <= W) and sizes[-1] > 0
+    bud = _list_budgets(info, len(sizes))
+    assert np.all(cost[:-1] > bud[:-1] - 32 - ik) and np.all(cost <= bud) and sizes[-1] > 0
     # items start on 32-key boundaries of their sequence (16-key tiles never
     # straddle a physical block)
     assert np.all(spans[:, 1] % 32 == 0)
@@ -255,22 +268,25 @@ def test_balanced_decode_lists_partition_the_keys(seed):
     assert info["decode_tokens_read"] == int(lens.sum()) * 8
 
 
-def _lists_needed(lens, W, ik):
+def _lists_needed(lens, W, ik, xcd):
     """The list cut of the balanced decode schedule, counted: a list closes
-    when less than 32 of its budget W is left, or before an item (which costs
-    ik) that would start with less."""
+    when less than 32 of its budget (W, or W -+ W/128 for even / odd lists
+    with XCD budgets) is left, or before an item (which costs ik) that would
+    start with less."""
+    def bud(i):
+        return W if not xcd else (W - W // 128 if i % 2 == 0 else W + W // 128)
     n, filled = 0, 0
     for L in lens:
         k0 = 0
         while k0 < L:
-            if W - filled - ik < 32:
+            if bud(n) - filled - ik < 32:
                 n, filled = n + 1, 0
             filled += ik
-            room = W - filled
+            room = bud(n) - filled
             take = L - k0 if L - k0 <= room else room // 32 * 32
             k0 += take
             filled += take
-            if W - filled < 32:
+            if bud(n) - filled < 32:
                 n, filled = n + 1, 0
     return n + (1 if filled > 0 else 0)
 
@@ -297,10 +313,14 @@ def test_balanced_decode_lists_never_exceed_the_resident_groups():
         W, ik = info["decode_list_tokens"], info["decode_item_keys"]
         sizes = np.array([int((spans[a:b, 2] - spans[a:b, 1]).sum()) for a, b in zip(lists[:-1], lists[1:])])
         cost = sizes + ik * np.diff(lists)
-        assert sizes.sum() == int(np.sum(lens)) and np.all(cost <= W) and np.all(cost[:-1] > W - 32 - ik)
-        # the smallest budget: the same cut with W - 32 needs more lists
-        if W - 32 >= 32 + ik:
-            assert _lists_needed(lens, W - 32, ik) > min(256, need)
+        bud = _list_budgets(info, len(sizes))
+        assert sizes.sum() == int(np.sum(lens)) and np.all(cost <= bud) and np.all(cost[:-1] > bud[:-1] - 32 - ik)
+        # the cut the test counts is the planner's, and the budget is the
+        # smallest: the same cut with W - 32 needs more lists
+        xcd = info["decode_list_xcd_budgets"]
+        assert _lists_needed(lens, W, ik, xcd) == info["num_decode_lists"]
+        if W - 32 >= 64 + ik:
+            assert _lists_needed(lens, W - 32, ik, xcd) > min(256, need)
 
 
 def test_decode_lists_are_single_items_with_an_explicit_split():
@@ -320,6 +340,8 @@ def test_balanced_decode_lists_start_past_a_shared_prefix():
     plan, info = host_plan([1, 1, 1, 1], lens, prefix=P, block_table=bt, mbs=313, H=32, Hkv=8)
     lists, spans = _decode_schedule(plan, info)
     assert info["decode_list_tokens"] > 0 and info["num_decode_lists"] <= 256
+    # beside a shared-prefix pass: one budget for all lists, items at 64 keys
+    assert info["decode_item_keys"] == 64 and info["decode_list_xcd_budgets"] == 0
     assert np.all(spans[:, 1] >= P) and np.all(spans[:, 1] % 32 == 0)
     assert info["decode_tokens_read"] == sum(L - P for L in lens) * 8
     order = pa.pa_plan_get_array(plan, pa.PA_ARRAY_ORDER)
@@ -366,6 +388,8 @@ def test_decode_lists_beside_prefills_take_a_share_of_the_machine(heavy):
     lists, spans = _decode_schedule(plan, info)
     n = info["num_decode_lists"]
     assert info["decode_list_tokens"] > 0 and 64 <= n <= 192
+    # beside prefills: one budget for all lists, items at 64 keys
+    assert info["decode_item_keys"] == 64 and info["decode_list_xcd_budgets"] == 0
     if heavy == "decode":
         assert n >= 180
     else:
