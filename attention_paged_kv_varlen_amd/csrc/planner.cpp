@@ -86,9 +86,11 @@ double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t
 // time; the balanced lists count it in keys.  Timing every list of the
 // decode-only batch (256 lists, one per CU) and fitting their end times to
 // keys, items and XCD gives 0.112 us per key and 1.4 us per item (16 keys'
-// worth) for decodes alone; beside prefills or a shared-prefix pass a count
-// of 64 keys still times best.
+// worth) for decodes alone, and 2.3-2.5 us (about 24 keys) for the suffix
+// lists beside a shared-prefix pass in the same launch; beside prefills a
+// count of 64 keys still times best.
 constexpr int kDecodeItemKeysAlone = 16;
+constexpr int kDecodeItemKeysBesidePrefix = 24;
 constexpr int kDecodeItemKeys = 64;
 // The same fit shows the lists on even-numbered XCDs (workgroup index even:
 // workgroups are dealt to the eight XCDs in turn) ending about 1.6 % later
@@ -289,7 +291,9 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   // them (see kDecodeItemKeysAlone); otherwise the figure that times best
   // beside other work, and one budget for every list
   const bool decodes_alone = np == 0 && P == 0;
-  const int item_keys = decodes_alone ? kDecodeItemKeysAlone : kDecodeItemKeys;
+  const int item_keys = decodes_alone       ? kDecodeItemKeysAlone
+                        : hp.prefix_beside ? kDecodeItemKeysBesidePrefix
+                                           : kDecodeItemKeys;
   const bool xcd_budgets = decodes_alone && dec_units == dec_nw;  // list i is workgroup i
   auto list_budget = [&](int W, int64_t list) { return xcd_budgets ? xcd_list_budget(W, list) : W; };
   if (balanced) {
@@ -304,9 +308,10 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     // alone when each list is one workgroup), each of its items counting
     // item_keys more.  A list is closed with up to 31 (after an item) or
     // 31 + item_keys (before one) of its budget unused, so W is the smallest
-    // multiple of 32 from the even share up whose cut needs at most n_lists
-    // lists: keys never spill into a second, nearly empty round of
-    // workgroups.
+    // budget from the even share up whose cut needs at most n_lists lists:
+    // keys never spill into a second, nearly empty round of workgroups, and
+    // (the budget moving in steps of one key) no resident group is left
+    // without a list by a budget rounded up.
     auto lists_needed = [&](int W) {
       int64_t n = 0;
       int filled = 0;
@@ -332,9 +337,12 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
     };
     // (every sequence is at least one item: the even share of keys and item
     // starts is a lower bound)
-    int W = (int)std::max<int64_t>(64 + item_keys,
-                                   round_up(ceil_div(dec_tokens + (int64_t)nd * item_keys, n_lists), 32));
+    int W = (int)std::max<int64_t>(64 + item_keys, ceil_div(dec_tokens + (int64_t)nd * item_keys, n_lists));
     while (lists_needed(W) > n_lists) W += 32;
+    // back from the first fitting step of 32 to the smallest fitting budget
+    const int W32 = W;
+    for (int lower = W32 - 1; lower > W32 - 32 && lower >= 64 + item_keys && lists_needed(lower) <= n_lists; --lower)
+      W = lower;
     list_tokens = W;
     split = list_tokens;
   } else if (split == 0) {
