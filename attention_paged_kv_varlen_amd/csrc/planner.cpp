@@ -294,7 +294,9 @@ pa_status build_host_plan(const pa_params& p, const int32_t* qsl, const int32_t*
   const int item_keys = decodes_alone       ? kDecodeItemKeysAlone
                         : hp.prefix_beside ? kDecodeItemKeysBesidePrefix
                                            : kDecodeItemKeys;
-  const bool xcd_budgets = decodes_alone && dec_units == dec_nw;  // list i is workgroup i
+  // list i is workgroup i; the whole chip (256 CUs, eight XCDs), where the
+  // XCD timings were taken
+  const bool xcd_budgets = decodes_alone && dec_units == dec_nw && num_cus == 256;
   auto list_budget = [&](int W, int64_t list) { return xcd_budgets ? xcd_list_budget(W, list) : W; };
   if (balanced) {
     // resident list groups: workgroups per CU x CUs / workgroups per list

@@ -149,8 +149,9 @@ typedef struct pa_plan_info {
                                    others); 0: before it, or no prefix */
   int32_t decode_item_keys;     /* balanced lists: what one work item's start costs, in keys */
   int32_t decode_list_xcd_budgets; /* 1: list i's budget is W - W/128 for even i, W + W/128 for odd i
-                                   (decodes alone, one workgroup per list: workgroups are dealt to the
-                                   XCDs in turn, and lists on even XCDs run slower); 0: W for all */
+                                   (decodes alone, one workgroup per list, a 256-CU device: workgroups
+                                   are dealt to the eight XCDs in turn, and lists on even XCDs run
+                                   slower); 0: W for all */
 } pa_plan_info;
 
 /* Arrays a plan exposes through pa_plan_get_array. */
