@@ -50,14 +50,19 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 // decode kernel's rate, about 6 TB/s) and the attention FLOPs of the side
 // stream (the prefills', and a shared-prefix pass's: every decode row against
 // the prefix; at the prefill kernel's rate: about 0.9 PFLOP/s on bf16 MFMA,
+// 0.7 over an e4m3 pool, whose prefill widens the codes on the way to LDS,
 // far less in fp32), kept within [0.25, 0.75].  On MI355X the decode keeps HBM near its
 // rate with about 70 % of the groups, while the prefill waits for free CUs
 // when the decode holds them all: on a mixed step of 192 decodes and four
-// 512-token chunks the step takes 1.29 ms at 70-75 % against 1.41 ms at 100 %.
+// 512-token chunks the step takes 1.29 ms at 70-75 % against 1.41 ms at 100 %;
+// over an e4m3 pool 0.78 ms at 60 % (the share the 0.7 rate gives) against
+// 0.79-0.80 ms at 50-55 % and 0.81 ms at 65.5 % (the share of the 0.9 rate).
 double decode_share(const pa_params& p, int B, const int32_t* qsl, const int32_t* seq_lens, int64_t dec_tokens,
                     int32_t n_decode_rows) {
   constexpr double kDecodeBytesPerSec = 6.0e12;
-  const double pre_flops_per_sec = p.dtype == PA_BF16 ? 0.9e15 : 0.1e15;
+  const double pre_flops_per_sec = p.dtype != PA_BF16                ? 0.1e15
+                                   : p.kv_dtype == PA_KV_FP8_E4M3 ? 0.7e15
+                                                                  : 0.9e15;
   const double elem = p.kv_dtype == PA_KV_FP8_E4M3 ? 1.0 : (p.dtype == PA_BF16 ? 2.0 : 4.0);
   double pairs = 0.0;  // (query row, visible key) pairs of the prefills, per query head
   for (int b = 0; b < B; ++b) {
