@@ -522,3 +522,24 @@ def test_cascade_schedules_cover_rows_and_fit_the_chip(seed):
     if info["prefix_beside_decode"]:
         units = info["num_prefix_items"] * 8 * info["prefill_head_groups"]
         assert units + info["num_decode_lists"] <= 256
+
+
+def test_decode_share_beside_prefills_follows_the_pool_type():
+    """The chunked-prefill mixed batch (192 decodes, four 512-token chunks):
+    the decode lists take the share the two parts' estimated times give,
+    capped at three quarters for bf16 (192 of 256 groups); over an e4m3 pool
+    the prefill's slower rate (0.7 against 0.9 PFLOP/s) and the decode's
+    halved bytes leave the decode about 60 % (153 lists)."""
+    from workloads import config_lengths
+    q, L, _ = config_lengths(4)
+    qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    mbs = int(-(-int(L.max()) // 64))
+    counts = {}
+    for kvd in ("same", "fp8_e4m3"):
+        p = pa.make_params(num_seqs=len(L), num_heads=64, num_kv_heads=8, head_size=128, block_size=64,
+                           num_blocks=len(L) * mbs, max_blocks_per_seq=mbs, dtype="bf16", scale=128 ** -0.5,
+                           kv_dtype=kvd)
+        info = pa.pa_plan_get_info(pa.pa_plan_create(p, qsl, L.astype(np.int32), None, device=-1))
+        assert info["num_prefills"] == 4 and info["decode_item_keys"] == 64
+        counts[kvd] = info["num_decode_lists"]
+    assert counts == {"same": 192, "fp8_e4m3": 153}
